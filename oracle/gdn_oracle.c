@@ -1,0 +1,395 @@
+/*
+ * gdn_oracle.c -- plain, slow fp64 reference of the gated-delta-rule (GDN) mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this file's library.  It shares no
+ * code, header, table or helper with the HIP library, and never calls it.
+ *
+ * What it computes, and where that is stated:
+ *   - The mixer (the Qwen3.5 hybrid model's linear-attention layer) is a
+ *     depthwise causal conv1d of width 4 over the packed q/k/v channels with a
+ *     3-row tail state, then SiLU, then L2-normalised q and k (q also scaled
+ *     by dk^-1/2), then per value head the recurrence
+ *         S <- alpha * S * (I - beta k k^T) + beta v k^T,   o = S q,
+ *         alpha = exp(-exp(A_log) * softplus(a + dt_bias)),  beta = sigmoid(b).
+ *     S is dv x dk; this file stores its transpose M = S^T as [dk][dv]
+ *     (dv contiguous), so the same step reads
+ *         M <- alpha * (M - beta k (k^T M)) + beta k v^T,   o = M^T q.
+ *   - Verify windows hold at most 16 rows, and the engine records each row's
+ *     recurrent state and conv tail; the rows of a window must give what the
+ *     same rows give as one-row steps, bit for bit: page "perf(qwen3_5 cuda):
+ *     deliver the first token before drafting", commit note on the MLX affine
+ *     4-bit checkpoint on the native CUDA server.
+ *   - A window's rows may form a tree in which each row names its parent; the
+ *     conv taps and the delta rule then follow each row's own branch; one-row
+ *     steps and prompt passes change the state in place: same page, commit
+ *     note on tree-shaped verify windows.
+ *   - A verify round packs every stream's window together, at most 16 streams
+ *     of 16 rows: page "perf(qwen27 cuda): reduce repeated-prompt TTFT", commit
+ *     note on the qwen3_5 checkpoint with the 27B's shapes.
+ *   - The prompt oracle is the plain recurrence, row after row.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   conv is a cross-correlation, y_t = sum_j w[c][j] x_{t-3+j}[c], no bias;
+ *   the tail holds the last three raw (pre-conv) rows, oldest first; SiLU acts
+ *   on every channel; channels are [q | k | v], head-major; value head h uses
+ *   key head h / (hv / hk); khat = k / sqrt(|k|^2 + 1e-6),
+ *   qhat = q / sqrt(|q|^2 + 1e-6) / sqrt(dk); o is read after the update.
+ *
+ * Arithmetic is fp64 throughout, from the exact bf16 / fp32 input values.
+ * Parallelism (OpenMP over (stream, value head)) never changes a result: no
+ * sum crosses those units.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define CONV_W 4
+#define TAIL 3
+
+typedef struct {
+    int32_t hk, hv, dk, dv;
+} oracle_shape;
+
+static int channels(const oracle_shape *s) { return 2 * s->hk * s->dk + s->hv * s->dv; }
+
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* softplus(x) = log(1 + e^x), in the form that neither overflows nor cancels. */
+static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static double silu(double y) { return y * sigmoid(y); }
+
+/* Decay alpha and write strength beta of one (row, value head). */
+void gdn_oracle_gates(double a, double b, double a_log, double dt_bias,
+                      double *alpha, double *beta)
+{
+    double g = -exp(a_log) * softplus(a + dt_bias);
+    *alpha = exp(g);
+    *beta = sigmoid(b);
+}
+
+/* Causal depthwise conv of one row: taps[j] is the raw row x_{t-3+j}
+ * (taps[3] = the current row).  Writes the conv output before and after SiLU. */
+void gdn_oracle_conv_silu(int32_t C, const float *conv_w, const uint16_t *const taps[4],
+                          double *pre, double *post)
+{
+    for (int c = 0; c < C; ++c) {
+        double y = 0.0;
+        for (int j = 0; j < CONV_W; ++j)
+            y += (double)conv_w[(size_t)c * CONV_W + j] * bf16_value(taps[j][c]);
+        if (pre) pre[c] = y;
+        if (post) post[c] = silu(y);
+    }
+}
+
+/* Everything value head h needs from one row: normalised q and k of its key
+ * head, its v, and its gates.  act[] is the SiLU'd conv output of all C
+ * channels of the row. */
+static void head_inputs(const oracle_shape *s, const double *act, int h,
+                        double a, double b, double a_log, double dt_bias,
+                        double *qhat, double *khat, double *v, double *alpha, double *beta)
+{
+    const int r = s->hv / s->hk;
+    const int kh = h / r;
+    const double *q = act + (size_t)kh * s->dk;
+    const double *k = act + (size_t)s->hk * s->dk + (size_t)kh * s->dk;
+    const double *vv = act + (size_t)2 * s->hk * s->dk + (size_t)h * s->dv;
+    double qq = 0.0, kk = 0.0;
+    for (int i = 0; i < s->dk; ++i) {
+        qq += q[i] * q[i];
+        kk += k[i] * k[i];
+    }
+    const double qs = 1.0 / sqrt(qq + 1e-6) / sqrt((double)s->dk);
+    const double ks = 1.0 / sqrt(kk + 1e-6);
+    for (int i = 0; i < s->dk; ++i) {
+        qhat[i] = q[i] * qs;
+        khat[i] = k[i] * ks;
+    }
+    for (int j = 0; j < s->dv; ++j) v[j] = vv[j];
+    gdn_oracle_gates(a, b, a_log, dt_bias, alpha, beta);
+}
+
+/* One step of the recurrence on M = S^T ([dk][dv]), in the literal product
+ * form M <- alpha (M - beta k (k^T M)) + beta k v^T, then o = M^T q. */
+static void delta_step(int dk, int dv, const double *khat, const double *qhat,
+                       const double *v, double alpha, double beta, double *M,
+                       double *kTM, double *o)
+{
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += khat[i] * M[(size_t)i * dv + j];
+        kTM[j] = acc;
+    }
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) {
+            double *m = &M[(size_t)i * dv + j];
+            *m = alpha * (*m - beta * khat[i] * kTM[j]) + beta * khat[i] * v[j];
+        }
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += M[(size_t)i * dv + j] * qhat[i];
+        o[j] = acc;
+    }
+}
+
+/* The recurrence alone, on inputs given directly: T rows of alpha, beta,
+ * khat [T][dk], qhat [T][dk] and v [T][dv], from M0 [dk][dv].  Writes the
+ * final state and o [T][dv]; M_all [T][dk][dv] (optional) gets every row's
+ * state. */
+void gdn_oracle_raw_recurrence(int32_t dk, int32_t dv, int32_t T, const double *alpha,
+                               const double *beta, const double *khat, const double *qhat,
+                               const double *v, const double *M0, double *M_out,
+                               double *o, double *M_all)
+{
+    double *M = malloc(sizeof(double) * (size_t)dk * dv);
+    double *tmp = malloc(sizeof(double) * (size_t)dv);
+    memcpy(M, M0, sizeof(double) * (size_t)dk * dv);
+    for (int t = 0; t < T; ++t) {
+        delta_step(dk, dv, khat + (size_t)t * dk, qhat + (size_t)t * dk, v + (size_t)t * dv,
+                   alpha[t], beta[t], M, tmp, o + (size_t)t * dv);
+        if (M_all) memcpy(M_all + (size_t)t * dk * dv, M, sizeof(double) * (size_t)dk * dv);
+    }
+    memcpy(M_out, M, sizeof(double) * (size_t)dk * dv);
+    free(M);
+    free(tmp);
+}
+
+/*
+ * Rows of one stream, as a tree.  Row i (local index) hangs off parent[i]
+ * (parent[i] < i; -1 = the stream's committed state and tail).  A chain is the
+ * tree with parent[i] = i - 1.  For each row:
+ *   tail_i = (tail_p[1], tail_p[2], x_i)  where tail_p is the parent's tail,
+ *   taps   = (tail_p[0], tail_p[1], tail_p[2], x_i),
+ *   M_i    = delta step of M_p with row i's inputs.
+ * Results go to o [rows][hv][dv] (fp64), and optionally to each row's tail
+ * (raw bf16 bits, [rows][3][C]) and state ([rows][hv][dk][dv] as fp64 and/or
+ * fp32).  final_state / final_tail (optional) get the last row's.
+ */
+typedef struct {
+    const oracle_shape *s;
+    const float *conv_w, *a_log, *dt_bias;
+    const uint16_t *qkv, *a, *b;   /* rows of this stream: [rows][C], [rows][hv] */
+    const int32_t *parent;         /* [rows] local, or NULL = chain              */
+    const uint16_t *tail0;         /* [3][C]                                     */
+    const double *state0;          /* [hv][dk][dv]                               */
+    int32_t rows;
+    double *o;                     /* [rows][hv][dv]                             */
+    uint16_t *tail_snap;           /* [rows][3][C] or NULL                        */
+    double *snap64;                /* [rows][hv][dk][dv] or NULL                  */
+    float *snap32;                 /* [rows][hv][dk][dv] or NULL                  */
+    double *final_state;           /* [hv][dk][dv] or NULL                        */
+    uint16_t *final_tail;          /* [3][C] or NULL                              */
+} stream_job;
+
+/* Per-row tails of a stream (bf16 bits): node tails follow the parents. */
+static uint16_t *stream_tails(const stream_job *jb)
+{
+    const int C = channels(jb->s);
+    uint16_t *tails = malloc(sizeof(uint16_t) * (size_t)jb->rows * TAIL * C);
+    for (int i = 0; i < jb->rows; ++i) {
+        const int p = jb->parent ? jb->parent[i] : i - 1;
+        const uint16_t *tp = p < 0 ? jb->tail0 : tails + (size_t)p * TAIL * C;
+        uint16_t *ti = tails + (size_t)i * TAIL * C;
+        memcpy(ti, tp + C, sizeof(uint16_t) * 2 * C);               /* (tail_p[1], tail_p[2]) */
+        memcpy(ti + 2 * C, jb->qkv + (size_t)i * C, sizeof(uint16_t) * C); /* x_i */
+    }
+    return tails;
+}
+
+/* The recurrence of one value head over one stream's rows. */
+static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
+{
+    const oracle_shape *s = jb->s;
+    const int C = channels(s), dk = s->dk, dv = s->dv;
+    const size_t msz = (size_t)dk * dv;
+    const int is_tree = jb->parent != NULL;
+    /* a chain needs only the running state; a tree keeps every node's */
+    double *states = malloc(sizeof(double) * msz * (is_tree ? (size_t)jb->rows : 1));
+    double *cur = malloc(sizeof(double) * msz);
+    double *act = malloc(sizeof(double) * C);
+    double *qhat = malloc(sizeof(double) * dk), *khat = malloc(sizeof(double) * dk);
+    double *v = malloc(sizeof(double) * dv), *tmp = malloc(sizeof(double) * dv);
+    const double *M0 = jb->state0 + (size_t)h * msz;
+    memcpy(cur, M0, sizeof(double) * msz);
+    for (int i = 0; i < jb->rows; ++i) {
+        const int p = is_tree ? jb->parent[i] : i - 1;
+        if (is_tree) memcpy(cur, p < 0 ? M0 : states + (size_t)p * msz, sizeof(double) * msz);
+        const uint16_t *tp = p < 0 ? jb->tail0 : tails + (size_t)p * TAIL * C;
+        const uint16_t *taps[4] = {tp, tp + C, tp + 2 * C, jb->qkv + (size_t)i * C};
+        gdn_oracle_conv_silu(C, jb->conv_w, taps, NULL, act);
+        double alpha, beta;
+        head_inputs(s, act, h, bf16_value(jb->a[(size_t)i * s->hv + h]),
+                    bf16_value(jb->b[(size_t)i * s->hv + h]), jb->a_log[h], jb->dt_bias[h],
+                    qhat, khat, v, &alpha, &beta);
+        delta_step(dk, dv, khat, qhat, v, alpha, beta, cur,
+                   tmp, jb->o + ((size_t)i * s->hv + h) * dv);
+        if (is_tree) memcpy(states + (size_t)i * msz, cur, sizeof(double) * msz);
+        const size_t off = ((size_t)i * s->hv + h) * msz;
+        if (jb->snap64) memcpy(jb->snap64 + off, cur, sizeof(double) * msz);
+        if (jb->snap32)
+            for (size_t e = 0; e < msz; ++e) jb->snap32[off + e] = (float)cur[e];
+    }
+    if (jb->final_state && jb->rows > 0)
+        memcpy(jb->final_state + (size_t)h * msz, cur, sizeof(double) * msz);
+    free(states); free(cur); free(act); free(qhat); free(khat); free(v); free(tmp);
+}
+
+static void finish_tails(const stream_job *jb, const uint16_t *tails)
+{
+    const int C = channels(jb->s);
+    if (jb->tail_snap)
+        memcpy(jb->tail_snap, tails, sizeof(uint16_t) * (size_t)jb->rows * TAIL * C);
+    if (jb->final_tail && jb->rows > 0)
+        memcpy(jb->final_tail, tails + (size_t)(jb->rows - 1) * TAIL * C,
+               sizeof(uint16_t) * TAIL * C);
+}
+
+/* Runs many streams; OpenMP threads take (stream, value head) units. */
+static void run_streams(const stream_job *jobs, int n, int hv)
+{
+    uint16_t **tails = malloc(sizeof(uint16_t *) * (size_t)(n > 0 ? n : 1));
+    for (int s = 0; s < n; ++s) tails[s] = stream_tails(&jobs[s]);
+    const long units = (long)n * hv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u) stream_head(&jobs[u / hv], tails[u / hv], (int)(u % hv));
+    for (int s = 0; s < n; ++s) {
+        finish_tails(&jobs[s], tails[s]);
+        free(tails[s]);
+    }
+    free(tails);
+}
+
+static void fill_job(stream_job *jb, const oracle_shape *s, const float *conv_w,
+                     const float *a_log, const float *dt_bias, const int32_t *row_start,
+                     int stream, const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                     const uint16_t *tail, const double *state)
+{
+    const int C = channels(s);
+    const int r0 = row_start[stream];
+    memset(jb, 0, sizeof *jb);
+    jb->s = s;
+    jb->conv_w = conv_w; jb->a_log = a_log; jb->dt_bias = dt_bias;
+    jb->qkv = qkv + (size_t)r0 * C;
+    jb->a = a + (size_t)r0 * s->hv;
+    jb->b = b + (size_t)r0 * s->hv;
+    jb->tail0 = tail + (size_t)stream * TAIL * C;
+    jb->state0 = state + (size_t)stream * s->hv * s->dk * s->dv;
+    jb->rows = row_start[stream + 1] - r0;
+}
+
+/*
+ * Verify windows (parent == NULL: each stream's rows form a chain) or trees
+ * (parent[r] = local parent index of packed row r, -1 for a root).  Inputs:
+ * row_start [n+1] (host), qkv [R][C] bf16 bits, a, b [R][hv] bf16 bits, tail
+ * [n][3][C] bf16 bits, state [n][hv][dk][dv] fp64.  Outputs (any may be NULL
+ * but o): o [R][hv][dv] fp64, tail_snap [R][3][C], snap64 / snap32
+ * [R][hv][dk][dv].  Returns 0, or -1 on a malformed layout.
+ */
+int gdn_oracle_window(const oracle_shape *s, const float *conv_w, const float *a_log,
+                      const float *dt_bias, int32_t n, const int32_t *row_start,
+                      const int32_t *parent, const uint16_t *qkv, const uint16_t *a,
+                      const uint16_t *b, const uint16_t *tail, const double *state,
+                      double *o, uint16_t *tail_snap, double *snap64, float *snap32)
+{
+    if (s->hk <= 0 || s->hv <= 0 || s->hv % s->hk || s->dk <= 0 || s->dv <= 0 || n < 0)
+        return -1;
+    const int C = channels(s);
+    const size_t msz = (size_t)s->dk * s->dv;
+    stream_job *jobs = calloc((size_t)(n > 0 ? n : 1), sizeof *jobs);
+    for (int st = 0; st < n; ++st) {
+        if (row_start[st + 1] < row_start[st]) { free(jobs); return -1; }
+        fill_job(&jobs[st], s, conv_w, a_log, dt_bias, row_start, st, qkv, a, b, tail, state);
+        const int r0 = row_start[st];
+        if (parent) {
+            jobs[st].parent = parent + r0;
+            for (int i = 0; i < jobs[st].rows; ++i)
+                if (parent[r0 + i] < -1 || parent[r0 + i] >= i) { free(jobs); return -1; }
+        }
+        jobs[st].o = o + (size_t)r0 * s->hv * s->dv;
+        if (tail_snap) jobs[st].tail_snap = tail_snap + (size_t)r0 * TAIL * C;
+        if (snap64) jobs[st].snap64 = snap64 + (size_t)r0 * s->hv * msz;
+        if (snap32) jobs[st].snap32 = snap32 + (size_t)r0 * s->hv * msz;
+    }
+    run_streams(jobs, n, s->hv);
+    free(jobs);
+    return 0;
+}
+
+/*
+ * Prompt passes: each of the n prompts runs its rows as one chain from its
+ * stream's state and tail, and its final state and tail replace them (in
+ * place).  state is fp64 [n][hv][dk][dv] in/out, tail [n][3][C] bf16 bits
+ * in/out, o [T][hv][dv] fp64.  A prompt of zero rows leaves its stream as it
+ * was.
+ */
+int gdn_oracle_prefill(const oracle_shape *s, const float *conv_w, const float *a_log,
+                       const float *dt_bias, int32_t n, const int32_t *seq_start,
+                       const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                       uint16_t *tail, double *state, double *o)
+{
+    if (s->hk <= 0 || s->hv <= 0 || s->hv % s->hk || s->dk <= 0 || s->dv <= 0 || n < 0)
+        return -1;
+    const int C = channels(s);
+    const size_t ssz = (size_t)s->hv * s->dk * s->dv;
+    /* inputs are copied so that the in-place results never feed a later read */
+    double *state_in = malloc(sizeof(double) * ssz * (size_t)(n > 0 ? n : 1));
+    uint16_t *tail_in = malloc(sizeof(uint16_t) * (size_t)TAIL * C * (n > 0 ? n : 1));
+    memcpy(state_in, state, sizeof(double) * ssz * (size_t)n);
+    memcpy(tail_in, tail, sizeof(uint16_t) * (size_t)TAIL * C * n);
+    stream_job *jobs = calloc((size_t)(n > 0 ? n : 1), sizeof *jobs);
+    for (int st = 0; st < n; ++st) {
+        if (seq_start[st + 1] < seq_start[st]) {
+            free(jobs); free(state_in); free(tail_in);
+            return -1;
+        }
+        fill_job(&jobs[st], s, conv_w, a_log, dt_bias, seq_start, st, qkv, a, b, tail_in,
+                 state_in);
+        jobs[st].o = o + (size_t)seq_start[st] * s->hv * s->dv;
+        jobs[st].final_state = state + (size_t)st * ssz;
+        jobs[st].final_tail = tail + (size_t)st * TAIL * C;
+    }
+    run_streams(jobs, n, s->hv);
+    free(jobs);
+    free(state_in);
+    free(tail_in);
+    return 0;
+}
+
+/* Commit: a stream's state and tail become those recorded for its accepted
+ * row (packed index), or stay as they are for -1. */
+int gdn_oracle_commit(const oracle_shape *s, int32_t n, int32_t total_rows,
+                      const int32_t *accept, const uint16_t *tail_snap, const double *snap64,
+                      uint16_t *tail, double *state)
+{
+    const int C = channels(s);
+    const size_t ssz = (size_t)s->hv * s->dk * s->dv;
+    for (int st = 0; st < n; ++st) {
+        const int r = accept[st];
+        if (r < -1 || r >= total_rows) return -1;
+        if (r < 0) continue;
+        memcpy(state + (size_t)st * ssz, snap64 + (size_t)r * ssz, sizeof(double) * ssz);
+        memcpy(tail + (size_t)st * TAIL * C, tail_snap + (size_t)r * TAIL * C,
+               sizeof(uint16_t) * TAIL * C);
+    }
+    return 0;
+}
+
+int gdn_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
