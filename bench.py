@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of libgdn's verify window: GDN layer tokens/s and achieved HBM
+GB/s at 16 streams x 16-row verify on a 27B-like layer (hk=16, hv=48,
+dk=dv=128), every row's state and conv tail recorded.
+
+One step = one gdn_recur_window call over the packed 256 rows, inputs already
+resident in HBM.  Prints ONE JSON line (see the keys below).  Extra workloads
+(``--workload tree27b`` ...) print the same line for that workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0     # MI355X dense bf16 matrix peak, published
+
+
+def window_bytes(shape, n, rows):
+    """Algorithmic HBM bytes of one window / tree call: every input read once,
+    every output written once."""
+    C = shape.channels
+    S = shape.hv * shape.dk * shape.dv * 4
+    return (n * S                        # stream states in
+            + rows * S                   # per-row state snapshots out
+            + n * 3 * C * 2              # conv tails in
+            + rows * 3 * C * 2           # per-row tail snapshots out
+            + rows * C * 2               # packed qkv rows in
+            + rows * shape.hv * 2 * 2    # a, b in
+            + rows * shape.hv * shape.dv * 4   # o out
+            + C * 4 * 4 + 2 * shape.hv * 4)    # conv weights, A_log, dt_bias
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="verify27b", choices=["verify27b", "tree27b", "ragged27b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy, a kernel of known traffic "
+                         "for scaling hardware byte counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(the verify path shards by stream or key-head group with no "
+                                   "exchange, see the design notes)"}))
+        sys.exit(2)
+
+    import torch
+    from verify_causal_conv1d_amd import gdn
+    from verify_causal_conv1d_amd import inputs as gi
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    shape, lengths, kw = gi.workload(args.workload)
+    tree = args.workload == "tree27b"
+    b = gi.make_batch(shape, lengths, **kw)
+    n, R = b.n, b.rows
+    params = gdn.LayerParams.from_host(b.params, dev)
+    row_start = b.row_start.to(dev)
+    qkv, a, bb = b.qkv.to(dev), b.a.to(dev), b.b.to(dev)
+    tail, state = b.tail.to(dev), b.state.to(dev)
+    parent = b.parent.to(dev) if tree else None
+    out = torch.empty((R, shape.hv, shape.dv), dtype=torch.float32, device=dev)
+    tsnap = torch.empty((R, 3, shape.channels), dtype=torch.bfloat16, device=dev)
+    ssnap = torch.empty((R, shape.hv, shape.dk, shape.dv), dtype=torch.float32, device=dev)
+    max_rows = max(lengths)
+
+    def step():
+        if tree:
+            gdn.recur_tree(shape, params, row_start, parent, qkv, a, bb, tail, state, out, tsnap,
+                           ssnap, max_rows=max_rows)
+        else:
+            gdn.recur_window(shape, params, row_start, qkv, a, bb, tail, state, out, tsnap, ssnap,
+                             max_rows=max_rows)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Per-launch timing with events on the launch stream (torch's current
+    # stream, which is the stream libgdn launches on), then the wall clock of
+    # the whole timed region.
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_ms = sum(kernel_ms) / len(kernel_ms)
+    med_ms = kernel_ms[len(kernel_ms) // 2]
+
+    bytes_per_launch = window_bytes(shape, n, R)
+    achieved_gbs = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = R * args.steps / wall
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(b, tree, args.cpu_seconds)
+
+    line = {
+        "metric": "GDN layer tokens/s and achieved HBM GB/s at 16 streams x 16-row verify",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 inputs)",
+        "data": "synthetic",
+        "config": {
+            "workload": {"verify27b": "16 streams x 16-row verify window, per-row state and tail recorded",
+                         "tree27b": "16 streams x 16-node random draft trees, per-node state and tail recorded",
+                         "ragged27b": "16 streams, ragged windows U{1..16}, per-row recording"}[args.workload],
+            "layer": {"hk": shape.hk, "hv": shape.hv, "dk": shape.dk, "dv": shape.dv, "conv_width": 4},
+            "streams": n, "rows": R, "seed": kw["seed"],
+        },
+        "hbm_gbs": round(achieved_gbs, 1),
+        "kernel_ms_avg": round(avg_ms, 5),
+        "kernel_ms_median": round(med_ms, 5),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "rows_kernel<128>",
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(b, tree, budget_s):
+    """The fp64 oracle, as it stands, on the same inputs: whole calls repeated
+    until about ``budget_s`` seconds of wall time have passed."""
+    import numpy as np
+    import oracle
+    from verify_causal_conv1d_amd import inputs as gi
+    h = dict(conv_w=b.params.conv_w.numpy(), a_log=b.params.a_log.numpy(),
+             dt_bias=b.params.dt_bias.numpy(), row_start=b.row_start.numpy(),
+             qkv=gi.bf16_bits(b.qkv), a=gi.bf16_bits(b.a), b=gi.bf16_bits(b.b),
+             tail=gi.bf16_bits(b.tail), state=b.state.numpy().astype(np.float64))
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        if tree:
+            oracle.tree(b.shape, h["conv_w"], h["a_log"], h["dt_bias"], h["row_start"],
+                        b.parent.numpy(), h["qkv"], h["a"], h["b"], h["tail"], h["state"],
+                        snap64=False, snap32=True)
+        else:
+            oracle.window(b.shape, h["conv_w"], h["a_log"], h["dt_bias"], h["row_start"],
+                          h["qkv"], h["a"], h["b"], h["tail"], h["state"], snap64=False, snap32=True)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    return {"value": round(b.rows * calls / el, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{calls} whole calls of the same workload ({b.rows} rows each), fp64, "
+                      f"{el:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

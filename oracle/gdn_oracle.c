@@ -78,44 +78,51 @@ void gdn_oracle_gates(double a, double b, double a_log, double dt_bias,
     *beta = sigmoid(b);
 }
 
-/* Causal depthwise conv of one row: taps[j] is the raw row x_{t-3+j}
- * (taps[3] = the current row).  Writes the conv output before and after SiLU. */
-void gdn_oracle_conv_silu(int32_t C, const float *conv_w, const uint16_t *const taps[4],
-                          double *pre, double *post)
+/* Causal depthwise conv of channels [c0, c0 + count) of one row: taps[j] is
+ * the raw row x_{t-3+j} (taps[3] = the current row).  Writes the conv output
+ * before (optional) and after SiLU, indexed from c0. */
+static void conv_silu_range(const float *conv_w, const uint16_t *const taps[4], int c0, int count,
+                            double *pre, double *post)
 {
-    for (int c = 0; c < C; ++c) {
+    for (int c = c0; c < c0 + count; ++c) {
         double y = 0.0;
         for (int j = 0; j < CONV_W; ++j)
             y += (double)conv_w[(size_t)c * CONV_W + j] * bf16_value(taps[j][c]);
-        if (pre) pre[c] = y;
-        if (post) post[c] = silu(y);
+        if (pre) pre[c - c0] = y;
+        if (post) post[c - c0] = silu(y);
     }
 }
 
+/* The same for all C channels of a row. */
+void gdn_oracle_conv_silu(int32_t C, const float *conv_w, const uint16_t *const taps[4],
+                          double *pre, double *post)
+{
+    conv_silu_range(conv_w, taps, 0, C, pre, post);
+}
+
 /* Everything value head h needs from one row: normalised q and k of its key
- * head, its v, and its gates.  act[] is the SiLU'd conv output of all C
- * channels of the row. */
-static void head_inputs(const oracle_shape *s, const double *act, int h,
-                        double a, double b, double a_log, double dt_bias,
+ * head, its v, and its gates.  Only the conv channels of those heads are
+ * computed: q of key head kh, k of key head kh, v of value head h. */
+static void head_inputs(const oracle_shape *s, const float *conv_w, const uint16_t *const taps[4],
+                        int h, double a, double b, double a_log, double dt_bias,
                         double *qhat, double *khat, double *v, double *alpha, double *beta)
 {
     const int r = s->hv / s->hk;
     const int kh = h / r;
-    const double *q = act + (size_t)kh * s->dk;
-    const double *k = act + (size_t)s->hk * s->dk + (size_t)kh * s->dk;
-    const double *vv = act + (size_t)2 * s->hk * s->dk + (size_t)h * s->dv;
+    conv_silu_range(conv_w, taps, kh * s->dk, s->dk, NULL, qhat);
+    conv_silu_range(conv_w, taps, s->hk * s->dk + kh * s->dk, s->dk, NULL, khat);
+    conv_silu_range(conv_w, taps, 2 * s->hk * s->dk + h * s->dv, s->dv, NULL, v);
     double qq = 0.0, kk = 0.0;
     for (int i = 0; i < s->dk; ++i) {
-        qq += q[i] * q[i];
-        kk += k[i] * k[i];
+        qq += qhat[i] * qhat[i];
+        kk += khat[i] * khat[i];
     }
     const double qs = 1.0 / sqrt(qq + 1e-6) / sqrt((double)s->dk);
     const double ks = 1.0 / sqrt(kk + 1e-6);
     for (int i = 0; i < s->dk; ++i) {
-        qhat[i] = q[i] * qs;
-        khat[i] = k[i] * ks;
+        qhat[i] = qhat[i] * qs;
+        khat[i] = khat[i] * ks;
     }
-    for (int j = 0; j < s->dv; ++j) v[j] = vv[j];
     gdn_oracle_gates(a, b, a_log, dt_bias, alpha, beta);
 }
 
@@ -216,7 +223,6 @@ static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
     /* a chain needs only the running state; a tree keeps every node's */
     double *states = malloc(sizeof(double) * msz * (is_tree ? (size_t)jb->rows : 1));
     double *cur = malloc(sizeof(double) * msz);
-    double *act = malloc(sizeof(double) * C);
     double *qhat = malloc(sizeof(double) * dk), *khat = malloc(sizeof(double) * dk);
     double *v = malloc(sizeof(double) * dv), *tmp = malloc(sizeof(double) * dv);
     const double *M0 = jb->state0 + (size_t)h * msz;
@@ -226,9 +232,8 @@ static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
         if (is_tree) memcpy(cur, p < 0 ? M0 : states + (size_t)p * msz, sizeof(double) * msz);
         const uint16_t *tp = p < 0 ? jb->tail0 : tails + (size_t)p * TAIL * C;
         const uint16_t *taps[4] = {tp, tp + C, tp + 2 * C, jb->qkv + (size_t)i * C};
-        gdn_oracle_conv_silu(C, jb->conv_w, taps, NULL, act);
         double alpha, beta;
-        head_inputs(s, act, h, bf16_value(jb->a[(size_t)i * s->hv + h]),
+        head_inputs(s, jb->conv_w, taps, h, bf16_value(jb->a[(size_t)i * s->hv + h]),
                     bf16_value(jb->b[(size_t)i * s->hv + h]), jb->a_log[h], jb->dt_bias[h],
                     qhat, khat, v, &alpha, &beta);
         delta_step(dk, dv, khat, qhat, v, alpha, beta, cur,
@@ -241,7 +246,7 @@ static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
     }
     if (jb->final_state && jb->rows > 0)
         memcpy(jb->final_state + (size_t)h * msz, cur, sizeof(double) * msz);
-    free(states); free(cur); free(act); free(qhat); free(khat); free(v); free(tmp);
+    free(states); free(cur); free(qhat); free(khat); free(v); free(tmp);
 }
 
 static void finish_tails(const stream_job *jb, const uint16_t *tails)

@@ -1,0 +1,233 @@
+"""GPU parity of the row kernels (step, window, tree, commit) against the oracle,
+and the bitwise invariants the pages require: a window's rows equal one-row
+steps, a tree's paths equal chains, a stream's results do not depend on what
+else is packed with it.  Outputs start poisoned (NaN), so an element the
+kernels fail to write shows up as a failure."""
+import numpy as np
+import pytest
+import torch
+
+from verify_causal_conv1d_amd import gdn
+from verify_causal_conv1d_amd import inputs as gi
+
+from gpu_util import (TOL_ROWS, announce, bits16, bits32, device_batch, max_rel_err,
+                      oracle_rows, poisoned_outputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_window(b: gi.Batch, tree=False, max_rows=16, d=None):
+    d = d or device_batch(b)
+    out, tsnap, ssnap = poisoned_outputs(b.shape, b.rows)
+    if tree:
+        gdn.recur_tree(b.shape, d["params"], d["row_start"], d["parent"], d["qkv"], d["a"], d["b"],
+                       d["tail"], d["state"], out, tsnap, ssnap, max_rows=max_rows)
+    else:
+        gdn.recur_window(b.shape, d["params"], d["row_start"], d["qkv"], d["a"], d["b"],
+                         d["tail"], d["state"], out, tsnap, ssnap, max_rows=max_rows)
+    torch.cuda.synchronize()
+    return out, tsnap, ssnap
+
+
+def check_against_oracle(b: gi.Batch, out, tsnap, ssnap, tree=False, tol=TOL_ROWS):
+    ref = oracle_rows(b, tree=tree)
+    e_o = max_rel_err(out.cpu().numpy(), ref["o"], 1)
+    e_s = max_rel_err(ssnap.cpu().numpy(), ref["snap32"], 2)
+    assert e_o <= tol, f"o: max rel err {e_o:.3e}"
+    assert e_s <= tol, f"state snapshots: max rel err {e_s:.3e}"
+    assert np.array_equal(bits16(tsnap), ref["tail_snap"]), "tail snapshots must match bitwise"
+    return e_o, e_s
+
+
+CASES = {
+    "step-small": ("step", {}),
+    "window-2b": ("window2b", {}),
+    "ragged-27b": ("ragged27b", {}),
+    "verify-27b-16x16": ("verify27b", {}),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_window_matches_oracle(case):
+    name, _ = CASES[case]
+    shape, lengths, kw = gi.workload(name)
+    b = gi.make_batch(shape, lengths, **kw)
+    announce(f"recur_window {case} lengths={lengths} seed={kw['seed']}")
+    out, tsnap, ssnap = run_window(b)
+    e_o, e_s = check_against_oracle(b, out, tsnap, ssnap)
+    print(f"{case}: o err {e_o:.2e}, snapshot err {e_s:.2e}")
+
+
+def test_window_long_memory():
+    shape, lengths, kw = gi.workload("ragged27b")
+    b = gi.make_batch(shape, lengths[:6], long_memory=True, **kw)
+    announce(f"recur_window long-memory lengths={lengths[:6]}")
+    out, tsnap, ssnap = run_window(b)
+    check_against_oracle(b, out, tsnap, ssnap)
+
+
+def test_tree_matches_oracle_and_commit():
+    shape, lengths, kw = gi.workload("tree27b")
+    b = gi.make_batch(shape, lengths, **kw)
+    announce(f"recur_tree tree27b seed={kw['seed']}")
+    d = device_batch(b)
+    out, tsnap, ssnap = run_window(b, tree=True, d=d)
+    check_against_oracle(b, out, tsnap, ssnap, tree=True)
+    # commit each stream's accepted leaf (one stream keeps its state)
+    acc = b.accept.clone()
+    acc[3] = -1
+    tail, state = d["tail"].clone(), d["state"].clone()
+    announce("commit tree27b")
+    gdn.commit(shape, acc.cuda(), tsnap, ssnap, tail, state)
+    torch.cuda.synchronize()
+    for s in range(b.n):
+        if acc[s] < 0:
+            assert torch.equal(state[s], d["state"][s]) and torch.equal(tail[s], d["tail"][s])
+        else:
+            r = int(acc[s])
+            assert torch.equal(state[s], ssnap[r]), s
+            assert np.array_equal(bits16(tail[s]), bits16(tsnap[r])), s
+
+
+@pytest.mark.parametrize("name,n_streams", [("step", 1), ("window2b", 1), ("ragged27b", 3)])
+def test_window_rows_equal_one_row_steps_bitwise(name, n_streams):
+    shape, lengths, kw = gi.workload(name)
+    lengths = lengths[:n_streams] if name != "step" else [5]
+    b = gi.make_batch(shape, lengths, **kw)
+    announce(f"window vs steps {name} lengths={lengths}")
+    d = device_batch(b)
+    out, tsnap, ssnap = run_window(b, d=d)
+    rs = b.row_start.tolist()
+    for s in range(b.n):
+        tail = d["tail"][s:s + 1].clone()
+        state = d["state"][s:s + 1].clone()
+        o1 = torch.empty((1, shape.hv, shape.dv), dtype=torch.float32, device="cuda")
+        for t in range(rs[s + 1] - rs[s]):
+            r = rs[s] + t
+            gdn.conv_step(shape, d["params"], d["qkv"][r:r + 1], d["a"][r:r + 1], d["b"][r:r + 1],
+                          tail, state, o1)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits32(o1[0]), bits32(out[r])), (s, t, "o")
+            assert np.array_equal(bits32(state[0]), bits32(ssnap[r])), (s, t, "state")
+            assert np.array_equal(bits16(tail[0]), bits16(tsnap[r])), (s, t, "tail")
+
+
+def test_step_matches_oracle_many_streams():
+    shape = gi.QWEN_27B
+    b = gi.make_batch(shape, [1] * 16, seed=77)
+    announce("conv_step 16 streams 27b")
+    d = device_batch(b)
+    out = torch.full((16, shape.hv, shape.dv), float("nan"), device="cuda")
+    tail, state = d["tail"].clone(), d["state"].clone()
+    gdn.conv_step(shape, d["params"], d["qkv"], d["a"], d["b"], tail, state, out)
+    torch.cuda.synchronize()
+    ref = oracle_rows(b)
+    assert max_rel_err(out.cpu().numpy(), ref["o"], 1) <= TOL_ROWS
+    assert max_rel_err(state.cpu().numpy(), ref["snap32"], 2) <= TOL_ROWS
+    assert np.array_equal(bits16(tail), ref["tail_snap"])
+
+
+def test_tree_paths_equal_chains_bitwise():
+    shape, lengths, kw = gi.workload("tree27b")
+    b = gi.make_batch(shape, lengths[:4], **kw)
+    announce("tree paths vs chains 27b, 4 streams")
+    out, tsnap, ssnap = run_window(b, tree=True)
+    par = b.parent.tolist()
+    rs = b.row_start.tolist()
+    for s in range(b.n):
+        local = par[rs[s]:rs[s + 1]]
+        for leaf in range(len(local)):
+            rows = [rs[s] + i for i in gi.path_to_root(local, leaf)]
+            chain = gi.Batch(shape=shape, params=b.params,
+                             row_start=torch.tensor([0, len(rows)], dtype=torch.int32),
+                             qkv=b.qkv[rows], a=b.a[rows], b=b.b[rows], tail=b.tail[s:s + 1],
+                             state=b.state[s:s + 1])
+            co, ct, cs = run_window(chain)
+            assert np.array_equal(bits32(co), bits32(out[rows])), (s, leaf)
+            assert np.array_equal(bits32(cs), bits32(ssnap[rows])), (s, leaf)
+            assert np.array_equal(bits16(ct), bits16(tsnap[rows])), (s, leaf)
+
+
+def test_packed_equals_solo_bitwise():
+    """A stream's rows do not depend on the other streams of the pass nor on
+    its packing offset."""
+    shape, lengths, kw = gi.workload("ragged27b")
+    b = gi.make_batch(shape, lengths[:5], **kw)
+    announce(f"packed vs solo lengths={lengths[:5]}")
+    out, tsnap, ssnap = run_window(b)
+    rs = b.row_start.tolist()
+    for s in (0, 2, 4):
+        rows = list(range(rs[s], rs[s + 1]))
+        solo = gi.Batch(shape=shape, params=b.params,
+                        row_start=torch.tensor([0, len(rows)], dtype=torch.int32),
+                        qkv=b.qkv[rows], a=b.a[rows], b=b.b[rows], tail=b.tail[s:s + 1],
+                        state=b.state[s:s + 1])
+        so, st, ss = run_window(solo)
+        assert np.array_equal(bits32(so), bits32(out[rows]))
+        assert np.array_equal(bits32(ss), bits32(ssnap[rows]))
+        assert np.array_equal(bits16(st), bits16(tsnap[rows]))
+
+
+def test_empty_streams_and_zero_rows():
+    shape = gi.QWEN_27B
+    b = gi.make_batch(shape, [3, 0, 16, 0, 1], seed=5)
+    announce("windows with empty streams")
+    out, tsnap, ssnap = run_window(b)
+    check_against_oracle(b, out, tsnap, ssnap)
+    # a call with no rows at all does nothing
+    e = gi.make_batch(shape, [0, 0], seed=6)
+    d = device_batch(e)
+    o, t, s = poisoned_outputs(shape, 0)
+    gdn.recur_window(shape, d["params"], d["row_start"], d["qkv"], d["a"], d["b"], d["tail"],
+                     d["state"], o, t, s)
+    torch.cuda.synchronize()
+
+
+def test_device_layout_breaking_rules_is_skipped():
+    """A window longer than max_rows is skipped by the kernel's own check: its
+    outputs stay poisoned and the other streams are unaffected."""
+    shape = gi.SMALL
+    b = gi.make_batch(shape, [4, 9, 2], seed=21)
+    announce("window longer than max_rows is skipped")
+    out, tsnap, ssnap = run_window(b, max_rows=8)
+    assert torch.isnan(out[4:13]).all() and torch.isnan(ssnap[4:13]).all()
+    ref = oracle_rows(b)
+    keep = list(range(0, 4)) + list(range(13, 15))
+    assert max_rel_err(out.cpu().numpy()[keep], ref["o"][keep], 1) <= TOL_ROWS
+    # a tree row whose parent is not an earlier row: that stream is skipped
+    t = gi.make_batch(shape, [3, 3], seed=22, tree=True)
+    t.parent[4] = 1   # stream 1, row 1 names itself
+    out, tsnap, ssnap = run_window(t, tree=True)
+    assert torch.isnan(out[3:6]).all()
+    assert not torch.isnan(out[0:3]).any()
+
+
+def test_special_cases_through_the_kernels():
+    """alpha = 1 and beta = 1 (A_log = -inf, b = +inf) with q's channels equal
+    to k's: each row writes v at key khat and reads it back, o = v / sqrt(dk);
+    beta = 0 (b = -inf) and A_log = 0 with a + dt_bias = 0 halve the state each
+    row."""
+    shape = gi.Shape(hk=4, hv=8, dk=128, dv=64)
+    b = gi.make_batch(shape, [6, 3], seed=23)
+    hkdk = shape.hk * shape.dk
+    b.params.a_log[:] = -float("inf")
+    b.b[:] = float("inf")
+    b.qkv[:, :hkdk] = b.qkv[:, hkdk:2 * hkdk]
+    b.tail[:, :, :hkdk] = b.tail[:, :, hkdk:2 * hkdk]
+    b.params.conv_w[:hkdk] = b.params.conv_w[hkdk:2 * hkdk]
+    announce("unit write read-back")
+    out, tsnap, ssnap = run_window(b)
+    check_against_oracle(b, out, tsnap, ssnap)
+    ref = oracle_rows(b)
+    assert max_rel_err(out.cpu().numpy(), ref["o"], 1) <= 1e-4
+
+    c = gi.make_batch(shape, [5], seed=24)
+    c.params.a_log[:] = 0.0
+    c.params.dt_bias[:] = 0.25
+    c.a[:] = -0.25
+    c.b[:] = -float("inf")
+    announce("pure decay")
+    out, tsnap, ssnap = run_window(c)
+    for t in range(5):
+        expect = c.state[0] * 0.5 ** (t + 1)
+        assert torch.allclose(ssnap[t].cpu(), expect, rtol=1e-6, atol=0)

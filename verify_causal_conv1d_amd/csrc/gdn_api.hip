@@ -1,0 +1,344 @@
+// Host side of libgdn's C ABI: argument checks, launch configuration, and
+// launches on the caller's stream.  Declarations and contracts are in
+// include/libgdn.h.  Nothing here allocates device memory or keeps state
+// between calls.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/libgdn.h"
+#include "gdn_internal.h"
+#include "gdn_prefill.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const gdn_shape *s)
+{
+    if (!s) return fail(GDN_EINVAL, "shape is NULL");
+    if (s->hk <= 0 || s->hv <= 0 || s->dk <= 0 || s->dv <= 0 || s->conv_width <= 0)
+        return fail(GDN_EINVAL, "shape sizes must be positive (hk=%d hv=%d dk=%d dv=%d conv_width=%d)",
+                    s->hk, s->hv, s->dk, s->dv, s->conv_width);
+    if (s->hv % s->hk != 0)
+        return fail(GDN_EINVAL, "hv (%d) must be a multiple of hk (%d)", s->hv, s->hk);
+    if (s->conv_width != 4) return fail(GDN_EUNSUPPORTED, "conv_width %d: only 4 is supported", s->conv_width);
+    if (s->dk != 64 && s->dk != 128) return fail(GDN_EUNSUPPORTED, "dk %d: only 64 and 128 are supported", s->dk);
+    if (s->dv != 64 && s->dv != 128) return fail(GDN_EUNSUPPORTED, "dv %d: only 64 and 128 are supported", s->dv);
+    const long long C = 2LL * s->hk * s->dk + (long long)s->hv * s->dv;
+    if (C > (1LL << 24)) return fail(GDN_EUNSUPPORTED, "too many channels (%lld)", C);
+    return GDN_OK;
+}
+
+int check_params(const gdn_params *p)
+{
+    if (!p) return fail(GDN_EINVAL, "params is NULL");
+    if (!p->conv_w || !p->a_log || !p->dt_bias) return fail(GDN_EINVAL, "a parameter pointer is NULL");
+    if (!aligned16(p->conv_w)) return fail(GDN_EINVAL, "conv_w must be 16-byte aligned");
+    return GDN_OK;
+}
+
+#define REQUIRE_PTR(p)                                                                  \
+    do {                                                                                \
+        if (!(p)) return fail(GDN_EINVAL, "%s is NULL", #p);                            \
+        if (!aligned16(p)) return fail(GDN_EINVAL, "%s must be 16-byte aligned", #p);   \
+    } while (0)
+
+// Value heads per workgroup: the largest divisor of r whose workgroup stays
+// within 8 waves (512 threads).  LIBGDN_HEADS_PER_BLOCK overrides it (a
+// tuning knob; it must divide r and fit the limit).
+int heads_per_block(int r, int dv)
+{
+    const int waves_per_head = dv / 64;
+    int best = 1;
+    for (int v = 1; v <= r; ++v)
+        if (r % v == 0 && v * waves_per_head <= 8) best = v;
+    if (const char *e = getenv("LIBGDN_HEADS_PER_BLOCK")) {
+        const int v = atoi(e);
+        if (v >= 1 && r % v == 0 && v * waves_per_head <= 8) best = v;
+    }
+    return best;
+}
+
+gdn::RowsArgs rows_args(const gdn_shape *s, const gdn_params *p)
+{
+    gdn::RowsArgs A = {};
+    A.hk = s->hk;
+    A.hv = s->hv;
+    A.dk = s->dk;
+    A.dv = s->dv;
+    A.C = 2 * s->hk * s->dk + s->hv * s->dv;
+    A.r = s->hv / s->hk;
+    A.conv_w = p->conv_w;
+    A.a_log = p->a_log;
+    A.dt_bias = p->dt_bias;
+    return A;
+}
+
+int launched(hipError_t e)
+{
+    if (e != hipSuccess) return fail(GDN_EHIP, "launch failed: %s", hipGetErrorString(e));
+    g_err[0] = '\0';
+    return GDN_OK;
+}
+
+int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
+                   int32_t total_rows, int32_t max_rows, const int32_t *row_start,
+                   const int32_t *parent, bool tree, const uint16_t *qkv, const uint16_t *a,
+                   const uint16_t *b, const uint16_t *conv_tail, const float *state, float *out,
+                   uint16_t *tail_snap, float *state_snap, void *stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    rc = check_params(params);
+    if (rc) return rc;
+    if (n_streams < 0) return fail(GDN_EINVAL, "n_streams %d is negative", n_streams);
+    if (total_rows < 0) return fail(GDN_EINVAL, "total_rows %d is negative", total_rows);
+    if (max_rows < 1 || max_rows > GDN_MAX_WINDOW_ROWS)
+        return fail(GDN_EINVAL, "max_rows %d is outside 1..%d", max_rows, GDN_MAX_WINDOW_ROWS);
+    if ((long long)total_rows > (long long)n_streams * max_rows)
+        return fail(GDN_EINVAL, "total_rows %d exceeds n_streams * max_rows", total_rows);
+    if (n_streams == 0 || total_rows == 0) {
+        g_err[0] = '\0';
+        return GDN_OK;  // nothing to do
+    }
+    if (!row_start) return fail(GDN_EINVAL, "row_start is NULL");
+    if (tree && !parent) return fail(GDN_EINVAL, "parent is NULL");
+    REQUIRE_PTR(qkv);
+    if (!a || !b) return fail(GDN_EINVAL, "a or b is NULL");
+    REQUIRE_PTR(conv_tail);
+    REQUIRE_PTR(state);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(tail_snap);
+    REQUIRE_PTR(state_snap);
+    gdn::RowsArgs A = rows_args(shape, params);
+    A.vpw = heads_per_block(A.r, A.dv);
+    A.n_streams = n_streams;
+    A.total_rows = total_rows;
+    A.max_rows = max_rows;
+    A.mode = tree ? gdn::MODE_TREE : gdn::MODE_WINDOW;
+    A.row_start = row_start;
+    A.parent = parent;
+    A.qkv = qkv;
+    A.a = a;
+    A.b = b;
+    A.tail_in = conv_tail;
+    A.state_in = state;
+    A.out = out;
+    A.tail_snap = tail_snap;
+    A.state_snap = state_snap;
+    if ((long long)n_streams * A.hk * (A.r / A.vpw) > 0x7fffffffLL)
+        return fail(GDN_EUNSUPPORTED, "too many streams for one launch");
+    return launched(gdn::launch_rows(A, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_name(int status)
+{
+    switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_EINVAL: return "GDN_EINVAL";
+    case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED";
+    case GDN_EWORKSPACE: return "GDN_EWORKSPACE";
+    case GDN_EHIP: return "GDN_EHIP";
+    default: return "GDN_UNKNOWN";
+    }
+}
+
+const char *gdn_last_error(void) { return g_err; }
+
+int32_t gdn_channels(const gdn_shape *shape)
+{
+    if (check_shape(shape) != GDN_OK) return -1;
+    return 2 * shape->hk * shape->dk + shape->hv * shape->dv;
+}
+
+int gdn_conv_step(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
+                  const uint16_t *qkv, const uint16_t *a, const uint16_t *b, uint16_t *conv_tail,
+                  float *state, float *out, void *stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    rc = check_params(params);
+    if (rc) return rc;
+    if (n_streams < 0) return fail(GDN_EINVAL, "n_streams %d is negative", n_streams);
+    const int r = shape->hv / shape->hk;
+    if (r * (shape->dv / 64) > 8)
+        return fail(GDN_EUNSUPPORTED, "one-row steps need (hv/hk) * dv <= 512 (got %d * %d)", r, shape->dv);
+    if (n_streams == 0) {
+        g_err[0] = '\0';
+        return GDN_OK;
+    }
+    REQUIRE_PTR(qkv);
+    if (!a || !b) return fail(GDN_EINVAL, "a or b is NULL");
+    REQUIRE_PTR(conv_tail);
+    REQUIRE_PTR(state);
+    REQUIRE_PTR(out);
+    gdn::RowsArgs A = rows_args(shape, params);
+    A.vpw = A.r;  // one workgroup per key head: it alone reads and rewrites those tail channels
+    A.n_streams = n_streams;
+    A.total_rows = n_streams;
+    A.max_rows = 1;
+    A.mode = gdn::MODE_STEP;
+    A.qkv = qkv;
+    A.a = a;
+    A.b = b;
+    A.tail_in = conv_tail;
+    A.tail_out = conv_tail;
+    A.state_in = state;
+    A.state_out = state;
+    A.out = out;
+    return launched(gdn::launch_rows(A, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_recur_window(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
+                     int32_t total_rows, int32_t max_rows, const int32_t *row_start,
+                     const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                     const uint16_t *conv_tail, const float *state, float *out,
+                     uint16_t *tail_snap, float *state_snap, void *stream)
+{
+    return window_or_tree(shape, params, n_streams, total_rows, max_rows, row_start, nullptr, false,
+                          qkv, a, b, conv_tail, state, out, tail_snap, state_snap, stream);
+}
+
+int gdn_recur_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
+                   int32_t total_rows, int32_t max_rows, const int32_t *row_start,
+                   const int32_t *parent, const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                   const uint16_t *conv_tail, const float *state, float *out, uint16_t *tail_snap,
+                   float *state_snap, void *stream)
+{
+    return window_or_tree(shape, params, n_streams, total_rows, max_rows, row_start, parent, true,
+                          qkv, a, b, conv_tail, state, out, tail_snap, state_snap, stream);
+}
+
+int gdn_commit(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,
+               const int32_t *accept_row, const uint16_t *tail_snap, const float *state_snap,
+               uint16_t *conv_tail, float *state, void *stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (n_streams < 0) return fail(GDN_EINVAL, "n_streams %d is negative", n_streams);
+    if (total_rows < 0) return fail(GDN_EINVAL, "total_rows %d is negative", total_rows);
+    if (n_streams > 65535) return fail(GDN_EUNSUPPORTED, "at most 65535 streams a commit");
+    if (n_streams == 0 || total_rows == 0) {
+        g_err[0] = '\0';
+        return GDN_OK;
+    }
+    if (!accept_row) return fail(GDN_EINVAL, "accept_row is NULL");
+    REQUIRE_PTR(tail_snap);
+    REQUIRE_PTR(state_snap);
+    REQUIRE_PTR(conv_tail);
+    REQUIRE_PTR(state);
+    gdn::CommitArgs A = {};
+    A.n_streams = n_streams;
+    A.total_rows = total_rows;
+    A.state_elems = (size_t)shape->hv * shape->dk * shape->dv;
+    A.tail_elems = 3 * (size_t)(2 * shape->hk * shape->dk + shape->hv * shape->dv);
+    A.accept = accept_row;
+    A.tail_snap = tail_snap;
+    A.state_snap = state_snap;
+    A.tail = conv_tail;
+    A.state = state;
+    return launched(gdn::launch_commit(A, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int32_t n_seqs, int32_t total_rows)
+{
+    if (check_shape(shape) != GDN_OK || n_seqs < 0 || total_rows < 0) return 0;
+    return gdn::prefill_workspace_bytes(shape->hk, shape->hv, shape->dk, shape->dv, n_seqs, total_rows);
+}
+
+int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_t n_seqs,
+                        int32_t total_rows, int32_t max_len, const int32_t *seq_start,
+                        const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                        uint16_t *conv_tail, float *state, float *out, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    rc = check_params(params);
+    if (rc) return rc;
+    if (n_seqs < 0) return fail(GDN_EINVAL, "n_seqs %d is negative", n_seqs);
+    if (total_rows < 0) return fail(GDN_EINVAL, "total_rows %d is negative", total_rows);
+    if (max_len < 0) return fail(GDN_EINVAL, "max_len %d is negative", max_len);
+    if (n_seqs == 0 || total_rows == 0) {
+        g_err[0] = '\0';
+        return GDN_OK;
+    }
+    if (max_len == 0) return fail(GDN_EINVAL, "max_len is 0 but total_rows is %d", total_rows);
+    if ((long long)max_len > total_rows) return fail(GDN_EINVAL, "max_len exceeds total_rows");
+    if (!gdn::prefill_supported(shape->hk, shape->hv, shape->dk, shape->dv))
+        return fail(GDN_EUNSUPPORTED, "chunked prompt passes need dk == dv == 128 and hv/hk <= 8");
+    if (!seq_start) return fail(GDN_EINVAL, "seq_start is NULL");
+    REQUIRE_PTR(qkv);
+    if (!a || !b) return fail(GDN_EINVAL, "a or b is NULL");
+    REQUIRE_PTR(conv_tail);
+    REQUIRE_PTR(state);
+    REQUIRE_PTR(out);
+    const size_t need = gdn::prefill_workspace_bytes(shape->hk, shape->hv, shape->dk, shape->dv, n_seqs,
+                                                     total_rows);
+    if (!workspace || workspace_bytes < need)
+        return fail(GDN_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(GDN_EINVAL, "workspace must be 16-byte aligned");
+    gdn::PrefillArgs P = {};
+    P.hk = shape->hk;
+    P.hv = shape->hv;
+    P.dk = shape->dk;
+    P.dv = shape->dv;
+    P.C = 2 * shape->hk * shape->dk + shape->hv * shape->dv;
+    P.n_seqs = n_seqs;
+    P.total_rows = total_rows;
+    P.max_len = max_len;
+    P.seq_start = seq_start;
+    P.qkv = qkv;
+    P.a = a;
+    P.b = b;
+    P.conv_w = params->conv_w;
+    P.a_log = params->a_log;
+    P.dt_bias = params->dt_bias;
+    P.conv_tail = conv_tail;
+    P.state = state;
+    P.out = out;
+    P.workspace = workspace;
+    return launched(gdn::launch_prefill(P, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_check_layout(int32_t n_streams, int32_t total_rows, int32_t max_rows,
+                     const int32_t *row_start_host, const int32_t *parent_host)
+{
+    if (n_streams < 0 || total_rows < 0) return fail(GDN_EINVAL, "negative count");
+    if (max_rows < 1 || max_rows > GDN_MAX_WINDOW_ROWS)
+        return fail(GDN_EINVAL, "max_rows %d is outside 1..%d", max_rows, GDN_MAX_WINDOW_ROWS);
+    if (n_streams == 0) return GDN_OK;
+    if (!row_start_host) return fail(GDN_EINVAL, "row_start is NULL");
+    if (row_start_host[0] < 0) return fail(GDN_EINVAL, "row_start[0] = %d is negative", row_start_host[0]);
+    for (int s = 0; s < n_streams; ++s) {
+        const int r0 = row_start_host[s], r1 = row_start_host[s + 1];
+        if (r1 < r0) return fail(GDN_EINVAL, "row_start decreases at stream %d", s);
+        if (r1 > total_rows) return fail(GDN_EINVAL, "stream %d ends past total_rows", s);
+        if (r1 - r0 > max_rows) return fail(GDN_EINVAL, "stream %d has %d rows > max_rows %d", s, r1 - r0, max_rows);
+        if (parent_host)
+            for (int t = 0; t < r1 - r0; ++t) {
+                const int p = parent_host[r0 + t];
+                if (p < -1 || p >= t)
+                    return fail(GDN_EINVAL, "stream %d row %d: parent %d is not in [-1, %d)", s, t, p, t);
+            }
+    }
+    g_err[0] = '\0';
+    return GDN_OK;
+}
+
+}  // extern "C"

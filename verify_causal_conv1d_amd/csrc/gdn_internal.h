@@ -1,0 +1,54 @@
+// Internal declarations shared by libgdn's host layer and its kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum RowsMode : int32_t {
+    MODE_WINDOW = 0,  // chain windows, every row recorded
+    MODE_TREE = 1,    // tree windows, every row recorded
+    MODE_STEP = 2,    // one row per stream, state and tail updated in place
+};
+
+// Everything one launch of the row kernel needs (passed by value).
+struct RowsArgs {
+    int32_t hk, hv, dk, dv, C;
+    int32_t r;          // value heads per key head
+    int32_t vpw;        // value heads handled by one workgroup (divides r)
+    int32_t n_streams, total_rows, max_rows;
+    int32_t mode;
+    const int32_t *row_start;  // [n+1] (unused in MODE_STEP)
+    const int32_t *parent;     // [total_rows] (MODE_TREE only)
+    const uint16_t *qkv, *a, *b;
+    const float *conv_w, *a_log, *dt_bias;
+    const uint16_t *tail_in;
+    uint16_t *tail_out;        // MODE_STEP: in place (== tail_in)
+    const float *state_in;
+    float *state_out;          // MODE_STEP: in place (== state_in)
+    float *out;
+    uint16_t *tail_snap;       // [total_rows][3][C] (window / tree)
+    float *state_snap;         // [total_rows][hv][dk][dv] (window / tree)
+};
+
+struct CommitArgs {
+    int32_t n_streams, total_rows;
+    size_t state_elems;   // hv * dk * dv
+    size_t tail_elems;    // 3 * C
+    const int32_t *accept;
+    const uint16_t *tail_snap;
+    const float *state_snap;
+    uint16_t *tail;
+    float *state;
+};
+
+// Threads of one row-kernel workgroup and its dynamic LDS bytes.
+int rows_block_threads(const RowsArgs &A);
+size_t rows_lds_bytes(const RowsArgs &A);
+
+hipError_t launch_rows(const RowsArgs &A, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs &A, hipStream_t stream);
+
+}  // namespace gdn
