@@ -139,6 +139,8 @@ int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
     A.state_snap = state_snap;
     if ((long long)n_streams * A.hk * (A.r / A.vpw) > 0x7fffffffLL)
         return fail(GDN_EUNSUPPORTED, "too many streams for one launch");
+    if (gdn::rows_lds_bytes(A) > gdn::kRowsMaxLds)
+        return fail(GDN_EUNSUPPORTED, "window needs %zu bytes of LDS", gdn::rows_lds_bytes(A));
     return launched(gdn::launch_rows(A, static_cast<hipStream_t>(stream)));
 }
 

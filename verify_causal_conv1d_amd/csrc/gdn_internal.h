@@ -44,6 +44,9 @@ struct CommitArgs {
     float *state;
 };
 
+// LDS one row-kernel workgroup may use (gfx950 has 160 KiB a CU).
+constexpr size_t kRowsMaxLds = 160 * 1024;
+
 // Threads of one row-kernel workgroup and its dynamic LDS bytes.
 int rows_block_threads(const RowsArgs &A);
 size_t rows_lds_bytes(const RowsArgs &A);

@@ -3,10 +3,13 @@
 //
 // One workgroup serves one stream and `vpw` value heads of one key head.
 //
-//   prologue  every (row, channel) of the window: causal conv (taps along the
-//             row's own branch) + SiLU into LDS; gates per (row, value head);
-//             then per row an L2 norm of q and of k (q also times dk^-1/2).
-//             Raw tail rows are copied to the tail snapshots here.
+//   prologue  the raw bf16 rows of the window and the stream's tail (only the
+//             workgroup's channels) and the conv weights are staged in LDS
+//             with 16-byte loads issued together, so the prologue pays one
+//             global latency; then every (row, channel): causal conv (taps
+//             along the row's own branch) + SiLU, from LDS; gates per (row,
+//             value head); per row an L2 norm of q and of k (q also times
+//             dk^-1/2).  Tail snapshots are 16-byte copies out of the staged rows.
 //   rows      each wave owns 64 columns of one value head's state M = S^T
 //             ([dk][dv], dv contiguous).  Lane (c, g) = (lane & 15, lane >> 4)
 //             keeps rows [g*dk/4, (g+1)*dk/4) x columns [4c, 4c+4) of the
@@ -29,6 +32,8 @@
 namespace gdn {
 namespace {
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16f(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
 
 // softplus(x) = log(1 + e^x) without overflow or cancellation.
@@ -36,7 +41,9 @@ __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + l
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-__device__ __forceinline__ float silu_f(float y) { return y / (1.0f + expf(-y)); }
+// SiLU of a conv output: y * sigmoid(y), with the hardware exp2 and
+// reciprocal (within a few ulp, well inside the fp32 path's error budget).
+__device__ __forceinline__ float silu_f(float y) { return y * __frcp_rn(1.0f + __expf(-y)); }
 
 // Sum over the four 16-lane rows of the wave; every lane gets the same bits.
 // permlane16_swap pairs rows (0,1) and (2,3), permlane32_swap the two halves.
@@ -58,6 +65,17 @@ __device__ __forceinline__ float sum_wave(float x)
     x = x + __shfl_xor(x, 4);
     x = x + __shfl_xor(x, 8);
     return sum_rows4(x);
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load and store of the thread (its fence covers
+// global memory), which here would hold each barrier on the state loads and
+// the snapshot stores in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Global channel of local prologue channel `ch`: [q of kh | k of kh | v of
@@ -101,14 +119,18 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     const int len = r1 - r0;
     if (len == 0) return;
 
-    const int nch = 2 * DK + A.vpw * A.dv;
-    float *act = smem;                                 // [max_rows][nch]
-    float *galpha = act + A.max_rows * nch;            // [max_rows][vpw]
-    float *gbeta = galpha + A.max_rows * A.vpw;        // [max_rows][vpw]
-    int *anc = reinterpret_cast<int *>(gbeta + A.max_rows * A.vpw);  // [max_rows][4]
-    int *bad = anc + A.max_rows * 4;
+    const int nch = 2 * DK + A.vpw * A.dv;   // channels of this workgroup
+    const int mr = A.max_rows;
+    // LDS (every 16-byte-accessed array starts 16-byte aligned: nch % 64 == 0)
+    float *act = smem;                                              // [mr][nch] conv+SiLU, then q^, k^
+    float4 *wl = reinterpret_cast<float4 *>(act + mr * nch);        // [nch] conv weights
+    uint16_t *raw = reinterpret_cast<uint16_t *>(wl + nch);         // [3 + mr][nch] raw bf16 rows
+    float *galpha = reinterpret_cast<float *>(raw + (3 + mr) * nch);  // [mr][vpw]
+    float *gbeta = galpha + mr * A.vpw;                             // [mr][vpw]
+    int *anc = reinterpret_cast<int *>(gbeta + mr * A.vpw);         // [mr][4]
+    int *bad = anc + mr * 4;
 
-    // ---- this wave's tile of the state: issue its loads first
+    // ---- this wave's tile of the state
     const int waves_per_head = A.dv / 64;
     const int jl = wave / waves_per_head;       // local value head
     const int tile = wave - jl * waves_per_head;
@@ -117,19 +139,16 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     const int col = tile * 64 + c4 * 4;
     const size_t head_elems = (size_t)DK * A.dv;
     const size_t lane_off = (size_t)(grp * R) * A.dv + col;
-    const float *st_in = A.state_in + ((size_t)s * A.hv + h) * head_elems + lane_off;
-    float4 m[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in + (size_t)i * A.dv);
+    const float *st_in_head = A.state_in + ((size_t)s * A.hv + h) * head_elems + lane_off;
 
     // ---- parents and the three nearest ancestors of every row.  anc[t][0]
     // is the parent (whose state row t starts from); anc[t][d] is the source
     // of x_{t-d}: a local row >= 0, or -1, -2, -3 for tail rows 2, 1, 0.
     if (tid == 0) *bad = 0;
     if (tid < len) anc[tid * 4] = (A.mode == MODE_TREE) ? A.parent[r0 + tid] : tid - 1;
-    __syncthreads();
+    lds_barrier();
     if (tid < len && (anc[tid * 4] < -1 || anc[tid * 4] >= tid)) *bad = 1;
-    __syncthreads();
+    lds_barrier();
     if (*bad) return;
     if (tid < len) {
         int i = tid;
@@ -139,63 +158,123 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
             anc[tid * 4 + d] = i;
         }
     }
-    __syncthreads();
 
-    // ---- conv + SiLU of every (row, channel); tail snapshots
+    // ---- stage raw rows (tail rows 0..2, then window rows), conv weights and
+    // gates.  Raw row 3 + a holds x of local row a (a = -3..-1: the tail).
+    // These loads are issued before the state loads: loads retire in order,
+    // so the prologue waits only for what it needs.
     const int C = A.C;
     const uint16_t *tail = A.tail_in + (size_t)s * 3 * C;
     const uint16_t *rows = A.qkv + (size_t)r0 * C;
-    const bool record = (A.mode != MODE_STEP);
-    for (int idx = tid; idx < len * nch; idx += nthr) {
-        const int t = idx / nch;
-        const int ch = idx - t * nch;
-        const int gc = global_channel(A, DK, kh, h0, ch);
-        const int a1 = anc[t * 4 + 1], a2 = anc[t * 4 + 2], a3 = anc[t * 4 + 3];
-        const uint16_t x3 = rows[(size_t)t * C + gc];
-        const uint16_t x2 = a1 >= 0 ? rows[(size_t)a1 * C + gc] : tail[(3 + a1) * C + gc];
-        const uint16_t x1 = a2 >= 0 ? rows[(size_t)a2 * C + gc] : tail[(3 + a2) * C + gc];
-        const uint16_t x0 = a3 >= 0 ? rows[(size_t)a3 * C + gc] : tail[(3 + a3) * C + gc];
-        const float4 w = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)gc * 4);
-        float y = w.x * bf16f(x0);
-        y = fmaf(w.y, bf16f(x1), y);
-        y = fmaf(w.z, bf16f(x2), y);
-        y = fmaf(w.w, bf16f(x3), y);
-        act[t * nch + ch] = silu_f(y);
-        // q/k channels are shared by the key head's workgroups: group 0 records them
-        if (record && (ch >= 2 * DK || g == 0)) {
-            uint16_t *ts = A.tail_snap + (size_t)(r0 + t) * 3 * C + gc;
-            ts[0] = x1;
-            ts[C] = x2;
-            ts[2 * C] = x3;
+    const int cpr = nch / 8;                     // 16-byte chunks a row
+    {
+        // every load of the batch is issued before any of them is consumed
+        const int nchunks = (len + 3) * cpr;
+        const int ngates = len * A.vpw;
+        constexpr int B = 8, BW = 2;             // row chunks / weights in flight per thread
+        for (int base = 0, wbase = 0, gbase = 0; base < nchunks || wbase < nch || gbase < ngates;
+             base += B * nthr, wbase += BW * nthr, gbase += nthr) {
+            uint4 v[B];
+            float4 w[BW];
+#pragma unroll
+            for (int k = 0; k < B; ++k) {
+                const int idx = base + k * nthr + tid;
+                if (idx < nchunks) {
+                    const int rr = idx / cpr;
+                    const int lc = (idx - rr * cpr) * 8;
+                    const int gc = global_channel(A, DK, kh, h0, lc);
+                    const uint16_t *src = rr < 3 ? tail + (size_t)rr * C + gc : rows + (size_t)(rr - 3) * C + gc;
+                    v[k] = *reinterpret_cast<const uint4 *>(src);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < BW; ++k) {
+                const int ch = wbase + k * nthr + tid;
+                if (ch < nch)
+                    w[k] = *reinterpret_cast<const float4 *>(A.conv_w +
+                                                             (size_t)global_channel(A, DK, kh, h0, ch) * 4);
+            }
+            const int gi = gbase + tid;
+            float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
+            if (gi < ngates) {
+                const int t = gi / A.vpw;
+                const int hh = h0 + (gi - t * A.vpw);
+                av = bf16f(A.a[(size_t)(r0 + t) * A.hv + hh]);
+                bv = bf16f(A.b[(size_t)(r0 + t) * A.hv + hh]);
+                al = A.a_log[hh];
+                db = A.dt_bias[hh];
+            }
+#pragma unroll
+            for (int k = 0; k < B; ++k) {
+                const int idx = base + k * nthr + tid;
+                if (idx < nchunks) {
+                    const int rr = idx / cpr;
+                    const int lc = (idx - rr * cpr) * 8;
+                    *reinterpret_cast<uint4 *>(raw + rr * nch + lc) = v[k];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < BW; ++k) {
+                const int ch = wbase + k * nthr + tid;
+                if (ch < nch) wl[ch] = w[k];
+            }
+            if (gi < ngates) {
+                // gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+                galpha[gi] = expf(-expf(al) * softplus_f(av + db));
+                gbeta[gi] = sigmoid_f(bv);
+            }
         }
     }
-    // ---- gates of every (row, value head)
-    for (int idx = tid; idx < len * A.vpw; idx += nthr) {
-        const int t = idx / A.vpw;
-        const int j = idx - t * A.vpw;
-        const int hh = h0 + j;
-        const float av = bf16f(A.a[(size_t)(r0 + t) * A.hv + hh]);
-        const float bv = bf16f(A.b[(size_t)(r0 + t) * A.hv + hh]);
-        const float gl = -expf(A.a_log[hh]) * softplus_f(av + A.dt_bias[hh]);
-        galpha[t * A.vpw + j] = expf(gl);
-        gbeta[t * A.vpw + j] = sigmoid_f(bv);
-    }
-    __syncthreads();
 
-    // ---- one-row step: the new tail replaces the old one in place.  All of
-    // this workgroup's tail reads are behind the barrier above, and (with one
-    // workgroup per key head in this mode) no other workgroup reads these
-    // channels.
-    if (A.mode == MODE_STEP) {
-        uint16_t *tl = A.tail_out + (size_t)s * 3 * C;
-        for (int ch = tid; ch < nch; ch += nthr) {
-            const int gc = global_channel(A, DK, kh, h0, ch);
-            const uint16_t t1 = tl[C + gc], t2 = tl[2 * C + gc];
-            tl[gc] = t1;
-            tl[C + gc] = t2;
-            tl[2 * C + gc] = rows[gc];
+    // ---- the state tile: its loads stay in flight through the prologue
+    float4 m[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
+    lds_barrier();
+
+    // ---- conv + SiLU of every (row, channel), from the staged rows; a thread
+    // walks the rows of one channel, so its iterations are independent
+    for (int ch = tid; ch < nch; ch += nthr) {
+        const float4 w = wl[ch];
+        const uint16_t *rc = raw + ch;
+#pragma unroll 4
+        for (int t = 0; t < len; ++t) {
+            const int a1 = anc[t * 4 + 1], a2 = anc[t * 4 + 2], a3 = anc[t * 4 + 3];
+            float y = w.x * bf16f(rc[(3 + a3) * nch]);
+            y = fmaf(w.y, bf16f(rc[(3 + a2) * nch]), y);
+            y = fmaf(w.z, bf16f(rc[(3 + a1) * nch]), y);
+            y = fmaf(w.w, bf16f(rc[(3 + t) * nch]), y);
+            act[t * nch + ch] = silu_f(y);
         }
     }
+    // ---- tail snapshots: the tail after row t is (x_{t-2}, x_{t-1}, x_t);
+    // q/k channels are shared by the key head's workgroups, group 0 records them
+    if (A.mode != MODE_STEP) {
+        const int c_first = (g == 0) ? 0 : (2 * DK) / 8;
+        const int cw = cpr - c_first;
+        for (int idx = tid; idx < len * 3 * cw; idx += nthr) {
+            const int tj = idx / cw;
+            const int lc = (c_first + idx - tj * cw) * 8;
+            const int t = tj / 3, j = tj - t * 3;
+            const int src_row = 3 + (j == 2 ? t : anc[t * 4 + 2 - j]);
+            const int gc = global_channel(A, DK, kh, h0, lc);
+            *reinterpret_cast<uint4 *>(A.tail_snap + ((size_t)(r0 + t) * 3 + j) * C + gc) =
+                *reinterpret_cast<const uint4 *>(raw + src_row * nch + lc);
+        }
+    } else {
+        // one-row step: the new tail replaces the old one in place.  The old
+        // tail is staged in LDS, and with one workgroup per key head in this
+        // mode no other workgroup reads these channels.
+        uint16_t *tl = A.tail_out + (size_t)s * 3 * C;
+        for (int idx = tid; idx < 3 * cpr; idx += nthr) {
+            const int j = idx / cpr;
+            const int lc = (idx - j * cpr) * 8;
+            const int gc = global_channel(A, DK, kh, h0, lc);
+            *reinterpret_cast<uint4 *>(tl + (size_t)j * C + gc) =
+                *reinterpret_cast<const uint4 *>(raw + (j + 1) * nch + lc);
+        }
+    }
+    lds_barrier();
 
     // ---- L2 norms of q and k per row (q also scaled by dk^-1/2)
     {
@@ -218,10 +297,9 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
             if (DK == 128) v[lane + 64] = x1 * sc;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- the recurrence, row after row, on the tile held in registers
-    const float *st_in_head = A.state_in + ((size_t)s * A.hv + h) * head_elems + lane_off;
     int prev = -1;
     for (int t = 0; t < len; ++t) {
         const int p = anc[t * 4];
@@ -296,8 +374,13 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
         float *dst = (A.mode == MODE_STEP)
                          ? A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off
                          : A.state_snap + ((size_t)row * A.hv + h) * head_elems + lane_off;
+        // snapshots are streamed out (non-temporal): nothing in this launch
+        // rereads them except a tree's parent reload
 #pragma unroll
-        for (int i = 0; i < R; ++i) *reinterpret_cast<float4 *>(dst + (size_t)i * A.dv) = m[i];
+        for (int i = 0; i < R; ++i) {
+            const f4v val = {m[i].x, m[i].y, m[i].z, m[i].w};
+            __builtin_nontemporal_store(val, reinterpret_cast<f4v *>(dst + (size_t)i * A.dv));
+        }
         prev = t;
     }
 }
@@ -325,15 +408,34 @@ int rows_block_threads(const RowsArgs &A) { return 64 * A.vpw * (A.dv / 64); }
 size_t rows_lds_bytes(const RowsArgs &A)
 {
     const size_t nch = 2 * (size_t)A.dk + (size_t)A.vpw * A.dv;
-    return sizeof(float) * ((size_t)A.max_rows * nch + 2 * (size_t)A.max_rows * A.vpw) +
-           sizeof(int) * (4 * (size_t)A.max_rows + 1);
+    const size_t mr = A.max_rows;
+    return sizeof(float) * mr * nch                  // act
+           + sizeof(float) * 4 * nch                 // conv weights
+           + sizeof(uint16_t) * (3 + mr) * nch       // raw rows
+           + sizeof(float) * 2 * mr * A.vpw          // gates
+           + sizeof(int) * (4 * mr + 1);             // ancestors, flag
 }
+
+namespace {
+// Dynamic LDS above the 64 KiB default has to be allowed per kernel once.
+template <int DK>
+hipError_t allow_lds()
+{
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&rows_kernel<DK>),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    (int)kRowsMaxLds);
+    return e;
+}
+}  // namespace
 
 hipError_t launch_rows(const RowsArgs &A, hipStream_t stream)
 {
     const dim3 grid((unsigned)A.n_streams * A.hk * (A.r / A.vpw));
     const dim3 block(rows_block_threads(A));
     const size_t lds = rows_lds_bytes(A);
+    if (lds > kRowsMaxLds) return hipErrorInvalidValue;
+    const hipError_t e = (A.dk == 128) ? allow_lds<128>() : allow_lds<64>();
+    if (e != hipSuccess) return e;
     if (A.dk == 128)
         hipLaunchKernelGGL(rows_kernel<128>, grid, block, lds, stream, A);
     else
