@@ -93,3 +93,23 @@ def bits16(t: torch.Tensor) -> np.ndarray:
 
 def bits32(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int32).cpu().numpy()
+
+
+def max_rel_err_segments(gpu: np.ndarray, ref: np.ndarray, starts) -> float:
+    """Outputs of a prompt pass: for each prompt (rows starts[i]..starts[i+1]),
+    max |gpu - ref| over its rows, heads and columns divided by max |ref| over
+    the same, then the maximum over prompts.  The bf16 operands of the chunked
+    form leave an absolute error of a few 1e-3 of the terms a readout sums, so
+    a row whose outputs all cancel (|o| far below the prompt's typical
+    magnitude) has no meaningful relative error of its own."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    if not np.all(np.isfinite(g)):
+        return float("inf")
+    worst = 0.0
+    st = list(starts)
+    for i in range(len(st) - 1):
+        a, b = st[i], st[i + 1]
+        if b > a:
+            worst = max(worst, float(np.abs(g[a:b] - r[a:b]).max() / max(np.abs(r[a:b]).max(), 1e-30)))
+    return worst

@@ -149,6 +149,19 @@ def test_prefill_refusals(L):
     assert call(n=0, total=0, seq=None) == gdn.GDN_OK
     small = _shape(hk=2, hv=4, dk=64, dv=64)
     assert call(shape=small) == gdn.GDN_EUNSUPPORTED
+    assert call(wsb=1) == gdn.GDN_EWORKSPACE
+    assert call(ws=None) == gdn.GDN_EWORKSPACE
+    assert call(ws=P_ODD) == gdn.GDN_EINVAL
+
+
+def test_prefill_workspace_bytes(L):
+    sh = _shape()
+    need = L.gdn_prefill_workspace_bytes(C.byref(sh), 4, 8306)
+    # q/k, v, W, U~ (bf16), P (bf16, 64 a row) and three fp32 per-row gates
+    T, hk, hv, d = 8306, 16, 48, 128
+    lower = T * (hk * 2 * d * 2 + hv * d * 2 * 3 + hv * 64 * 2 + hv * 4 * 3)
+    assert lower <= need <= lower + 8 * 256
+    assert L.gdn_prefill_workspace_bytes(C.byref(_shape(dk=64)), 4, 100) == 0
 
 
 def test_check_layout(L):

@@ -1,0 +1,133 @@
+"""GPU parity of the chunked prompt pass (bf16 matrix-core operands, fp32
+state) against the oracle's row-by-row recurrence, within 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from verify_causal_conv1d_amd import gdn
+from verify_causal_conv1d_amd import inputs as gi
+
+from gpu_util import TOL_PREFILL, announce, bits16, host_batch, max_rel_err, max_rel_err_segments
+
+pytestmark = pytest.mark.gpu
+
+SMALL_27B_HEADS = gi.Shape(hk=2, hv=6, dk=128, dv=128)   # 3 value heads a key head
+
+
+def run_prefill(b: gi.Batch, dev="cuda"):
+    params = gdn.LayerParams.from_host(b.params, dev)
+    seq_start = b.row_start.to(dev)
+    qkv, a, bb = b.qkv.to(dev), b.a.to(dev), b.b.to(dev)
+    tail, state = b.tail.to(dev).clone(), b.state.to(dev).clone()
+    out = torch.full((b.rows, b.shape.hv, b.shape.dv), float("nan"), device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(b.shape, b.n, b.rows), dtype=torch.uint8, device=dev)
+    gdn.prefill_chunked(b.shape, params, seq_start, qkv, a, bb, tail, state, out, ws,
+                        max_len=max(b.lengths()))
+    torch.cuda.synchronize()
+    return out, tail, state
+
+
+def oracle_prefill(b: gi.Batch):
+    h = host_batch(b)
+    return oracle.prefill(b.shape, h["conv_w"], h["a_log"], h["dt_bias"], h["row_start"], h["qkv"],
+                          h["a"], h["b"], h["tail"], h["state"])
+
+
+def check(b: gi.Batch, out, tail, state, tol=TOL_PREFILL):
+    o_ref, st_ref, tl_ref = oracle_prefill(b)
+    o = out.cpu().numpy()
+    e_o = max_rel_err_segments(o, o_ref, b.row_start.tolist())
+    e_s = max_rel_err(state.cpu().numpy(), st_ref, 2)
+    # and no drift: the typical row is well inside the bound
+    if b.rows:
+        num = np.abs(o.astype(np.float64) - o_ref).reshape(b.rows, -1).max(1)
+        den = np.maximum(np.abs(o_ref).reshape(b.rows, -1).max(1), 1e-30)
+        assert np.median(num / den) <= tol / 2, f"median row error {np.median(num / den):.3e}"
+    assert np.array_equal(bits16(tail), tl_ref), "conv tails must match bitwise"
+    assert e_o <= tol, f"o: max rel err {e_o:.3e}"
+    assert e_s <= tol, f"final state: max rel err {e_s:.3e}"
+    return e_o, e_s
+
+
+@pytest.mark.parametrize("zero_state", [False, True])
+def test_prefill_ragged_prompts(zero_state):
+    lengths = [1, 2, 3, 63, 64, 65, 130, 200]
+    b = gi.make_batch(SMALL_27B_HEADS, lengths, seed=31, zero_state=zero_state)
+    announce(f"prefill ragged {lengths} zero_state={zero_state}")
+    out, tail, state = run_prefill(b)
+    e_o, e_s = check(b, out, tail, state)
+    print(f"o err {e_o:.2e}, state err {e_s:.2e}")
+
+
+def test_prefill_long_memory():
+    lengths = [300, 17, 129]
+    b = gi.make_batch(SMALL_27B_HEADS, lengths, seed=32, long_memory=True)
+    announce(f"prefill long memory {lengths}")
+    out, tail, state = run_prefill(b)
+    e_o, e_s = check(b, out, tail, state)
+    print(f"o err {e_o:.2e}, state err {e_s:.2e}")
+
+
+def test_prefill_2b_layer():
+    lengths = [96, 5, 160]
+    b = gi.make_batch(gi.QWEN_2B, lengths, seed=33)
+    announce(f"prefill 2B-like {lengths}")
+    out, tail, state = run_prefill(b)
+    check(b, out, tail, state)
+
+
+def test_prefill_with_empty_prompt():
+    lengths = [70, 0, 33]
+    b = gi.make_batch(SMALL_27B_HEADS, lengths, seed=34)
+    announce(f"prefill with an empty prompt {lengths}")
+    out, tail, state = run_prefill(b)
+    check(b, out, tail, state)
+    assert torch.equal(state[1].cpu(), b.state[1]) and torch.equal(tail[1].cpu(), b.tail[1])
+
+
+def test_prefill_27b_four_prompts():
+    shape, lengths, kw = gi.workload("prefill27b")
+    b = gi.make_batch(shape, lengths, **kw)
+    announce(f"prefill 27B-like {lengths} seed={kw['seed']}")
+    out, tail, state = run_prefill(b)
+    e_o, e_s = check(b, out, tail, state)
+    print(f"27B prefill: o err {e_o:.2e}, state err {e_s:.2e}")
+
+
+def test_prefill_27b_resumed_state():
+    """A non-zero initial state and tail (a resumed prompt) on the 27B-like layer."""
+    shape = gi.QWEN_27B
+    lengths = [700, 64, 1]
+    b = gi.make_batch(shape, lengths, seed=35)
+    announce(f"prefill 27B-like resumed {lengths}")
+    out, tail, state = run_prefill(b)
+    check(b, out, tail, state)
+
+
+def test_prefill_then_steps_continue_the_stream():
+    """A prompt pass followed by one-row steps gives what the recurrence gives
+    for the whole sequence (the steps start from the prefill's state)."""
+    shape = SMALL_27B_HEADS
+    b = gi.make_batch(shape, [90, 4], seed=36)
+    announce("prefill then steps")
+    out, tail, state = run_prefill(b)
+    # continue stream 0 with 3 more rows as steps
+    more = gi.make_batch(shape, [3], seed=37)
+    params = gdn.LayerParams.from_host(b.params, "cuda")
+    o1 = torch.empty((1, shape.hv, shape.dv), device="cuda")
+    tl, st = tail[0:1].clone(), state[0:1].clone()
+    outs = []
+    for t in range(3):
+        gdn.conv_step(shape, params, more.qkv[t:t + 1].cuda(), more.a[t:t + 1].cuda(),
+                      more.b[t:t + 1].cuda(), tl, st, o1)
+        torch.cuda.synchronize()
+        outs.append(o1[0].cpu().numpy().copy())
+    # oracle: the whole 93-row sequence as one prompt
+    whole = gi.Batch(shape=shape, params=b.params, row_start=torch.tensor([0, 93], dtype=torch.int32),
+                     qkv=torch.cat([b.qkv[:90], more.qkv]), a=torch.cat([b.a[:90], more.a]),
+                     b=torch.cat([b.b[:90], more.b]), tail=b.tail[0:1], state=b.state[0:1])
+    o_ref, st_ref, tl_ref = oracle_prefill(whole)
+    assert max_rel_err_segments(np.stack(outs), o_ref[90:93], [0, 3]) <= TOL_PREFILL
+    assert max_rel_err(st.cpu().numpy(), st_ref, 2) <= TOL_PREFILL
+    assert np.array_equal(bits16(tl), tl_ref)

@@ -1,0 +1,71 @@
+// Device helpers shared by libgdn's kernel files (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16f(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (a NaN stays a NaN).
+__device__ __forceinline__ uint16_t f2bf(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// softplus(x) = log(1 + e^x) without overflow or cancellation.
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// log of the per-row decay: g = -exp(A_log) softplus(a + dt_bias), alpha = e^g.
+__device__ __forceinline__ float log_decay(float a, float a_log, float dt_bias)
+{
+    return -expf(a_log) * softplus_f(a + dt_bias);
+}
+
+// SiLU of a conv output: y * sigmoid(y), with the hardware exp2 and
+// reciprocal (within a few ulp, well inside the fp32 path's error budget).
+__device__ __forceinline__ float silu_f(float y) { return y * __frcp_rn(1.0f + __expf(-y)); }
+
+// Sum over the four 16-lane rows of the wave; every lane gets the same bits.
+// permlane16_swap pairs rows (0,1) and (2,3), permlane32_swap the two halves.
+__device__ __forceinline__ float sum_rows4(float x)
+{
+    const uint32_t xi = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+    const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const uint32_t si = __float_as_uint(s);
+    const auto q = __builtin_amdgcn_permlane32_swap(si, si, false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Sum over all 64 lanes (butterfly, the same bits in every lane).
+__device__ __forceinline__ float sum_wave(float x)
+{
+    x = x + __shfl_xor(x, 1);
+    x = x + __shfl_xor(x, 2);
+    x = x + __shfl_xor(x, 4);
+    x = x + __shfl_xor(x, 8);
+    return sum_rows4(x);
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load and store of the thread (its fence covers
+// global memory), which would hold each barrier on loads and stores in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace gdn

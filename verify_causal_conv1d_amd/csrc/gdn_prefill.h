@@ -7,6 +7,8 @@
 
 namespace gdn {
 
+constexpr int kChunk = 64;   // rows of a chunk (chunks never cross prompts)
+
 struct PrefillArgs {
     int32_t hk, hv, dk, dv, C;
     int32_t n_seqs, total_rows, max_len;
@@ -19,6 +21,20 @@ struct PrefillArgs {
     void *workspace;
 };
 
+// Byte offsets of the workspace arrays, all indexed by packed row t:
+//   qk  bf16 [T][hk][2*dk]  q^ (scaled) then k^ of each key head
+//   v   bf16 [T][hv][dv]    SiLU'd values
+//   g   f32  [T][hv]        log alpha
+//   be  f32  [T][hv]        beta
+//   gam f32  [T][hv]        in-chunk cumulative log decay gamma
+//   w   bf16 [T][hv][dk]    W = T (beta e^gamma k^)
+//   u   bf16 [T][hv][dv]    U~ = T (beta v)
+//   p   bf16 [T][hv][64]    P, row t against its chunk's rows (zero above t)
+struct PrefillLayout {
+    size_t qk, v, g, be, gam, w, u, p, total;
+};
+
+PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int total_rows);
 bool prefill_supported(int hk, int hv, int dk, int dv);
 size_t prefill_workspace_bytes(int hk, int hv, int dk, int dv, int n_seqs, int total_rows);
 hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream);

@@ -27,56 +27,11 @@
 // "perf(qwen3_5 cuda): deliver the first token before drafting", commit note
 // on the MLX affine 4-bit checkpoint).  The build disables fp contraction;
 // every fused multiply-add below is written out.
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
-
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16f(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
-
-// softplus(x) = log(1 + e^x) without overflow or cancellation.
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
-
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
-
-// SiLU of a conv output: y * sigmoid(y), with the hardware exp2 and
-// reciprocal (within a few ulp, well inside the fp32 path's error budget).
-__device__ __forceinline__ float silu_f(float y) { return y * __frcp_rn(1.0f + __expf(-y)); }
-
-// Sum over the four 16-lane rows of the wave; every lane gets the same bits.
-// permlane16_swap pairs rows (0,1) and (2,3), permlane32_swap the two halves.
-__device__ __forceinline__ float sum_rows4(float x)
-{
-    const uint32_t xi = __float_as_uint(x);
-    const auto p = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-    const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    const uint32_t si = __float_as_uint(s);
-    const auto q = __builtin_amdgcn_permlane32_swap(si, si, false, false);
-    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
-// Sum over all 64 lanes (butterfly, the same bits in every lane).
-__device__ __forceinline__ float sum_wave(float x)
-{
-    x = x + __shfl_xor(x, 1);
-    x = x + __shfl_xor(x, 2);
-    x = x + __shfl_xor(x, 4);
-    x = x + __shfl_xor(x, 8);
-    return sum_rows4(x);
-}
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
-// every outstanding global load and store of the thread (its fence covers
-// global memory), which here would hold each barrier on the state loads and
-// the snapshot stores in flight.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Global channel of local prologue channel `ch`: [q of kh | k of kh | v of
 // the workgroup's value heads].
@@ -220,7 +175,7 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
             }
             if (gi < ngates) {
                 // gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
-                galpha[gi] = expf(-expf(al) * softplus_f(av + db));
+                galpha[gi] = expf(log_decay(av, al, db));
                 gbeta[gi] = sigmoid_f(bv);
             }
         }
