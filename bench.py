@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0     # MI355X dense bf16 matrix peak, published
+MFMA_FP32_PEAK_TFS = 157.3      # MI355X fp32 matrix peak, published
 
 
 def window_bytes(shape, n, rows):
@@ -37,6 +38,24 @@ def window_bytes(shape, n, rows):
             + rows * shape.hv * 2 * 2    # a, b in
             + rows * shape.hv * shape.dv * 4   # o out
             + C * 4 * 4 + 2 * shape.hv * 4)    # conv weights, A_log, dt_bias
+
+
+def prefill_flops(shape, lengths, chunk=64):
+    """Algorithmic flops of one chunked prompt pass, counted on the actual
+    chunk lengths L: bf16 matrix-core products K K^T and Q K^T (per key head),
+    T (beta e^gamma K) and T (beta V) (per value head); fp32 state contractions
+    W M0, (e^gamma Q) M0, (e^{gamma_L - gamma} K)^T U (2 L dk dv each) and P U
+    (2 L^2 dv), per value head."""
+    dk, dv = shape.dk, shape.dv
+    sum_l = sum_l2 = 0
+    for n in lengths:
+        for c0 in range(0, n, chunk):
+            L = min(chunk, n - c0)
+            sum_l += L
+            sum_l2 += L * L
+    bf16 = shape.hk * 2 * (2 * sum_l2 * dk) + shape.hv * (2 * sum_l2 * dk + 2 * sum_l2 * dv)
+    fp32 = shape.hv * (3 * 2 * sum_l * dk * dv + 2 * sum_l2 * dv)
+    return bf16, fp32
 
 
 def measured_traffic(key):
@@ -60,7 +79,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="verify27b", choices=["verify27b", "tree27b", "ragged27b"])
+    ap.add_argument("--workload", default="verify27b",
+                    choices=["verify27b", "tree27b", "ragged27b", "prefill27b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -84,6 +104,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.workload == "prefill27b":
+        return bench_prefill(args, torch, gdn, gi, dev)
 
     shape, lengths, kw = gi.workload(args.workload)
     tree = args.workload == "tree27b"
@@ -182,6 +205,100 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def timed(torch, dev, step, steps, warmup):
+    """Warm-up, then per-launch events on torch's current stream (where libgdn
+    launches) and the wall clock of the whole timed region."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return wall, sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def bench_prefill(args, torch, gdn, gi, dev):
+    """One step = one chunked prompt pass over the four packed prompts."""
+    shape, lengths, kw = gi.workload("prefill27b")
+    b = gi.make_batch(shape, lengths, **kw)
+    params = gdn.LayerParams.from_host(b.params, dev)
+    seq_start = b.row_start.to(dev)
+    qkv, a, bb = b.qkv.to(dev), b.a.to(dev), b.b.to(dev)
+    tail, state = b.tail.to(dev), b.state.to(dev)
+    out = torch.empty((b.rows, shape.hv, shape.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(shape, b.n, b.rows), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.prefill_chunked(shape, params, seq_start, qkv, a, bb, tail, state, out, ws,
+                            max_len=max(lengths))
+
+    wall, avg_ms, med_ms = timed(torch, dev, step, args.steps, args.warmup)
+    f_bf16, f_fp32 = prefill_flops(shape, lengths)
+    ideal_s = f_bf16 / (MFMA_BF16_PEAK_TFS * 1e12) + f_fp32 / (MFMA_FP32_PEAK_TFS * 1e12)
+    fp32_equiv = f_fp32 + f_bf16 * MFMA_FP32_PEAK_TFS / MFMA_BF16_PEAK_TFS
+    achieved = fp32_equiv / (avg_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_prefill(b, args.cpu_seconds)
+    line = {
+        "metric": "GDN layer prefill tokens/s (chunked prompt pass)",
+        "value": round(b.rows * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 matrix operands, f32 state", "data": "synthetic",
+        "config": {"workload": "4 prompts of 512, 1024, 2048 and 4722 rows packed in one pass, chunk 64",
+                   "layer": {"hk": shape.hk, "hv": shape.hv, "dk": shape.dk, "dv": shape.dv,
+                             "conv_width": 4},
+                   "prompts": lengths, "rows": b.rows, "seed": kw["seed"]},
+        "pass_ms_avg": round(avg_ms, 5), "pass_ms_median": round(med_ms, 5),
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFS,
+            "unit": "TFLOP/s", "frac": round(ideal_s / (avg_ms * 1e-3), 4), "traffic": None,
+            "kernel": "whole pass (prologue, intra, sweep)",
+            "flops_bf16": f_bf16, "flops_fp32": f_fp32,
+            "note": "achieved counts bf16 flops at the fp32/bf16 peak ratio; frac = ideal time "
+                    "(bf16 flops at 2.5 PF + fp32 flops at 157.3 TF) over the measured pass",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_prefill(b, budget_s):
+    """The oracle's recurrent prompt pass on a bounded sample: the first
+    ``n`` rows of the 512-row prompt, grown until about budget_s seconds."""
+    import numpy as np
+    import oracle
+    from verify_causal_conv1d_amd import inputs as gi
+    h = dict(conv_w=b.params.conv_w.numpy(), a_log=b.params.a_log.numpy(),
+             dt_bias=b.params.dt_bias.numpy(), qkv=gi.bf16_bits(b.qkv), a=gi.bf16_bits(b.a),
+             b=gi.bf16_bits(b.b), tail=gi.bf16_bits(b.tail), state=b.state.numpy().astype(np.float64))
+    rows, el = 0, 0.0
+    n = 64
+    while el < budget_s and n <= b.rows:
+        ss = np.array([0, n], np.int32)
+        t0 = time.perf_counter()
+        oracle.prefill(b.shape, h["conv_w"], h["a_log"], h["dt_bias"], ss, h["qkv"][:n], h["a"][:n],
+                       h["b"][:n], h["tail"][:1], h["state"][:1])
+        el += time.perf_counter() - t0
+        rows += n
+        n *= 2
+    return {"value": round(rows / el, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": f"recurrent prompt passes of 64, 128, ... rows ({rows} rows in all), "
+                                        f"fp64, {el:.1f} s wall"}
 
 
 def cpu_baseline(b, tree, budget_s):

@@ -156,10 +156,14 @@ def test_prefill_refusals(L):
 
 def test_prefill_workspace_bytes(L):
     sh = _shape()
-    need = L.gdn_prefill_workspace_bytes(C.byref(sh), 4, 8306)
-    # q/k, v, W, U~ (bf16), P (bf16, 64 a row) and three fp32 per-row gates
-    T, hk, hv, d = 8306, 16, 48, 128
-    lower = T * (hk * 2 * d * 2 + hv * d * 2 * 3 + hv * 64 * 2 + hv * 4 * 3)
+    n, T, hk, hv, d = 4, 8306, 16, 48, 128
+    need = L.gdn_prefill_workspace_bytes(C.byref(sh), n, T)
+    # per row: q^/k^ and v (bf16), log alpha and beta (fp32); per chunk and
+    # value head (at most T/64 + n chunks): the sweep's bf16 operand block
+    # (W, e^gamma q^, e^{gamma_L - gamma} k^: 64 x 128 each; P: 64 x 64;
+    # U~: 64 x 128) and e^{gamma_L} (fp32)
+    nc = T // 64 + n
+    lower = T * (hk * 2 * d * 2 + hv * d * 2 + hv * 4 * 2) + nc * hv * ((4 * 64 * d + 64 * 64) * 2 + 4)
     assert lower <= need <= lower + 8 * 256
     assert L.gdn_prefill_workspace_bytes(C.byref(_shape(dk=64)), 4, 100) == 0
 

@@ -21,20 +21,22 @@ struct PrefillArgs {
     void *workspace;
 };
 
-// Byte offsets of the workspace arrays, all indexed by packed row t:
+// Byte offsets of the workspace arrays.  Per packed row t:
 //   qk  bf16 [T][hk][2*dk]  q^ (scaled) then k^ of each key head
 //   v   bf16 [T][hv][dv]    SiLU'd values
 //   g   f32  [T][hv]        log alpha
 //   be  f32  [T][hv]        beta
-//   gam f32  [T][hv]        in-chunk cumulative log decay gamma
-//   w   bf16 [T][hv][dk]    W = T (beta e^gamma k^)
-//   u   bf16 [T][hv][dv]    U~ = T (beta v)
-//   p   bf16 [T][hv][64]    P, row t against its chunk's rows (zero above t)
+// Per chunk (dense index over the prompts' chunks, at most T/64 + n_seqs) and
+// value head, the sweep's matrix-core operands, each already in the lane order
+// the sweep's MFMAs read:
+//   blk bf16 [NC][hv][kBlockElems]  W, e^gamma q^, e^{gamma_L - gamma} k^, P, U~
+//   el  f32  [NC][hv]               e^{gamma_L} of the chunk
 struct PrefillLayout {
-    size_t qk, v, g, be, gam, w, u, p, total;
+    size_t qk, v, g, be, blk, el, total;
+    int max_chunks_total;
 };
 
-PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int total_rows);
+PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int n_seqs, int total_rows);
 bool prefill_supported(int hk, int hv, int dk, int dv);
 size_t prefill_workspace_bytes(int hk, int hv, int dk, int dv, int n_seqs, int total_rows);
 hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream);

@@ -17,17 +17,21 @@
 //             gates.  q^, k^, v are stored as bf16 (the matrix-core operand
 //             type), log alpha and beta as fp32.
 //   intra     per (chunk, key head): K K^T and Q K^T on bf16 MFMA
-//             (v_mfma_f32_32x32x16_bf16), then per value head gamma, the
-//             fp32 triangular solve for T (one wave, one column a lane), P,
-//             and W, U~ on bf16 MFMA.  Independent across chunks.
+//             (v_mfma_f32_32x32x16_bf16); per value head gamma, the fp32
+//             triangular solve for T (one wave, one column a lane), and W^T,
+//             U~ on bf16 MFMA.  Everything the sweep needs leaves this kernel
+//             in the exact lane order of the sweep's MFMA operands, so the
+//             sweep reads each operand with two 16-byte loads a lane.
 //   sweep     per (prompt, value head, 32 state columns), 4 waves, each
 //             holding 32 rows of the state as an fp32 MFMA accumulator: the
-//             state contractions U~ - W M0, (e^gamma q) M0, P U and the
-//             update (e^{gamma_L - gamma} k)^T U run on fp32 MFMA
-//             (v_mfma_f32_32x32x2_f32) with the accumulator itself as the
-//             B operand; partial sums over the four row blocks meet in LDS.
-//             Sequential over the prompt's chunks; the state never leaves
-//             the chip between them.
+//             state contractions U~ - W M0, (e^gamma q) M0, P U and the update
+//             (e^{gamma_L - gamma} k)^T U run on fp32 MFMA
+//             (v_mfma_f32_32x32x2_f32) with the accumulator itself as the B
+//             operand; partial sums over the four row blocks meet in LDS.
+//             Sequential over the prompt's chunks, with each operand of chunk
+//             c + 1 fetched right after its last use in chunk c; the state
+//             never leaves the chip between chunks.  Workgroups take prompts
+//             longest first, so the longest dependency chain starts first.
 // The prompt's final state replaces the stream's state and its last three raw
 // rows (or a mix with the old tail for prompts shorter than three rows) its
 // conv tail, in place (prompt passes update the stream in place: page
@@ -42,20 +46,52 @@ namespace {
 constexpr int DKP = 128;        // head sizes this pass is built for
 constexpr int PRO_ROWS = 32;    // packed rows a prologue workgroup
 constexpr int TILE = 32;        // state columns a sweep workgroup
+constexpr int HB = 3;           // value heads whose triangular solves run side by side
+
+// A chunk-head block of sweep operands (bf16), every sub-array in lane order
+// [.][.][64 lanes][16], lane l = (l32, hh) = (l & 31, l >> 5):
+//   W  [mb][w]     lane value i = W[32 mb + l32][32 w + kx(i)]
+//   QE [mb][w]     lane value i = e^{gamma_t} q^[t = 32 mb + l32][32 w + kx(i)]
+//   KT [mb][w]     lane value i = e^{gamma_L - gamma_t} k^[t = 32 mb + kx(i)][32 w + l32]
+//   P  [mb][mbk]   lane value i = P[32 mb + l32][32 mbk + kx(i)]
+//   UT [mb][tile]  lane value i = U~[32 mb + kx(i)][32 tile + l32]
+// with kx(i) = 8 (i / 4) + 4 hh + i % 4: the k index that lane l feeds at step
+// i of a v_mfma_f32_32x32x2_f32 chain whose B operand is register i of a
+// 32 x 32 accumulator (accumulator register i of lane l holds row kx(i),
+// column l32).  Rows past the chunk's end are zero.
+constexpr int kOffW = 0, kOffQE = 8192, kOffKT = 16384, kOffP = 24576, kOffUT = 28672;
+constexpr int kBlockElems = 36864;
 
 struct Ctx {
     PrefillArgs P;
     int r;                      // value heads per key head
-    int max_chunks;             // chunks of the longest prompt
-    uint16_t *qk, *v, *w, *u, *p;
-    float *g, *be, *gam;
+    int max_chunks;             // chunks of the longest prompt (bounds the intra grid)
+    int nc_total;               // chunk blocks in the workspace
+    uint16_t *qk, *v, *blk;
+    float *g, *be, *el;
 };
 
-__device__ __forceinline__ bool prompt_ok(const Ctx &X, int p, int &s0, int &s1)
+__device__ __forceinline__ int kx(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
+
+// Rows of prompt p, and the dense index of its first chunk.  False if p or an
+// earlier prompt breaks the layout rules (monotone starts within [0, T],
+// lengths <= max_len); such a prompt is skipped.
+__device__ bool prompt_chunks(const Ctx &X, int p, int &s0, int &s1, int &cid0)
 {
+    const int T = X.P.total_rows;
+    int base = 0;
+    int prev = X.P.seq_start[0];
+    if (prev < 0) return false;
+    for (int q = 0; q <= p; ++q) {
+        const int a = X.P.seq_start[q], b = X.P.seq_start[q + 1];
+        if (a != prev || b < a || b > T || b - a > X.P.max_len) return false;
+        prev = b;
+        if (q < p) base += (b - a + kChunk - 1) / kChunk;
+    }
     s0 = X.P.seq_start[p];
     s1 = X.P.seq_start[p + 1];
-    return s0 >= 0 && s1 >= s0 && s1 <= X.P.total_rows && s1 - s0 <= X.P.max_len;
+    cid0 = base;
+    return base + (s1 - s0 + kChunk - 1) / kChunk <= X.nc_total;
 }
 
 // Local prologue channel -> global channel: [q of kh | k of kh | v of kh's value heads].
@@ -78,9 +114,10 @@ __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
     const int C = X.P.C;
     const int nch = 2 * DKP + X.r * DKP;
     float *act = smem;                                                    // [PRO_ROWS][2*DKP]
-    uint16_t *raw = reinterpret_cast<uint16_t *>(act + PRO_ROWS * 2 * DKP);  // [PRO_ROWS + 3][nch]
-    int *rstart = reinterpret_cast<int *>(raw + (PRO_ROWS + 3) * nch);     // [PRO_ROWS]
-    int *rprompt = rstart + PRO_ROWS;                                      // [PRO_ROWS]
+    float4 *wl = reinterpret_cast<float4 *>(act + PRO_ROWS * 2 * DKP);    // [nch]
+    uint16_t *raw = reinterpret_cast<uint16_t *>(wl + nch);               // [PRO_ROWS + 3][nch]
+    int *rstart = reinterpret_cast<int *>(raw + (PRO_ROWS + 3) * nch);    // [PRO_ROWS]
+    int *rprompt = rstart + PRO_ROWS;                                     // [PRO_ROWS]
 
     // prompt of each row: the last p with seq_start[p] <= t, if t < seq_start[p + 1]
     if (tid < nrows) {
@@ -90,20 +127,37 @@ __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
             const int mid = (lo + hi + 1) >> 1;
             if (X.P.seq_start[mid] <= t) lo = mid; else hi = mid - 1;
         }
-        int s0, s1;
-        const bool ok = prompt_ok(X, lo, s0, s1) && s0 <= t && t < s1;
+        const int s0 = X.P.seq_start[lo], s1 = X.P.seq_start[lo + 1];
+        const bool ok = s0 >= 0 && s0 <= t && t < s1 && s1 <= T && s1 - s0 <= X.P.max_len;
         rstart[tid] = ok ? s0 : -1;
         rprompt[tid] = lo;
     }
-    // stage raw rows t0-3 .. t0+nrows-1 of this key head's channels
-    const int cpr = nch / 8;
-    for (int idx = tid; idx < (nrows + 3) * cpr; idx += 256) {
-        const int j = idx / cpr;
-        const int lc = (idx - j * cpr) * 8;
-        const int u = t0 - 3 + j;
-        if (u >= 0)
-            *reinterpret_cast<uint4 *>(raw + j * nch + lc) =
-                *reinterpret_cast<const uint4 *>(X.P.qkv + (size_t)u * C + pro_channel(X, kh, lc));
+    // stage raw rows t0-3 .. t0+nrows-1 of this key head's channels, and the weights
+    {
+        const int cpr = nch / 8;
+        const int nchunks = (nrows + 3) * cpr;
+        constexpr int B = 8;
+        for (int base = 0; base < nchunks; base += B * 256) {
+            uint4 v[B];
+#pragma unroll
+            for (int k = 0; k < B; ++k) {
+                const int idx = base + k * 256 + tid;
+                const int j = idx / cpr;
+                const int u = t0 - 3 + j;
+                if (idx < nchunks && u >= 0)
+                    v[k] = *reinterpret_cast<const uint4 *>(X.P.qkv + (size_t)u * C +
+                                                            pro_channel(X, kh, (idx - j * cpr) * 8));
+            }
+#pragma unroll
+            for (int k = 0; k < B; ++k) {
+                const int idx = base + k * 256 + tid;
+                const int j = idx / cpr;
+                if (idx < nchunks && t0 - 3 + j >= 0)
+                    *reinterpret_cast<uint4 *>(raw + j * nch + (idx - j * cpr) * 8) = v[k];
+            }
+        }
+        for (int ch = tid; ch < nch; ch += 256)
+            wl[ch] = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)pro_channel(X, kh, ch) * 4);
     }
     lds_barrier();
 
@@ -116,32 +170,31 @@ __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
         X.g[o] = log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]);
         X.be[o] = sigmoid_f(bf16f(X.P.b[o]));
     }
-    // conv + SiLU: q/k into LDS for the norms, v straight out as bf16
-    for (int idx = tid; idx < nrows * nch; idx += 256) {
-        const int i = idx / nch;
-        const int ch = idx - i * nch;
-        const int rs = rstart[i];
-        if (rs < 0) continue;
-        const int t = t0 + i;
+    // conv + SiLU, a thread walking the rows of one channel: q/k into LDS for
+    // the norms, v straight out as bf16
+    for (int ch = tid; ch < nch; ch += 256) {
+        const float4 w = wl[ch];
         const int gc = pro_channel(X, kh, ch);
-        const float4 w = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)gc * 4);
-        float x[4];
-#pragma unroll
-        for (int d = 3; d >= 0; --d) {
-            const int src = t - d;
-            const uint16_t bits = src >= rs ? raw[(i + 3 - d) * nch + ch]
-                                            : X.P.conv_tail[((size_t)rprompt[i] * 3 + (3 + src - rs)) * C + gc];
-            x[3 - d] = bf16f(bits);
+        for (int i = 0; i < nrows; ++i) {
+            const int rs = rstart[i];
+            if (rs < 0) continue;
+            const int t = t0 + i;
+            // tap j reads x_{t-3+j}: a staged row of this prompt, or its tail
+            const uint16_t *tailc = X.P.conv_tail + (size_t)rprompt[i] * 3 * C + gc;
+            const float x0 = bf16f(t - 3 >= rs ? raw[i * nch + ch] : tailc[(size_t)(t - rs) * C]);
+            const float x1 = bf16f(t - 2 >= rs ? raw[(i + 1) * nch + ch] : tailc[(size_t)(1 + t - rs) * C]);
+            const float x2 = bf16f(t - 1 >= rs ? raw[(i + 2) * nch + ch] : tailc[(size_t)(2 + t - rs) * C]);
+            const float x3 = bf16f(raw[(i + 3) * nch + ch]);
+            float y = w.x * x0;
+            y = fmaf(w.y, x1, y);
+            y = fmaf(w.z, x2, y);
+            y = fmaf(w.w, x3, y);
+            const float a = silu_f(y);
+            if (ch < 2 * DKP)
+                act[i * 2 * DKP + ch] = a;
+            else
+                X.v[(size_t)t * X.P.hv * DKP + (size_t)kh * X.r * DKP + (ch - 2 * DKP)] = f2bf(a);
         }
-        float y = w.x * x[0];
-        y = fmaf(w.y, x[1], y);
-        y = fmaf(w.z, x[2], y);
-        y = fmaf(w.w, x[3], y);
-        const float a = silu_f(y);
-        if (ch < 2 * DKP)
-            act[i * 2 * DKP + ch] = a;
-        else
-            X.v[(size_t)t * X.P.hv * DKP + (size_t)kh * X.r * DKP + (ch - 2 * DKP)] = f2bf(a);
     }
     lds_barrier();
 
@@ -164,16 +217,46 @@ __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
 }
 
 // ---------------------------------------------------------------- intra
-// 8 consecutive bf16 of a workspace row as an MFMA operand (zeros past the chunk).
-__device__ __forceinline__ bf8v load8(const uint16_t *p, bool ok)
-{
-    uint4 raw = ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
-    return __builtin_bit_cast(bf8v, raw);
-}
-
 __device__ __forceinline__ bf8v lds8(const uint16_t *p) { return __builtin_bit_cast(bf8v, *reinterpret_cast<const uint4 *>(p)); }
 
-constexpr int HB = 3;   // value heads whose triangular solves run side by side
+// Row T_ of the forward substitution T (I + A) = I for unit lower-triangular
+// I + A: lane c keeps column c of T; An holds -A (row-major, [64][64]).
+template <int T_>
+__device__ __forceinline__ void tsolve_row(float (&Tc)[64], const float *An, int lane)
+{
+    float acc = (T_ == lane) ? 1.0f : 0.0f;
+    const float *row = An + T_ * 64;
+#pragma unroll
+    for (int s4 = 0; s4 + 4 <= T_; s4 += 4) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(row + s4);
+        acc = fmaf(a4.x, Tc[s4], acc);
+        acc = fmaf(a4.y, Tc[s4 + 1], acc);
+        acc = fmaf(a4.z, Tc[s4 + 2], acc);
+        acc = fmaf(a4.w, Tc[s4 + 3], acc);
+    }
+#pragma unroll
+    for (int s = T_ & ~3; s < T_; ++s) acc = fmaf(row[s], Tc[s], acc);
+    Tc[T_] = acc;
+    // keep the scheduler from hoisting later rows' LDS reads above this one
+    // (it would hold hundreds of them in registers)
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int T_>
+__device__ __forceinline__ void tsolve(float (&Tc)[64], const float *An, int lane)
+{
+    tsolve_row<T_>(Tc, An, lane);
+    if constexpr (T_ + 1 < 64) tsolve<T_ + 1>(Tc, An, lane);
+}
+
+__device__ __forceinline__ void store16(uint16_t *dst, const float (&v)[16])
+{
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = (uint32_t)f2bf(v[2 * e]) | ((uint32_t)f2bf(v[2 * e + 1]) << 16);
+    reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
 
 __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
 {
@@ -182,41 +265,48 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
     const int l32 = lane & 31, hh = lane >> 5;
     const int kh = blockIdx.y;
     const int pidx = blockIdx.x / X.max_chunks, c = blockIdx.x - pidx * X.max_chunks;
-    int s0, s1;
-    if (!prompt_ok(X, pidx, s0, s1)) return;
+    int s0, s1, cid0;
+    if (!prompt_chunks(X, pidx, s0, s1, cid0)) return;
     const int r0 = s0 + c * kChunk;
     if (r0 >= s1) return;
     const int L = min(kChunk, s1 - r0);
     const int hv = X.P.hv, hk = X.P.hk;
 
-    float *Skk = smem;                          // [64][64]
-    float *Sqk = Skk + 64 * 64;                 // [64][64]
-    float *An = Sqk + 64 * 64;                  // [HB][64][64] -A, later KbT / VbT
+    uint16_t *qkr = reinterpret_cast<uint16_t *>(smem);            // [64][256] q^ | k^ rows
+    float *Skk = reinterpret_cast<float *>(qkr + 64 * 2 * DKP);    // [64][64]
+    float *Sqk = Skk + 64 * 64;                                    // [64][64]
+    float *An = Sqk + 64 * 64;                                     // [HB][64][64] -A, later KbT / VbT
     uint16_t *Tb = reinterpret_cast<uint16_t *>(An + HB * 64 * 64);   // [HB][64][64] bf16
     float *gam = reinterpret_cast<float *>(Tb + HB * 64 * 64);       // [HB][64]
     float *bet = gam + HB * 64;                                        // [HB][64]
     uint16_t *KbT = reinterpret_cast<uint16_t *>(An);                  // [128][64]
     uint16_t *VbT = KbT + 128 * 64;                                    // [128][64]
 
+    // the chunk's q^ | k^ rows (zero past its end)
+    for (int idx = tid; idx < 64 * 32; idx += 256) {
+        const int t = idx >> 5, q8 = (idx & 31) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < L) v = *reinterpret_cast<const uint4 *>(X.qk + ((size_t)(r0 + t) * hk + kh) * 2 * DKP + q8);
+        *reinterpret_cast<uint4 *>(qkr + t * 2 * DKP + q8) = v;
+    }
+    lds_barrier();
+
     // K K^T and Q K^T: wave w computes the 32 x 32 block (w >> 1, w & 1) of both
     {
         const int bi = wave >> 1, bj = wave & 1;
-        const int ra = 32 * bi + l32, rb = 32 * bj + l32;
-        const uint16_t *qa = X.qk + ((size_t)(r0 + ra) * hk + kh) * 2 * DKP;
-        const uint16_t *kb = X.qk + ((size_t)(r0 + rb) * hk + kh) * 2 * DKP + DKP;
+        const uint16_t *ra = qkr + (32 * bi + l32) * 2 * DKP;
+        const uint16_t *rb = qkr + (32 * bj + l32) * 2 * DKP + DKP;
         f16v kk = {}, qk = {};
 #pragma unroll
         for (int ks = 0; ks < DKP / 16; ++ks) {
             const int ko = 16 * ks + 8 * hh;
-            const bf8v ak = load8(qa + DKP + ko, ra < L);
-            const bf8v aq = load8(qa + ko, ra < L);
-            const bf8v bk = load8(kb + ko, rb < L);
-            kk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bk, kk, 0, 0, 0);
-            qk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, qk, 0, 0, 0);
+            const bf8v bk = lds8(rb + ko);
+            kk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(ra + DKP + ko), bk, kk, 0, 0, 0);
+            qk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(ra + ko), bk, qk, 0, 0, 0);
         }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            const int row = 32 * bi + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+            const int row = 32 * bi + kx(rr, hh);
             Skk[row * 64 + 32 * bj + l32] = kk[rr];
             Sqk[row * 64 + 32 * bj + l32] = qk[rr];
         }
@@ -237,7 +327,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             }
             gam[wave * 64 + lane] = gl;
             bet[wave * 64 + lane] = bl;
-            if (lane < L) X.gam[o] = gl;
         }
         lds_barrier();
 
@@ -251,88 +340,90 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
                 Aj[t * 64 + s] = t > s ? -bj[t] * __expf(gj[t] - gs) * Skk[t * 64 + s] : 0.0f;
             // T = (I + A)^-1 by forward substitution; lane c keeps column c
             float Tc[64];
-#pragma unroll
-            for (int t = 0; t < 64; ++t) {
-                float acc = (t == lane) ? 1.0f : 0.0f;
-#pragma unroll
-                for (int s4 = 0; s4 < 64; s4 += 4) {
-                    if (s4 < t) {
-                        const float4 a4 = *reinterpret_cast<const float4 *>(Aj + t * 64 + s4);
-                        acc = fmaf(a4.x, Tc[s4], acc);
-                        if (s4 + 1 < t) acc = fmaf(a4.y, Tc[s4 + 1], acc);
-                        if (s4 + 2 < t) acc = fmaf(a4.z, Tc[s4 + 2], acc);
-                        if (s4 + 3 < t) acc = fmaf(a4.w, Tc[s4 + 3], acc);
-                    }
-                }
-                Tc[t] = acc;
-            }
+            tsolve<0>(Tc, Aj, lane);
             uint16_t *Tj = Tb + wave * 64 * 64;
 #pragma unroll
             for (int t = 0; t < 64; ++t) Tj[t * 64 + lane] = f2bf(Tc[t]);
-        } else if (wave == 3) {
-            // P_ts = e^{gamma_t - gamma_s} (q_t . k_s) for s <= t, row `lane`
-            const int t = lane;
-            if (t < L) {
-                for (int jj = 0; jj < nh; ++jj) {
-                    const int h = kh * X.r + j0 + jj;
-                    const float *gj = gam + jj * 64;
-                    const float gt = gj[t];
-                    uint16_t *dst = X.p + ((size_t)(r0 + t) * hv + h) * 64;
-                    for (int s8 = 0; s8 < 64; s8 += 8) {
-                        uint16_t pk[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int s = s8 + e;
-                            pk[e] = s <= t ? f2bf(__expf(gt - gj[s]) * Sqk[t * 64 + s]) : (uint16_t)0;
-                        }
-                        *reinterpret_cast<uint4 *>(dst + s8) = *reinterpret_cast<const uint4 *>(pk);
-                    }
-                }
-            }
         }
         lds_barrier();
 
         for (int jj = 0; jj < nh; ++jj) {
             const int h = kh * X.r + j0 + jj;
             const float *gj = gam + jj * 64, *bj = bet + jj * 64;
+            const float gL = gj[63];
+            uint16_t *blk = X.blk + ((size_t)(cid0 + c) * hv + h) * kBlockElems;
             // KbT[k][s] = beta_s e^{gamma_s} k_s[k],  VbT[c][s] = beta_s v_s[c]
             for (int idx = tid; idx < 64 * 16 * 2; idx += 256) {
                 const int which = idx >= 64 * 16;
                 const int id = idx - which * 64 * 16;
                 const int s = id >> 4, q8 = (id & 15) * 8;
                 uint4 raw = make_uint4(0, 0, 0, 0);
-                if (s < L)
-                    raw = *reinterpret_cast<const uint4 *>(
-                        which ? X.v + ((size_t)(r0 + s) * hv + h) * DKP + q8
-                              : X.qk + ((size_t)(r0 + s) * hk + kh) * 2 * DKP + DKP + q8);
+                if (which && s < L) raw = *reinterpret_cast<const uint4 *>(X.v + ((size_t)(r0 + s) * hv + h) * DKP + q8);
+                if (!which) raw = *reinterpret_cast<const uint4 *>(qkr + s * 2 * DKP + DKP + q8);
                 const uint16_t *e8 = reinterpret_cast<const uint16_t *>(&raw);
                 const float sc = which ? bj[s] : bj[s] * __expf(gj[s]);
                 uint16_t *dst = which ? VbT : KbT;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) dst[(q8 + e) * 64 + s] = f2bf(sc * bf16f(e8[e]));
             }
-            lds_barrier();
-            // W = T Kb and U~ = T Vb: wave w does one 32-row half of one of them
-            {
-                const int which = wave >> 1, bi = wave & 1;
-                const uint16_t *Tj = Tb + jj * 64 * 64;
-                const uint16_t *BT = which ? VbT : KbT;
-                uint16_t *dst = which ? X.u : X.w;
+            // sweep operands formed elementwise: QE, KT (2 x 4 lane slots each) and P (2 x 2)
+            for (int slot = tid; slot < 2 * 4 * 64 * 2 + 2 * 2 * 64; slot += 256) {
+                float vals[16];
+                const int sl = slot & 63, sh = sl >> 5, s32 = sl & 31;
+                if (slot < 2 * 4 * 64) {                       // QE[mb][w][lane]
+                    const int mb = slot >> 8, w = (slot >> 6) & 3;
+                    const int t = 32 * mb + s32;
+                    const float e = __expf(gj[t]);
 #pragma unroll
-                for (int bjc = 0; bjc < 4; ++bjc) {
+                    for (int i = 0; i < 16; ++i) vals[i] = e * bf16f(qkr[t * 2 * DKP + 32 * w + kx(i, sh)]);
+                    store16(blk + kOffQE + (size_t)slot * 16, vals);
+                } else if (slot < 2 * 2 * 4 * 64) {           // KT[mb][w][lane]
+                    const int s2 = slot - 2 * 4 * 64;
+                    const int mb = s2 >> 8, w = (s2 >> 6) & 3;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = 32 * mb + kx(i, sh);
+                        vals[i] = __expf(gL - gj[t]) * bf16f(qkr[t * 2 * DKP + DKP + 32 * w + s32]);
+                    }
+                    store16(blk + kOffKT + (size_t)s2 * 16, vals);
+                } else {                                       // P[mb][mbk][lane]
+                    const int s3 = slot - 2 * 2 * 4 * 64;
+                    const int mb = s3 >> 7, mbk = (s3 >> 6) & 1;
+                    const int t = 32 * mb + s32;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int s = 32 * mbk + kx(i, sh);
+                        vals[i] = (s <= t && t < L) ? __expf(gj[t] - gj[s]) * Sqk[t * 64 + s] : 0.0f;
+                    }
+                    store16(blk + kOffP + (size_t)s3 * 16, vals);
+                }
+            }
+            if (tid == 0) X.el[(size_t)(cid0 + c) * hv + h] = __expf(gL);
+            lds_barrier();
+            // W^T = Kb^T T^T and U~ = T Vb: wave w does 4 of the 16 output blocks
+            {
+                const uint16_t *Tj = Tb + jj * 64 * 64;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int b = wave * 4 + q;              // 0..7: W^T (kb, bi); 8..15: U~ (bi, tile)
+                    const bool isw = b < 8;
+                    const int x = (b & 7) >> 1, y = b & 1;   // W^T: kb = x, bi = y; U~: tile = x, bi = y
                     f16v acc = {};
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
                         const int ko = 16 * ks + 8 * hh;
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(Tj + (32 * bi + l32) * 64 + ko),
-                                                                      lds8(BT + (32 * bjc + l32) * 64 + ko), acc,
-                                                                      0, 0, 0);
+                        const bf8v a = isw ? lds8(KbT + (32 * x + l32) * 64 + ko) : lds8(Tj + (32 * y + l32) * 64 + ko);
+                        const bf8v bb = isw ? lds8(Tj + (32 * y + l32) * 64 + ko) : lds8(VbT + (32 * x + l32) * 64 + ko);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
                     }
+                    float vals[16];
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        const int row = 32 * bi + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-                        if (row < L) dst[((size_t)(r0 + row) * hv + h) * DKP + 32 * bjc + l32] = f2bf(acc[rr]);
-                    }
+                    for (int i = 0; i < 16; ++i) vals[i] = acc[i];
+                    // W^T block (kb, bi): lane l holds W[32 bi + l32][32 kb + kx(i)] = W[mb=bi][w=kb]
+                    // U~ block (bi, tile): lane l holds U~[32 bi + kx(i)][32 tile + l32] = UT[mb=bi][tile]
+                    const size_t off = isw ? kOffW + ((size_t)(y * 4 + x) * 64 + lane) * 16
+                                           : kOffUT + ((size_t)(y * 4 + x) * 64 + lane) * 16;
+                    store16(blk + off, vals);
                 }
             }
             lds_barrier();
@@ -341,13 +432,18 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
 }
 
 // ---------------------------------------------------------------- sweep
-// 4 consecutive bf16 of a workspace row as fp32 (zeros past the chunk).
-__device__ __forceinline__ float4 load4(const uint16_t *p, bool ok)
+__device__ __forceinline__ float bfat(const uint4 (&v)[2], int i)
 {
-    if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
-    const uint2 r = *reinterpret_cast<const uint2 *>(p);
-    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    const uint4 &u = v[i >> 3];
+    const int k = (i & 7) >> 1;
+    const uint32_t w = k == 0 ? u.x : k == 1 ? u.y : k == 2 ? u.z : u.w;
+    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+}
+
+__device__ __forceinline__ void ld2(uint4 (&v)[2], const uint16_t *p)
+{
+    v[0] = reinterpret_cast<const uint4 *>(p)[0];
+    v[1] = reinterpret_cast<const uint4 *>(p)[1];
 }
 
 __device__ __forceinline__ f16v mfma_f32(float a, float b, f16v c)
@@ -360,50 +456,74 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     extern __shared__ float smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int hv = X.P.hv, hk = X.P.hk;
+    const int hv = X.P.hv, n = X.P.n_seqs;
     const int ntile = DKP / TILE;
     const int tile = blockIdx.x % ntile;
     const int h = (blockIdx.x / ntile) % hv;
-    const int pidx = blockIdx.x / (ntile * hv);
-    int s0, s1;
-    if (!prompt_ok(X, pidx, s0, s1)) return;
-    const int len = s1 - s0;
-    const int kh = h / X.r;
-    const int col = tile * TILE + l32;
+    const int slot = blockIdx.x / (ntile * hv);
 
     float *red_u = smem;                     // [4 waves][2][16][64]
     float *red_o = red_u + 4 * 2 * 16 * 64;  // [4 waves][2][16][64]
-    float *gbuf = red_o + 4 * 2 * 16 * 64;   // [2][64]
+    int *order = reinterpret_cast<int *>(red_o + 4 * 2 * 16 * 64);   // [256] prompt of each rank
+
+    // prompts by decreasing length (ties by index), so the longest chains start first
+    int pidx = slot;
+    if (n <= 256) {
+        if (tid < n) {
+            const int len = X.P.seq_start[tid + 1] - X.P.seq_start[tid];
+            int rank = 0;
+            for (int q = 0; q < n; ++q) {
+                const int lq = X.P.seq_start[q + 1] - X.P.seq_start[q];
+                rank += (lq > len) || (lq == len && q < tid);
+            }
+            order[rank] = tid;
+        }
+        lds_barrier();
+        pidx = order[slot];
+    }
+    int s0, s1, cid0;
+    if (!prompt_chunks(X, pidx, s0, s1, cid0)) return;
+    const int len = s1 - s0;
+    const int col = tile * TILE + l32;
 
     // this wave's 32 state rows x 32 columns, in accumulator layout:
-    // register i of lane l is M[32 w + 8 (i / 4) + 4 (l / 32) + i % 4][col]
+    // register i of lane l is M[32 w + kx(i)][col]
     float *st = X.P.state + ((size_t)pidx * hv + h) * DKP * DKP;
     f16v M;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) M[i] = st[(size_t)(32 * wave + 8 * (i >> 2) + 4 * hh + (i & 3)) * DKP + col];
+    for (int i = 0; i < 16; ++i) M[i] = st[(size_t)(32 * wave + kx(i, hh)) * DKP + col];
 
     const int nck = (len + kChunk - 1) / kChunk;
+    const size_t cstride = (size_t)hv * kBlockElems;
+    const uint16_t *blk = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
+    const int mbk = wave >> 1, i0 = 8 * (wave & 1);
+    // this lane's operands of the current chunk
+    uint4 Wo[2][2], QEo[2][2], KTo[2][2], UTo[2][2], Po[2];
+    if (nck > 0) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            ld2(Wo[mb], blk + kOffW + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+            ld2(UTo[mb], blk + kOffUT + ((size_t)(mb * 4 + tile) * 64 + lane) * 16);
+            ld2(QEo[mb], blk + kOffQE + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+            Po[mb] = *reinterpret_cast<const uint4 *>(blk + kOffP + ((size_t)(mb * 2 + mbk) * 64 + lane) * 16 + i0);
+            ld2(KTo[mb], blk + kOffKT + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+        }
+    }
     for (int c = 0; c < nck; ++c) {
         const int r0 = s0 + c * kChunk;
         const int L = min(kChunk, s1 - r0);
-        float *gb = gbuf + (c & 1) * 64;
-        if (wave == 0) gb[lane] = X.gam[(size_t)(r0 + min(lane, L - 1)) * hv + h];
+        const bool more = c + 1 < nck;
+        const uint16_t *bn = blk + (size_t)(c + 1) * cstride;
+        const float eL = X.el[(size_t)(cid0 + c) * hv + h];
 
-        // partial of W M0 over this wave's 32 state rows (chunk rows 32 mb + l % 32)
+        // partial of W M0 over this wave's 32 state rows
         f16v up[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int row = 32 * mb + l32;
-            const uint16_t *wr = X.w + ((size_t)(r0 + row) * hv + h) * DKP + 32 * wave + 4 * hh;
             up[mb] = f16v{};
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const float4 a4 = load4(wr + 8 * g4, row < L);
-                up[mb] = mfma_f32(a4.x, M[4 * g4 + 0], up[mb]);
-                up[mb] = mfma_f32(a4.y, M[4 * g4 + 1], up[mb]);
-                up[mb] = mfma_f32(a4.z, M[4 * g4 + 2], up[mb]);
-                up[mb] = mfma_f32(a4.w, M[4 * g4 + 3], up[mb]);
-            }
+            for (int i = 0; i < 16; ++i) up[mb] = mfma_f32(bfat(Wo[mb], i), M[i], up[mb]);
+            if (more) ld2(Wo[mb], bn + kOffW + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
 #pragma unroll
             for (int i = 0; i < 16; ++i) red_u[((wave * 2 + mb) * 16 + i) * 64 + lane] = up[mb][i];
         }
@@ -412,45 +532,31 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         // U = U~ - W M0 (every wave keeps all of it, in accumulator layout)
         f16v U[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
                 float s = red_u[((0 * 2 + mb) * 16 + i) * 64 + lane];
                 s += red_u[((1 * 2 + mb) * 16 + i) * 64 + lane];
                 s += red_u[((2 * 2 + mb) * 16 + i) * 64 + lane];
                 s += red_u[((3 * 2 + mb) * 16 + i) * 64 + lane];
-                const float ut = row < L ? bf16f(X.u[((size_t)(r0 + row) * hv + h) * DKP + col]) : 0.0f;
-                U[mb][i] = ut - s;
+                U[mb][i] = bfat(UTo[mb], i) - s;
             }
+            if (more) ld2(UTo[mb], bn + kOffUT + ((size_t)(mb * 4 + tile) * 64 + lane) * 16);
+        }
 
         // partial of O: (e^gamma q) M0 over this wave's state rows, plus a quarter of P U
         f16v op[2];
-        const int mbk = wave >> 1, i0 = 8 * (wave & 1);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int row = 32 * mb + l32;
-            const bool ok = row < L;
-            const float eg = __expf(gb[row]);
-            const uint16_t *qr = X.qk + ((size_t)(r0 + row) * hk + kh) * 2 * DKP + 32 * wave + 4 * hh;
             op[mb] = f16v{};
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const float4 a4 = load4(qr + 8 * g4, ok);
-                op[mb] = mfma_f32(eg * a4.x, M[4 * g4 + 0], op[mb]);
-                op[mb] = mfma_f32(eg * a4.y, M[4 * g4 + 1], op[mb]);
-                op[mb] = mfma_f32(eg * a4.z, M[4 * g4 + 2], op[mb]);
-                op[mb] = mfma_f32(eg * a4.w, M[4 * g4 + 3], op[mb]);
-            }
-            const uint16_t *pr = X.p + ((size_t)(r0 + row) * hv + h) * 64 + 32 * mbk + 4 * hh;
+            for (int i = 0; i < 16; ++i) op[mb] = mfma_f32(bfat(QEo[mb], i), M[i], op[mb]);
+            const uint4 pv[2] = {Po[mb], Po[mb]};
 #pragma unroll
-            for (int g4 = 0; g4 < 2; ++g4) {
-                const int i = i0 + 4 * g4;
-                const float4 a4 = load4(pr + 8 * (i >> 2), ok);
-                op[mb] = mfma_f32(a4.x, U[mbk][i + 0], op[mb]);
-                op[mb] = mfma_f32(a4.y, U[mbk][i + 1], op[mb]);
-                op[mb] = mfma_f32(a4.z, U[mbk][i + 2], op[mb]);
-                op[mb] = mfma_f32(a4.w, U[mbk][i + 3], op[mb]);
+            for (int i = 0; i < 8; ++i) op[mb] = mfma_f32(bfat(pv, i), U[mbk][i0 + i], op[mb]);
+            if (more) {
+                ld2(QEo[mb], bn + kOffQE + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+                Po[mb] = *reinterpret_cast<const uint4 *>(bn + kOffP + ((size_t)(mb * 2 + mbk) * 64 + lane) * 16 + i0);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) red_o[((wave * 2 + mb) * 16 + i) * 64 + lane] = op[mb][i];
@@ -460,7 +566,7 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         // O rows: wave w sums the four partials of registers [i0, i0 + 8) of block mbk
 #pragma unroll
         for (int i = i0; i < i0 + 8; ++i) {
-            const int row = 32 * mbk + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const int row = 32 * mbk + kx(i, hh);
             float s = red_o[((0 * 2 + mbk) * 16 + i) * 64 + lane];
             s += red_o[((1 * 2 + mbk) * 16 + i) * 64 + lane];
             s += red_o[((2 * 2 + mbk) * 16 + i) * 64 + lane];
@@ -469,22 +575,17 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         }
 
         // M <- e^{gamma_L} M0 + (e^{gamma_L - gamma} k)^T U on this wave's rows
-        const float gL = gb[L - 1];
-        const float eL = __expf(gL);
 #pragma unroll
         for (int i = 0; i < 16; ++i) M[i] *= eL;
-        const uint16_t *kc = X.qk + (size_t)kh * 2 * DKP + DKP + 32 * wave + l32;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                const float a = row < L ? __expf(gL - gb[row]) * bf16f(kc[(size_t)(r0 + row) * hk * 2 * DKP]) : 0.0f;
-                M = mfma_f32(a, U[mb][i], M);
-            }
+            for (int i = 0; i < 16; ++i) M = mfma_f32(bfat(KTo[mb], i), U[mb][i], M);
+            if (more) ld2(KTo[mb], bn + kOffKT + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+        }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st[(size_t)(32 * wave + 8 * (i >> 2) + 4 * hh + (i & 3)) * DKP + col] = M[i];
+    for (int i = 0; i < 16; ++i) st[(size_t)(32 * wave + kx(i, hh)) * DKP + col] = M[i];
 
     // the prompt's conv tail: its last three raw rows, continuing into the old
     // tail when the prompt is shorter (one workgroup a prompt, read then write)
@@ -504,9 +605,18 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     }
 }
 
-size_t prologue_lds(int r) { return sizeof(float) * PRO_ROWS * 2 * DKP + sizeof(uint16_t) * (PRO_ROWS + 3) * (2 + r) * DKP + sizeof(int) * 2 * PRO_ROWS; }
-size_t intra_lds() { return sizeof(float) * (2 * 64 * 64 + HB * 64 * 64 + 2 * HB * 64) + sizeof(uint16_t) * HB * 64 * 64; }
-size_t sweep_lds() { return sizeof(float) * (2 * 4 * 2 * 16 * 64 + 2 * 64); }
+size_t prologue_lds(int r)
+{
+    const size_t nch = (size_t)(2 + r) * DKP;
+    return sizeof(float) * PRO_ROWS * 2 * DKP + sizeof(float) * 4 * nch +
+           sizeof(uint16_t) * (PRO_ROWS + 3) * nch + sizeof(int) * 2 * PRO_ROWS;
+}
+size_t intra_lds()
+{
+    return sizeof(uint16_t) * 64 * 2 * DKP + sizeof(float) * (2 * 64 * 64 + HB * 64 * 64 + 2 * HB * 64) +
+           sizeof(uint16_t) * HB * 64 * 64;
+}
+size_t sweep_lds() { return sizeof(float) * (2 * 4 * 2 * 16 * 64) + sizeof(int) * 256; }
 
 template <typename K>
 hipError_t allow(K kernel, size_t bytes)
@@ -519,20 +629,21 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int T)
+PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int n_seqs, int T)
 {
     PrefillLayout Lo = {};
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
     const size_t t = (size_t)T;
+    // each prompt adds at most one partial chunk to floor(T / 64) whole ones
+    Lo.max_chunks_total = T / kChunk + n_seqs;
+    const size_t nc = (size_t)Lo.max_chunks_total;
     Lo.qk = take(t * hk * 2 * dk * 2);
     Lo.v = take(t * hv * dv * 2);
     Lo.g = take(t * hv * 4);
     Lo.be = take(t * hv * 4);
-    Lo.gam = take(t * hv * 4);
-    Lo.w = take(t * hv * dk * 2);
-    Lo.u = take(t * hv * dv * 2);
-    Lo.p = take(t * hv * kChunk * 2);
+    Lo.blk = take(nc * hv * kBlockElems * 2);
+    Lo.el = take(nc * hv * 4);
     Lo.total = o;
     return Lo;
 }
@@ -542,28 +653,27 @@ bool prefill_supported(int hk, int hv, int dk, int dv)
     return dk == DKP && dv == DKP && hk > 0 && hv % hk == 0 && hv / hk <= 8;
 }
 
-size_t prefill_workspace_bytes(int hk, int hv, int dk, int dv, int, int total_rows)
+size_t prefill_workspace_bytes(int hk, int hv, int dk, int dv, int n_seqs, int total_rows)
 {
     if (!prefill_supported(hk, hv, dk, dv)) return 0;
-    return prefill_layout(hk, hv, dk, dv, total_rows).total;
+    return prefill_layout(hk, hv, dk, dv, n_seqs, total_rows).total;
 }
 
 hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
 {
-    const PrefillLayout Lo = prefill_layout(P.hk, P.hv, P.dk, P.dv, P.total_rows);
+    const PrefillLayout Lo = prefill_layout(P.hk, P.hv, P.dk, P.dv, P.n_seqs, P.total_rows);
     char *ws = static_cast<char *>(P.workspace);
     Ctx X;
     X.P = P;
     X.r = P.hv / P.hk;
     X.max_chunks = (P.max_len + kChunk - 1) / kChunk;
+    X.nc_total = Lo.max_chunks_total;
     X.qk = reinterpret_cast<uint16_t *>(ws + Lo.qk);
     X.v = reinterpret_cast<uint16_t *>(ws + Lo.v);
     X.g = reinterpret_cast<float *>(ws + Lo.g);
     X.be = reinterpret_cast<float *>(ws + Lo.be);
-    X.gam = reinterpret_cast<float *>(ws + Lo.gam);
-    X.w = reinterpret_cast<uint16_t *>(ws + Lo.w);
-    X.u = reinterpret_cast<uint16_t *>(ws + Lo.u);
-    X.p = reinterpret_cast<uint16_t *>(ws + Lo.p);
+    X.blk = reinterpret_cast<uint16_t *>(ws + Lo.blk);
+    X.el = reinterpret_cast<float *>(ws + Lo.el);
 
     static const hipError_t e1 = allow(prologue_kernel, prologue_lds(8));
     static const hipError_t e2 = allow(intra_kernel, intra_lds());
