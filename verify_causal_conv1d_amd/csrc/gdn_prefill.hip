@@ -5,34 +5,44 @@
 // g_t = log alpha_t and gamma_t = g_1 + ... + g_t (in-chunk),
 //   A_tj = beta_t e^{gamma_t - gamma_j} k_t.k_j (j < t),  T = (I + A)^-1,
 //   W = T (beta e^gamma k),  U~ = T (beta v),  U = U~ - W M0,
-//   O = (e^gamma q) M0 + P U,  P_tj = e^{gamma_t - gamma_j} q_t.k_j (j <= t),
+//   P_tj = e^{gamma_t - gamma_j} q_t.k_j (j <= t),
+//   O = (e^gamma q) M0 + P U = Q' M0 + P U~,   Q' = e^gamma q - P W,
 //   M_next = e^{gamma_L} M0 + (e^{gamma_L - gamma} k)^T U.
 // (The derivation unrolls M_t = alpha_t M_{t-1} + k_t d_t^T with
 // d_t = beta_t (v_t - alpha_t M_{t-1}^T k_t) over the chunk; the gated delta
 // rule is Yang, Kautz and Hatamizadeh, "Gated Delta Networks", 2024.)
+// Folding P W into Q' moves every product that does not involve the state
+// into the parallel per-chunk kernel, and leaves the sequential sweep with
+// one fused contraction [W; Q'] M0 and the update.
 //
 // Three launches on the caller's stream:
-//   prologue  per 32 packed rows x key head: causal conv (taps from the
-//             prompt's own earlier rows or its tail) + SiLU, q/k L2 norms,
-//             gates.  q^, k^, v are stored as bf16 (the matrix-core operand
-//             type), log alpha and beta as fp32.
-//   intra     per (chunk, key head): K K^T and Q K^T on bf16 MFMA
-//             (v_mfma_f32_32x32x16_bf16); per value head gamma, the fp32
-//             triangular solve for T (one wave, one column a lane), and W^T,
-//             U~ on bf16 MFMA.  Everything the sweep needs leaves this kernel
-//             in the exact lane order of the sweep's MFMA operands, so the
-//             sweep reads each operand with two 16-byte loads a lane.
-//   sweep     per (prompt, value head, 32 state columns), 4 waves, each
-//             holding 32 rows of the state as an fp32 MFMA accumulator: the
-//             state contractions U~ - W M0, (e^gamma q) M0, P U and the update
-//             (e^{gamma_L - gamma} k)^T U run on fp32 MFMA
-//             (v_mfma_f32_32x32x2_f32) with the accumulator itself as the B
-//             operand; partial sums over the four row blocks meet in LDS.
-//             Sequential over the prompt's chunks, with each operand of chunk
-//             c + 1 fetched right after its last use in chunk c; the state
-//             never leaves the chip between chunks.  Workgroups take prompts
-//             longest first, so the longest dependency chain starts first.
-// The prompt's final state replaces the stream's state and its last three raw
+//   prologue  a thread owns 8 channels and walks 32 packed rows with the
+//             last three raw rows in registers: causal conv (taps from the
+//             prompt's own earlier rows or its tail) + SiLU, then per row the
+//             q/k L2 norms over the 16 lanes of a head; gates per (row, value
+//             head).  q^, k^, v are stored as bf16 (matrix-core operands), log
+//             alpha and beta as fp32.
+//   intra     per (chunk, value head), independent: K K^T and Q K^T on bf16
+//             MFMA, T by 16 x 16 blocks (fp32 forward substitution on the
+//             diagonal, fp32 MFMA off it), then W^T, U~ and (P W)^T on bf16
+//             MFMA.  Products are formed transposed where
+//             that puts each lane's accumulator values exactly where the
+//             sweep's lanes read them, so most operands leave straight from
+//             registers; everything is stored in the sweep's lane order.
+//   sweep     per (prompt, value head, 16 state columns), 4 waves, wave w
+//             holding state rows [32w, 32w + 32) as fp32 MFMA accumulators
+//             (v_mfma_f32_16x16x4_f32).  Per chunk: partial [W; Q'] M0 over
+//             the wave's rows with the accumulator itself as the B operand,
+//             one LDS reduction across the 4 waves, U = U~ - W M0,
+//             O = Q' M0 + P U~ (P U~ on bf16 MFMA), and the update
+//             M = e^{gamma_L} M + K~^T U, again with U's accumulator as B.
+//             Sequential over the prompt's chunks, operands of chunk c + 1
+//             fetched while chunk c computes; the state never leaves the
+//             chip.  The 8 column tiles of one (prompt, head) share their
+//             operands and are placed on one XCD (workgroup i runs on XCD
+//             i mod 8) so that they meet in that XCD's L2; prompts run
+//             longest first.
+// The prompt's final state replaces the stream's state, and its last three raw
 // rows (or a mix with the old tail for prompts shorter than three rows) its
 // conv tail, in place (prompt passes update the stream in place: page
 // "perf(qwen3_5 cuda): deliver the first token before drafting", commit note
@@ -43,24 +53,24 @@
 namespace gdn {
 namespace {
 
-constexpr int DKP = 128;        // head sizes this pass is built for
-constexpr int PRO_ROWS = 32;    // packed rows a prologue workgroup
-constexpr int TILE = 32;        // state columns a sweep workgroup
-constexpr int HB = 3;           // value heads whose triangular solves run side by side
+constexpr int D = 128;          // dk = dv of this pass
+constexpr int PRO_ROWS = 32;    // packed rows a prologue workgroup walks
+constexpr int NTILE = D / 16;   // 16-column state tiles of a head
 
 // A chunk-head block of sweep operands (bf16), every sub-array in lane order
-// [.][.][64 lanes][16], lane l = (l32, hh) = (l & 31, l >> 5):
-//   W  [mb][w]     lane value i = W[32 mb + l32][32 w + kx(i)]
-//   QE [mb][w]     lane value i = e^{gamma_t} q^[t = 32 mb + l32][32 w + kx(i)]
-//   KT [mb][w]     lane value i = e^{gamma_L - gamma_t} k^[t = 32 mb + kx(i)][32 w + l32]
-//   P  [mb][mbk]   lane value i = P[32 mb + l32][32 mbk + kx(i)]
-//   UT [mb][tile]  lane value i = U~[32 mb + kx(i)][32 tile + l32]
-// with kx(i) = 8 (i / 4) + 4 hh + i % 4: the k index that lane l feeds at step
-// i of a v_mfma_f32_32x32x2_f32 chain whose B operand is register i of a
-// 32 x 32 accumulator (accumulator register i of lane l holds row kx(i),
-// column l32).  Rows past the chunk's end are zero.
-constexpr int kOffW = 0, kOffQE = 8192, kOffKT = 16384, kOffP = 24576, kOffUT = 28672;
-constexpr int kBlockElems = 36864;
+// [..][64 lanes][8 values]; lane l = (l16, g4) = (l & 15, l >> 4), and
+// accumulator register i of a 16x16 block holds row 4 g4 + i, column l16.
+//   WQ [w 4][m 8][l][4b+i]      = WQ[16m + l16][32w + 16b + 4g4 + i]
+//        WQ = [W; Q'] (128 x dk); the A operand of step (b, i) of the
+//        wave-w partial for output rows 16m..16m+15
+//   KT [w 4][b 2][mp 2][l][e]   = K~[16m + 4g4 + i][32w + 16b + l16],
+//        m = 2mp + e/4, i = e%4, K~ = e^{gamma_L - gamma} k^
+//   UA [tile 8][mp 2][l][e]     = U~[16m + 4g4 + i][16tile + l16]   (accumulator layout)
+//   UB [tile 8][kb 2][l][j]     = U~[32kb + 8g4 + j][16tile + l16]  (bf16 MFMA B operand)
+//   PA [w 4][kb 2][l][j]        = P[16w + l16][32kb + 8g4 + j]      (bf16 MFMA A operand)
+// Rows past the chunk's end are zero in every array.
+constexpr int kOffWQ = 0, kOffKT = 16384, kOffUA = 24576, kOffUB = 32768, kOffPA = 40960;
+constexpr int kBlockElems = 45056;
 
 struct Ctx {
     PrefillArgs P;
@@ -70,8 +80,6 @@ struct Ctx {
     uint16_t *qk, *v, *blk;
     float *g, *be, *el;
 };
-
-__device__ __forceinline__ int kx(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
 
 // Rows of prompt p, and the dense index of its first chunk.  False if p or an
 // earlier prompt breaks the layout rules (monotone starts within [0, T],
@@ -94,35 +102,45 @@ __device__ bool prompt_chunks(const Ctx &X, int p, int &s0, int &s1, int &cid0)
     return base + (s1 - s0 + kChunk - 1) / kChunk <= X.nc_total;
 }
 
-// Local prologue channel -> global channel: [q of kh | k of kh | v of kh's value heads].
-__device__ __forceinline__ int pro_channel(const Ctx &X, int kh, int ch)
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(uint16_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+__device__ __forceinline__ bf8v as_bf8(uint4 v) { return __builtin_bit_cast(bf8v, v); }
+
+// bf16 value e (0..7) of a 16-byte vector, as fp32
+__device__ __forceinline__ float bfe(const uint4 &u, int e)
 {
-    if (ch < DKP) return kh * DKP + ch;
-    if (ch < 2 * DKP) return X.P.hk * DKP + kh * DKP + (ch - DKP);
-    return 2 * X.P.hk * DKP + kh * X.r * DKP + (ch - 2 * DKP);
+    const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+__device__ __forceinline__ f4v mfma_f32(float a, float b, f4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f4v mfma_bf16(uint4 a, uint4 b, f4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- prologue
 __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
 {
-    extern __shared__ float smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int kh = blockIdx.y;
+    __shared__ int rstart[PRO_ROWS];   // prompt start of each row, -1 outside every valid prompt
+    __shared__ int rprompt[PRO_ROWS];
+    const int tid = threadIdx.x;
     const int t0 = blockIdx.x * PRO_ROWS;
-    const int T = X.P.total_rows;
+    const int T = X.P.total_rows, C = X.P.C, hv = X.P.hv, hk = X.P.hk;
     const int nrows = min(PRO_ROWS, T - t0);
-    const int C = X.P.C;
-    const int nch = 2 * DKP + X.r * DKP;
-    float *act = smem;                                                    // [PRO_ROWS][2*DKP]
-    float4 *wl = reinterpret_cast<float4 *>(act + PRO_ROWS * 2 * DKP);    // [nch]
-    uint16_t *raw = reinterpret_cast<uint16_t *>(wl + nch);               // [PRO_ROWS + 3][nch]
-    int *rstart = reinterpret_cast<int *>(raw + (PRO_ROWS + 3) * nch);    // [PRO_ROWS]
-    int *rprompt = rstart + PRO_ROWS;                                     // [PRO_ROWS]
 
-    // prompt of each row: the last p with seq_start[p] <= t, if t < seq_start[p + 1]
     if (tid < nrows) {
         const int t = t0 + tid;
-        int lo = 0, hi = X.P.n_seqs - 1;
+        int lo = 0, hi = X.P.n_seqs - 1;   // the last p with seq_start[p] <= t
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (X.P.seq_start[mid] <= t) lo = mid; else hi = mid - 1;
@@ -132,138 +150,154 @@ __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
         rstart[tid] = ok ? s0 : -1;
         rprompt[tid] = lo;
     }
-    // stage raw rows t0-3 .. t0+nrows-1 of this key head's channels, and the weights
-    {
-        const int cpr = nch / 8;
-        const int nchunks = (nrows + 3) * cpr;
-        constexpr int B = 8;
-        for (int base = 0; base < nchunks; base += B * 256) {
-            uint4 v[B];
-#pragma unroll
-            for (int k = 0; k < B; ++k) {
-                const int idx = base + k * 256 + tid;
-                const int j = idx / cpr;
-                const int u = t0 - 3 + j;
-                if (idx < nchunks && u >= 0)
-                    v[k] = *reinterpret_cast<const uint4 *>(X.P.qkv + (size_t)u * C +
-                                                            pro_channel(X, kh, (idx - j * cpr) * 8));
-            }
-#pragma unroll
-            for (int k = 0; k < B; ++k) {
-                const int idx = base + k * 256 + tid;
-                const int j = idx / cpr;
-                if (idx < nchunks && t0 - 3 + j >= 0)
-                    *reinterpret_cast<uint4 *>(raw + j * nch + (idx - j * cpr) * 8) = v[k];
-            }
-        }
-        for (int ch = tid; ch < nch; ch += 256)
-            wl[ch] = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)pro_channel(X, kh, ch) * 4);
-    }
     lds_barrier();
 
-    // gates of every (row, value head of kh)
-    for (int idx = tid; idx < nrows * X.r; idx += 256) {
-        const int i = idx / X.r;
-        if (rstart[i] < 0) continue;
-        const int h = kh * X.r + (idx - i * X.r);
-        const size_t o = (size_t)(t0 + i) * X.P.hv + h;
-        X.g[o] = log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]);
-        X.be[o] = sigmoid_f(bf16f(X.P.b[o]));
+    // gates of every (row, value head): log alpha and beta
+    if (blockIdx.y == 0) {
+        for (int idx = tid; idx < nrows * hv; idx += 256) {
+            const int i = idx / hv, h = idx - i * hv;
+            if (rstart[i] < 0) continue;
+            const size_t o = (size_t)(t0 + i) * hv + h;
+            X.g[o] = log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]);
+            X.be[o] = sigmoid_f(bf16f(X.P.b[o]));
+        }
     }
-    // conv + SiLU, a thread walking the rows of one channel: q/k into LDS for
-    // the norms, v straight out as bf16
-    for (int ch = tid; ch < nch; ch += 256) {
-        const float4 w = wl[ch];
-        const int gc = pro_channel(X, kh, ch);
-        for (int i = 0; i < nrows; ++i) {
-            const int rs = rstart[i];
-            if (rs < 0) continue;
+
+    const int c0 = (blockIdx.y * 256 + tid) * 8;   // this thread's 8 channels
+    if (c0 >= C) return;                            // no barrier below
+    // role: 16 consecutive lanes form one head of 128 channels
+    const int nq = hk * D;
+    const int kind = c0 < nq ? 0 : (c0 < 2 * nq ? 1 : 2);   // q, k, v
+    const int hc = kind == 2 ? c0 - 2 * nq : c0 - kind * nq;
+    const int head = hc / D, off = hc - head * D;
+    uint16_t *dst = kind == 2 ? X.v + (size_t)head * D + off
+                              : X.qk + ((size_t)head * 2 + kind) * D + off;
+    const size_t dst_row = kind == 2 ? (size_t)hv * D : (size_t)hk * 2 * D;
+    const float qscale = kind == 0 ? 1.0f / sqrtf((float)D) : 1.0f;
+
+    float w[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float4 wv = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)(c0 + e) * 4);
+        w[e][0] = wv.x; w[e][1] = wv.y; w[e][2] = wv.z; w[e][3] = wv.w;
+    }
+
+    const uint16_t *col = X.P.qkv + c0;
+    uint4 x1 = make_uint4(0, 0, 0, 0), x2 = x1, x3 = x1;   // x_{t-1}, x_{t-2}, x_{t-3}
+    int cur = -2;                                          // prompt start the window belongs to
+    constexpr int B = 8;
+    for (int i0 = 0; i0 < nrows; i0 += B) {
+        uint4 xb[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            if (i0 + k < nrows && rstart[i0 + k] >= 0) xb[k] = ld16(col + (size_t)(t0 + i0 + k) * C);
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            const int i = i0 + k;
+            if (i >= nrows) break;
+            const int s0 = rstart[i];
             const int t = t0 + i;
-            // tap j reads x_{t-3+j}: a staged row of this prompt, or its tail
-            const uint16_t *tailc = X.P.conv_tail + (size_t)rprompt[i] * 3 * C + gc;
-            const float x0 = bf16f(t - 3 >= rs ? raw[i * nch + ch] : tailc[(size_t)(t - rs) * C]);
-            const float x1 = bf16f(t - 2 >= rs ? raw[(i + 1) * nch + ch] : tailc[(size_t)(1 + t - rs) * C]);
-            const float x2 = bf16f(t - 1 >= rs ? raw[(i + 2) * nch + ch] : tailc[(size_t)(2 + t - rs) * C]);
-            const float x3 = bf16f(raw[(i + 3) * nch + ch]);
-            float y = w.x * x0;
-            y = fmaf(w.y, x1, y);
-            y = fmaf(w.z, x2, y);
-            y = fmaf(w.w, x3, y);
-            const float a = silu_f(y);
-            if (ch < 2 * DKP)
-                act[i * 2 * DKP + ch] = a;
-            else
-                X.v[(size_t)t * X.P.hv * DKP + (size_t)kh * X.r * DKP + (ch - 2 * DKP)] = f2bf(a);
+            if (s0 < 0) {
+                cur = -2;
+                continue;
+            }
+            if (s0 != cur || i == 0) {
+                // (re)build the window of row t: earlier rows of its prompt, else its tail
+                const uint16_t *tl = X.P.conv_tail + (size_t)rprompt[i] * 3 * C + c0;
+                uint4 xs[3];
+#pragma unroll
+                for (int d = 1; d <= 3; ++d) {
+                    const int src = t - d;
+                    xs[d - 1] = src >= s0 ? ld16(col + (size_t)src * C) : ld16(tl + (size_t)(3 + src - s0) * C);
+                }
+                x1 = xs[0];
+                x2 = xs[1];
+                x3 = xs[2];
+                cur = s0;
+            }
+            const uint4 xt = xb[k];
+            float a[8];
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = w[e][0] * bfe(x3, e);
+                y = fmaf(w[e][1], bfe(x2, e), y);
+                y = fmaf(w[e][2], bfe(x1, e), y);
+                y = fmaf(w[e][3], bfe(xt, e), y);
+                a[e] = silu_f(y);
+                ss = fmaf(a[e], a[e], ss);
+            }
+            float sc = 1.0f;
+            if (kind < 2) {
+                // sum over the 16 lanes of this head (all of them take this branch)
+                ss += __shfl_xor(ss, 1);
+                ss += __shfl_xor(ss, 2);
+                ss += __shfl_xor(ss, 4);
+                ss += __shfl_xor(ss, 8);
+                sc = (1.0f / sqrtf(ss + 1e-6f)) * qscale;
+            }
+            uint4 o;
+            o.x = pack2(a[0] * sc, a[1] * sc);
+            o.y = pack2(a[2] * sc, a[3] * sc);
+            o.z = pack2(a[4] * sc, a[5] * sc);
+            o.w = pack2(a[6] * sc, a[7] * sc);
+            st16(dst + (size_t)t * dst_row, o);
+            x3 = x2;
+            x2 = x1;
+            x1 = xt;
         }
-    }
-    lds_barrier();
-
-    // L2 norms of q (times dk^-1/2) and k, one wave a (row, q|k) pair
-    const float qscale = 1.0f / sqrtf((float)DKP);
-    for (int pr = wave; pr < 2 * nrows; pr += 4) {
-        const int i = pr >> 1, which = pr & 1;
-        if (rstart[i] < 0) continue;
-        const float *src = act + i * 2 * DKP + which * DKP;
-        const float x0 = src[lane], x1 = src[lane + 64];
-        float ss = x0 * x0;
-        ss = fmaf(x1, x1, ss);
-        ss = sum_wave(ss);
-        float sc = 1.0f / sqrtf(ss + 1e-6f);
-        if (which == 0) sc = sc * qscale;
-        uint16_t *dst = X.qk + ((size_t)(t0 + i) * X.P.hk + kh) * 2 * DKP + which * DKP;
-        dst[lane] = f2bf(x0 * sc);
-        dst[lane + 64] = f2bf(x1 * sc);
     }
 }
 
 // ---------------------------------------------------------------- intra
-__device__ __forceinline__ bf8v lds8(const uint16_t *p) { return __builtin_bit_cast(bf8v, *reinterpret_cast<const uint4 *>(p)); }
+// T = (I + A)^-1 for the strictly lower-triangular 64 x 64 A, by 16 x 16
+// blocks: the diagonal blocks B_i = (I + A_ii)^-1 by forward substitution,
+// then T_ij = -B_i sum_{k=j}^{i-1} A_ik T_kj (i > j) on fp32 MFMA, one
+// diagonal distance after the other.  An holds -A in fp32, [64][64]; its
+// strictly upper blocks are free and keep the fp32 T blocks later stages read
+// (B_i over A_ii once that is used, T_10 in block (0,1), T_21 in (1,2), T_20
+// in (0,2)).
 
-// Row T_ of the forward substitution T (I + A) = I for unit lower-triangular
-// I + A: lane c keeps column c of T; An holds -A (row-major, [64][64]).
-template <int T_>
-__device__ __forceinline__ void tsolve_row(float (&Tc)[64], const float *An, int lane)
+// z += X Y for fp32 16 x 16 blocks X = An block (xi, xj), Y = An block (yi, yj)
+__device__ __forceinline__ f4v mm_blocks(const float *An, int xi, int xj, int yi, int yj, f4v z, int l16, int g4)
 {
-    float acc = (T_ == lane) ? 1.0f : 0.0f;
-    const float *row = An + T_ * 64;
 #pragma unroll
-    for (int s4 = 0; s4 + 4 <= T_; s4 += 4) {
-        const float4 a4 = *reinterpret_cast<const float4 *>(row + s4);
-        acc = fmaf(a4.x, Tc[s4], acc);
-        acc = fmaf(a4.y, Tc[s4 + 1], acc);
-        acc = fmaf(a4.z, Tc[s4 + 2], acc);
-        acc = fmaf(a4.w, Tc[s4 + 3], acc);
-    }
-#pragma unroll
-    for (int s = T_ & ~3; s < T_; ++s) acc = fmaf(row[s], Tc[s], acc);
-    Tc[T_] = acc;
-    // keep the scheduler from hoisting later rows' LDS reads above this one
-    // (it would hold hundreds of them in registers)
-    __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < 4; ++kk)
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(An[(16 * xi + l16) * 64 + 16 * xj + 4 * kk + g4],
+                                                 An[(16 * yi + 4 * kk + g4) * 64 + 16 * yj + l16], z, 0, 0, 0);
+    return z;
 }
 
-template <int T_>
-__device__ __forceinline__ void tsolve(float (&Tc)[64], const float *An, int lane)
+// -B_i S for S held in the accumulator layout (register kk of lane l is
+// S[4 g4 + kk][l16]), B_i = An block (i, i)
+__device__ __forceinline__ f4v neg_diag_times(const float *An, int i, f4v s, int l16, int g4)
 {
-    tsolve_row<T_>(Tc, An, lane);
-    if constexpr (T_ + 1 < 64) tsolve<T_ + 1>(Tc, An, lane);
+    f4v z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(-An[(16 * i + l16) * 64 + 16 * i + 4 * g4 + kk], s[kk], z, 0, 0, 0);
+    return z;
 }
 
-__device__ __forceinline__ void store16(uint16_t *dst, const float (&v)[16])
-{
-    uint32_t w[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = (uint32_t)f2bf(v[2 * e]) | ((uint32_t)f2bf(v[2 * e + 1]) << 16);
-    reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-}
+constexpr int SB = 72;   // bf16 row stride of the [.][64] LDS arrays (144 B: rows 4 banks apart)
+
+// LDS of an intra workgroup (bytes)
+constexpr int kIntraAn = 0;                       // fp32 [64][64] -A; later WT bf16 [128][SB]
+constexpr int kIntraPb = 128 * SB * 2;            // bf16 [64][SB]  P
+constexpr int kIntraTb = kIntraPb + 64 * SB * 2;  // bf16 [64][SB]  T
+constexpr int kIntraKb = kIntraTb + 64 * SB * 2;  // bf16 [128][SB] (beta e^gamma k^)^T
+constexpr int kIntraVb = kIntraKb + 128 * SB * 2; // bf16 [128][SB] (beta v)^T; later U~^T
+constexpr int kIntraVec = kIntraVb + 128 * SB * 2;
+constexpr int kIntraLds = kIntraVec + 4 * 64 * 4;
+static_assert(64 * 64 * 4 <= kIntraPb, "An fits its region");
 
 __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int kh = blockIdx.y;
+    const int h = blockIdx.y, kh = h / X.r;
     const int pidx = blockIdx.x / X.max_chunks, c = blockIdx.x - pidx * X.max_chunks;
     int s0, s1, cid0;
     if (!prompt_chunks(X, pidx, s0, s1, cid0)) return;
@@ -271,326 +305,263 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
     if (r0 >= s1) return;
     const int L = min(kChunk, s1 - r0);
     const int hv = X.P.hv, hk = X.P.hk;
+    const size_t cidh = (size_t)(cid0 + c) * hv + h;
+    uint16_t *blk = X.blk + cidh * kBlockElems;
 
-    uint16_t *qkr = reinterpret_cast<uint16_t *>(smem);            // [64][256] q^ | k^ rows
-    float *Skk = reinterpret_cast<float *>(qkr + 64 * 2 * DKP);    // [64][64]
-    float *Sqk = Skk + 64 * 64;                                    // [64][64]
-    float *An = Sqk + 64 * 64;                                     // [HB][64][64] -A, later KbT / VbT
-    uint16_t *Tb = reinterpret_cast<uint16_t *>(An + HB * 64 * 64);   // [HB][64][64] bf16
-    float *gam = reinterpret_cast<float *>(Tb + HB * 64 * 64);       // [HB][64]
-    float *bet = gam + HB * 64;                                        // [HB][64]
-    uint16_t *KbT = reinterpret_cast<uint16_t *>(An);                  // [128][64]
-    uint16_t *VbT = KbT + 128 * 64;                                    // [128][64]
+    float *An = reinterpret_cast<float *>(lds + kIntraAn);
+    uint16_t *WT = reinterpret_cast<uint16_t *>(lds + kIntraAn);
+    uint16_t *Pb = reinterpret_cast<uint16_t *>(lds + kIntraPb);
+    uint16_t *Tb = reinterpret_cast<uint16_t *>(lds + kIntraTb);
+    uint16_t *KbT = reinterpret_cast<uint16_t *>(lds + kIntraKb);
+    uint16_t *VbT = reinterpret_cast<uint16_t *>(lds + kIntraVb);
+    uint16_t *UT = VbT;
+    float *gam = reinterpret_cast<float *>(lds + kIntraVec);
+    float *bet = gam + 64, *eg = bet + 64, *ekt = eg + 64;
 
-    // the chunk's q^ | k^ rows (zero past its end)
-    for (int idx = tid; idx < 64 * 32; idx += 256) {
-        const int t = idx >> 5, q8 = (idx & 31) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < L) v = *reinterpret_cast<const uint4 *>(X.qk + ((size_t)(r0 + t) * hk + kh) * 2 * DKP + q8);
-        *reinterpret_cast<uint4 *>(qkr + t * 2 * DKP + q8) = v;
+    const size_t qkrow = (size_t)hk * 2 * D;              // elements a packed row of q^|k^
+    const uint16_t *Qg = X.qk + ((size_t)r0 * hk + kh) * 2 * D;
+    const uint16_t *Kg = Qg + D;
+    const uint16_t *Vg = X.v + ((size_t)r0 * hv + h) * D;
+    const size_t vrow = (size_t)hv * D;
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+
+    // ---- gamma (inclusive in-chunk scan of log alpha), beta and the decays
+    if (wave == 0) {
+        const size_t o = (size_t)(r0 + lane) * hv + h;
+        float gl = lane < L ? X.g[o] : 0.0f;
+        const float bl = lane < L ? X.be[o] : 0.0f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float up = __shfl_up(gl, d);
+            if (lane >= d) gl += up;
+        }
+        const float gL = __shfl(gl, L - 1);
+        gam[lane] = gl;
+        bet[lane] = bl;
+        eg[lane] = lane < L ? __expf(gl) : 0.0f;
+        ekt[lane] = lane < L ? __expf(gL - gl) : 0.0f;
+        if (lane == 0) X.el[cidh] = __expf(gL);
+    }
+
+    // ---- K K^T and Q K^T, wave w: the 32 x 32 block (w >> 1, w & 1)
+    f16v S = {}, QK = {};
+    {
+        const int bi = wave >> 1, bj = wave & 1;
+        const int ra = 32 * bi + l32, rb = 32 * bj + l32;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const int ko = 16 * ks + 8 * hh;
+            const uint4 ka = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;
+            const uint4 qa = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;
+            const uint4 kb = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ka), as_bf8(kb), S, 0, 0, 0);
+            QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qa), as_bf8(kb), QK, 0, 0, 0);
+        }
+    }
+    lds_barrier();   // gamma, beta visible
+
+    // -A (strictly lower, fp32) and P (lower with diagonal, bf16)
+    {
+        const int bi = wave >> 1, bj = wave & 1;
+        const int s = 32 * bj + l32;
+        const float gs = gam[s];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = 32 * bi + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const bool live = s <= t && t < L;
+            const float dec = live ? __expf(gam[t] - gs) : 0.0f;
+            An[t * 64 + s] = (live && s < t) ? -bet[t] * dec * S[i] : 0.0f;
+            Pb[t * SB + s] = f2bf(dec * QK[i]);
+        }
+    }
+    // (beta e^gamma k^)^T and (beta v)^T: lanes take consecutive rows s, so the
+    // transposed LDS writes are contiguous
+    {
+        constexpr int NB = 8;
+        uint4 raw[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int idx = k * 256 + tid;          // 0..2047: 16 column groups x 64 rows, K then V
+            const int which = idx >> 10, s = idx & 63, q8 = ((idx >> 6) & 15) * 8;
+            raw[k] = s < L ? ld16(which ? Vg + s * vrow + q8 : Kg + s * qkrow + q8) : z4;
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int idx = k * 256 + tid;
+            const int which = idx >> 10, s = idx & 63, q8 = ((idx >> 6) & 15) * 8;
+            const float sc = which ? bet[s] : bet[s] * eg[s];
+            uint16_t *dst = (which ? VbT : KbT) + q8 * SB + s;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e * SB] = f2bf(sc * bfe(raw[k], e));
+        }
+    }
+    // K~ = e^{gamma_L - gamma} k^ in the sweep's lane order
+    for (int u = tid; u < 1024; u += 256) {
+        const int l = u & 63, ul16 = l & 15, ug4 = l >> 4;
+        const int e_blk = u >> 6;                 // (w, b, mp)
+        const int w = e_blk >> 2, b = (e_blk >> 1) & 1, mp = e_blk & 1;
+        const int kr = 32 * w + 16 * b + ul16;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 16 * (2 * mp + (e >> 2)) + 4 * ug4 + (e & 3);
+            v[e] = t < L ? ekt[t] * bf16f(Kg[t * qkrow + kr]) : 0.0f;
+        }
+        st16(blk + kOffKT + (size_t)u * 8,
+             make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
     }
     lds_barrier();
 
-    // K K^T and Q K^T: wave w computes the 32 x 32 block (w >> 1, w & 1) of both
+    // ---- T = (I + A)^-1.  Stage 1: wave w inverts diagonal block w (every
+    // lane group computes column l16; group g4 stores rows 4 g4 .. 4 g4 + 3)
     {
-        const int bi = wave >> 1, bj = wave & 1;
-        const uint16_t *ra = qkr + (32 * bi + l32) * 2 * DKP;
-        const uint16_t *rb = qkr + (32 * bj + l32) * 2 * DKP + DKP;
-        f16v kk = {}, qk = {};
+        const int j = l16, w = wave;
+        float Tc[16];
 #pragma unroll
-        for (int ks = 0; ks < DKP / 16; ++ks) {
-            const int ko = 16 * ks + 8 * hh;
-            const bf8v bk = lds8(rb + ko);
-            kk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(ra + DKP + ko), bk, kk, 0, 0, 0);
-            qk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(ra + ko), bk, qk, 0, 0, 0);
+        for (int t = 0; t < 16; ++t) {
+            float acc = (t == j) ? 1.0f : 0.0f;
+            const float *row = An + (16 * w + t) * 64 + 16 * w;
+#pragma unroll
+            for (int s = 0; s < t; ++s) acc = fmaf(row[s], Tc[s], acc);
+            Tc[t] = acc;
         }
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int row = 32 * bi + kx(rr, hh);
-            Skk[row * 64 + 32 * bj + l32] = kk[rr];
-            Sqk[row * 64 + 32 * bj + l32] = qk[rr];
+        for (int i = 0; i < 4; ++i) {
+            const float v = g4 == 0 ? Tc[i] : g4 == 1 ? Tc[4 + i] : g4 == 2 ? Tc[8 + i] : Tc[12 + i];
+            const int t = 16 * w + 4 * g4 + i;
+            An[t * 64 + 16 * w + j] = v;
+            Tb[t * SB + 16 * w + j] = f2bf(v);
+            for (int cb = w + 1; cb < 4; ++cb) Tb[t * SB + 16 * cb + j] = 0;
         }
     }
-
-    for (int j0 = 0; j0 < X.r; j0 += HB) {
-        const int nh = min(HB, X.r - j0);
-        // gamma (inclusive in-chunk scan of log alpha) and beta, one wave a head
-        if (wave < nh) {
-            const int h = kh * X.r + j0 + wave;
-            const size_t o = (size_t)(r0 + lane) * hv + h;
-            float gl = lane < L ? X.g[o] : 0.0f;
-            const float bl = lane < L ? X.be[o] : 0.0f;
+    // P in the sweep's lane order
+    for (int u = tid; u < 512; u += 256) {
+        const int l = u & 63, w = u >> 7, kb = (u >> 6) & 1;
+        st16(blk + kOffPA + (size_t)u * 8, ld16(Pb + (16 * w + (l & 15)) * SB + 32 * kb + 8 * (l >> 4)));
+    }
+    lds_barrier();
+    // Stage 2: T_{i,i-1} = -B_i A_{i,i-1} B_{i-1}, wave i (An holds -A)
+    if (wave >= 1) {
+        const int i = wave;
+        f4v x = {0.f, 0.f, 0.f, 0.f};
+        x = mm_blocks(An, i, i - 1, i - 1, i - 1, x, l16, g4);   // -A_{i,i-1} B_{i-1}
+        const f4v z = -neg_diag_times(An, i, x, l16, g4);
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float up = __shfl_up(gl, d);
-                if (lane >= d) gl += up;
-            }
-            gam[wave * 64 + lane] = gl;
-            bet[wave * 64 + lane] = bl;
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * i + 4 * g4 + r;
+            Tb[t * SB + 16 * (i - 1) + l16] = f2bf(z[r]);
+            if (i < 3) An[(16 * (i - 1) + 4 * g4 + r) * 64 + 16 * i + l16] = z[r];   // T_10 -> (0,1), T_21 -> (1,2)
         }
-        lds_barrier();
-
-        if (wave < nh) {
-            // -A, column `lane`: -beta_t e^{gamma_t - gamma_s} (k_t . k_s) for t > s
-            const float *gj = gam + wave * 64, *bj = bet + wave * 64;
-            float *Aj = An + wave * 64 * 64;
-            const int s = lane;
-            const float gs = gj[s];
-            for (int t = 0; t < 64; ++t)
-                Aj[t * 64 + s] = t > s ? -bj[t] * __expf(gj[t] - gs) * Skk[t * 64 + s] : 0.0f;
-            // T = (I + A)^-1 by forward substitution; lane c keeps column c
-            float Tc[64];
-            tsolve<0>(Tc, Aj, lane);
-            uint16_t *Tj = Tb + wave * 64 * 64;
+    }
+    lds_barrier();
+    // Stage 3: T_{i,i-2} = -B_i (A_{i,i-2} B_{i-2} + A_{i,i-1} T_{i-1,i-2}), waves 2 and 3
+    if (wave >= 2) {
+        const int i = wave;
+        f4v x = {0.f, 0.f, 0.f, 0.f};
+        x = mm_blocks(An, i, i - 2, i - 2, i - 2, x, l16, g4);
+        x = mm_blocks(An, i, i - 1, i - 2, i - 1, x, l16, g4);   // T_{i-1,i-2} is kept in block (i-2, i-1)
+        const f4v z = -neg_diag_times(An, i, x, l16, g4);
 #pragma unroll
-            for (int t = 0; t < 64; ++t) Tj[t * 64 + lane] = f2bf(Tc[t]);
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * i + 4 * g4 + r;
+            Tb[t * SB + 16 * (i - 2) + l16] = f2bf(z[r]);
+            if (i == 2) An[(4 * g4 + r) * 64 + 32 + l16] = z[r];   // T_20 -> (0,2)
         }
-        lds_barrier();
+    }
+    lds_barrier();
+    // Stage 4: T_30 = -B_3 (A_30 B_0 + A_31 T_10 + A_32 T_20), wave 3
+    if (wave == 3) {
+        f4v x = {0.f, 0.f, 0.f, 0.f};
+        x = mm_blocks(An, 3, 0, 0, 0, x, l16, g4);
+        x = mm_blocks(An, 3, 1, 0, 1, x, l16, g4);
+        x = mm_blocks(An, 3, 2, 0, 2, x, l16, g4);
+        const f4v z = -neg_diag_times(An, 3, x, l16, g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tb[(48 + 4 * g4 + r) * SB + l16] = f2bf(z[r]);
+    }
+    lds_barrier();
 
-        for (int jj = 0; jj < nh; ++jj) {
-            const int h = kh * X.r + j0 + jj;
-            const float *gj = gam + jj * 64, *bj = bet + jj * 64;
-            const float gL = gj[63];
-            uint16_t *blk = X.blk + ((size_t)(cid0 + c) * hv + h) * kBlockElems;
-            // KbT[k][s] = beta_s e^{gamma_s} k_s[k],  VbT[c][s] = beta_s v_s[c]
-            for (int idx = tid; idx < 64 * 16 * 2; idx += 256) {
-                const int which = idx >= 64 * 16;
-                const int id = idx - which * 64 * 16;
-                const int s = id >> 4, q8 = (id & 15) * 8;
-                uint4 raw = make_uint4(0, 0, 0, 0);
-                if (which && s < L) raw = *reinterpret_cast<const uint4 *>(X.v + ((size_t)(r0 + s) * hv + h) * DKP + q8);
-                if (!which) raw = *reinterpret_cast<const uint4 *>(qkr + s * 2 * DKP + DKP + q8);
-                const uint16_t *e8 = reinterpret_cast<const uint16_t *>(&raw);
-                const float sc = which ? bj[s] : bj[s] * __expf(gj[s]);
-                uint16_t *dst = which ? VbT : KbT;
+    // ---- W^T = (beta e^gamma k^)^T T^T and U~ = T (beta v); wave w takes
+    // key column blocks kb = 2w, 2w + 1 of W^T and value tiles 2w, 2w + 1 of U~
+    f4v Ud[2][4];
+    {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) dst[(q8 + e) * 64 + s] = f2bf(sc * bf16f(e8[e]));
-            }
-            // sweep operands formed elementwise: QE, KT (2 x 4 lane slots each) and P (2 x 2)
-            for (int slot = tid; slot < 2 * 4 * 64 * 2 + 2 * 2 * 64; slot += 256) {
-                float vals[16];
-                const int sl = slot & 63, sh = sl >> 5, s32 = sl & 31;
-                if (slot < 2 * 4 * 64) {                       // QE[mb][w][lane]
-                    const int mb = slot >> 8, w = (slot >> 6) & 3;
-                    const int t = 32 * mb + s32;
-                    const float e = __expf(gj[t]);
+        for (int bb = 0; bb < 2; ++bb) {
+            const int kb = 2 * wave + bb;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) vals[i] = e * bf16f(qkr[t * 2 * DKP + 32 * w + kx(i, sh)]);
-                    store16(blk + kOffQE + (size_t)slot * 16, vals);
-                } else if (slot < 2 * 2 * 4 * 64) {           // KT[mb][w][lane]
-                    const int s2 = slot - 2 * 4 * 64;
-                    const int mb = s2 >> 8, w = (s2 >> 6) & 3;
+            for (int mt = 0; mt < 4; ++mt) {
+                f4v wacc = {}, uacc = {};
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int t = 32 * mb + kx(i, sh);
-                        vals[i] = __expf(gL - gj[t]) * bf16f(qkr[t * 2 * DKP + DKP + 32 * w + s32]);
-                    }
-                    store16(blk + kOffKT + (size_t)s2 * 16, vals);
-                } else {                                       // P[mb][mbk][lane]
-                    const int s3 = slot - 2 * 2 * 4 * 64;
-                    const int mb = s3 >> 7, mbk = (s3 >> 6) & 1;
-                    const int t = 32 * mb + s32;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int s = 32 * mbk + kx(i, sh);
-                        vals[i] = (s <= t && t < L) ? __expf(gj[t] - gj[s]) * Sqk[t * 64 + s] : 0.0f;
-                    }
-                    store16(blk + kOffP + (size_t)s3 * 16, vals);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int so = 32 * ks + 8 * g4;
+                    const uint4 tr = ld16(Tb + (16 * mt + l16) * SB + so);
+                    wacc = mfma_bf16(ld16(KbT + (16 * kb + l16) * SB + so), tr, wacc);
+                    uacc = mfma_bf16(tr, ld16(VbT + (16 * kb + l16) * SB + so), uacc);
                 }
+                Ud[bb][mt] = uacc;
+                // lane holds W[t = 16mt + l16][16kb + 4g4 + i]: WT rows and half of a WQ slot
+#pragma unroll
+                for (int i = 0; i < 4; ++i) WT[(16 * kb + 4 * g4 + i) * SB + 16 * mt + l16] = f2bf(wacc[i]);
+                uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(wave * 8 + mt) * 64 + lane) * 8 + 4 * bb);
+                *wq = make_uint2(pack2(wacc[0], wacc[1]), pack2(wacc[2], wacc[3]));
+                // lane holds U~[16mt + 4g4 + i][16 tile + l16], tile = kb: the accumulator layout
+                uint2 *ua = reinterpret_cast<uint2 *>(blk + kOffUA + ((size_t)(kb * 2 + (mt >> 1)) * 64 + lane) * 8 +
+                                                      4 * (mt & 1));
+                *ua = make_uint2(pack2(uacc[0], uacc[1]), pack2(uacc[2], uacc[3]));
             }
-            if (tid == 0) X.el[(size_t)(cid0 + c) * hv + h] = __expf(gL);
-            lds_barrier();
-            // W^T = Kb^T T^T and U~ = T Vb: wave w does 4 of the 16 output blocks
-            {
-                const uint16_t *Tj = Tb + jj * 64 * 64;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int b = wave * 4 + q;              // 0..7: W^T (kb, bi); 8..15: U~ (bi, tile)
-                    const bool isw = b < 8;
-                    const int x = (b & 7) >> 1, y = b & 1;   // W^T: kb = x, bi = y; U~: tile = x, bi = y
-                    f16v acc = {};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const int ko = 16 * ks + 8 * hh;
-                        const bf8v a = isw ? lds8(KbT + (32 * x + l32) * 64 + ko) : lds8(Tj + (32 * y + l32) * 64 + ko);
-                        const bf8v bb = isw ? lds8(Tj + (32 * y + l32) * 64 + ko) : lds8(VbT + (32 * x + l32) * 64 + ko);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
-                    }
-                    float vals[16];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) vals[i] = acc[i];
-                    // W^T block (kb, bi): lane l holds W[32 bi + l32][32 kb + kx(i)] = W[mb=bi][w=kb]
-                    // U~ block (bi, tile): lane l holds U~[32 bi + kx(i)][32 tile + l32] = UT[mb=bi][tile]
-                    const size_t off = isw ? kOffW + ((size_t)(y * 4 + x) * 64 + lane) * 16
-                                           : kOffUT + ((size_t)(y * 4 + x) * 64 + lane) * 16;
-                    store16(blk + off, vals);
-                }
-            }
-            lds_barrier();
         }
     }
-}
-
-// ---------------------------------------------------------------- sweep
-__device__ __forceinline__ float bfat(const uint4 (&v)[2], int i)
-{
-    const uint4 &u = v[i >> 3];
-    const int k = (i & 7) >> 1;
-    const uint32_t w = k == 0 ? u.x : k == 1 ? u.y : k == 2 ? u.z : u.w;
-    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-}
-
-__device__ __forceinline__ void ld2(uint4 (&v)[2], const uint16_t *p)
-{
-    v[0] = reinterpret_cast<const uint4 *>(p)[0];
-    v[1] = reinterpret_cast<const uint4 *>(p)[1];
-}
-
-__device__ __forceinline__ f16v mfma_f32(float a, float b, f16v c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
-__global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
-{
-    extern __shared__ float smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int hv = X.P.hv, n = X.P.n_seqs;
-    const int ntile = DKP / TILE;
-    const int tile = blockIdx.x % ntile;
-    const int h = (blockIdx.x / ntile) % hv;
-    const int slot = blockIdx.x / (ntile * hv);
-
-    float *red_u = smem;                     // [4 waves][2][16][64]
-    float *red_o = red_u + 4 * 2 * 16 * 64;  // [4 waves][2][16][64]
-    int *order = reinterpret_cast<int *>(red_o + 4 * 2 * 16 * 64);   // [256] prompt of each rank
-
-    // prompts by decreasing length (ties by index), so the longest chains start first
-    int pidx = slot;
-    if (n <= 256) {
-        if (tid < n) {
-            const int len = X.P.seq_start[tid + 1] - X.P.seq_start[tid];
-            int rank = 0;
-            for (int q = 0; q < n; ++q) {
-                const int lq = X.P.seq_start[q + 1] - X.P.seq_start[q];
-                rank += (lq > len) || (lq == len && q < tid);
-            }
-            order[rank] = tid;
-        }
-        lds_barrier();
-        pidx = order[slot];
-    }
-    int s0, s1, cid0;
-    if (!prompt_chunks(X, pidx, s0, s1, cid0)) return;
-    const int len = s1 - s0;
-    const int col = tile * TILE + l32;
-
-    // this wave's 32 state rows x 32 columns, in accumulator layout:
-    // register i of lane l is M[32 w + kx(i)][col]
-    float *st = X.P.state + ((size_t)pidx * hv + h) * DKP * DKP;
-    f16v M;
+    lds_barrier();   // every read of (beta v)^T done
 #pragma unroll
-    for (int i = 0; i < 16; ++i) M[i] = st[(size_t)(32 * wave + kx(i, hh)) * DKP + col];
-
-    const int nck = (len + kChunk - 1) / kChunk;
-    const size_t cstride = (size_t)hv * kBlockElems;
-    const uint16_t *blk = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
-    const int mbk = wave >> 1, i0 = 8 * (wave & 1);
-    // this lane's operands of the current chunk
-    uint4 Wo[2][2], QEo[2][2], KTo[2][2], UTo[2][2], Po[2];
-    if (nck > 0) {
+    for (int bb = 0; bb < 2; ++bb) {
+        const int tile = 2 * wave + bb;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            ld2(Wo[mb], blk + kOffW + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
-            ld2(UTo[mb], blk + kOffUT + ((size_t)(mb * 4 + tile) * 64 + lane) * 16);
-            ld2(QEo[mb], blk + kOffQE + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
-            Po[mb] = *reinterpret_cast<const uint4 *>(blk + kOffP + ((size_t)(mb * 2 + mbk) * 64 + lane) * 16 + i0);
-            ld2(KTo[mb], blk + kOffKT + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+        for (int mt = 0; mt < 4; ++mt) {
+            uint2 *dst = reinterpret_cast<uint2 *>(UT + (16 * tile + l16) * SB + 16 * mt + 4 * g4);
+            *dst = make_uint2(pack2(Ud[bb][mt][0], Ud[bb][mt][1]), pack2(Ud[bb][mt][2], Ud[bb][mt][3]));
         }
     }
-    for (int c = 0; c < nck; ++c) {
-        const int r0 = s0 + c * kChunk;
-        const int L = min(kChunk, s1 - r0);
-        const bool more = c + 1 < nck;
-        const uint16_t *bn = blk + (size_t)(c + 1) * cstride;
-        const float eL = X.el[(size_t)(cid0 + c) * hv + h];
+    lds_barrier();
 
-        // partial of W M0 over this wave's 32 state rows
-        f16v up[2];
+    // ---- Q'^T = (e^gamma q^)^T - W^T P^T, the lower half of WQ
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            up[mb] = f16v{};
+    for (int bb = 0; bb < 2; ++bb) {
+        const int kb = 2 * wave + bb;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) up[mb] = mfma_f32(bfat(Wo[mb], i), M[i], up[mb]);
-            if (more) ld2(Wo[mb], bn + kOffW + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+        for (int mt = 0; mt < 4; ++mt) {
+            f4v acc = {};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) red_u[((wave * 2 + mb) * 16 + i) * 64 + lane] = up[mb][i];
-        }
-        lds_barrier();
-
-        // U = U~ - W M0 (every wave keeps all of it, in accumulator layout)
-        f16v U[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = red_u[((0 * 2 + mb) * 16 + i) * 64 + lane];
-                s += red_u[((1 * 2 + mb) * 16 + i) * 64 + lane];
-                s += red_u[((2 * 2 + mb) * 16 + i) * 64 + lane];
-                s += red_u[((3 * 2 + mb) * 16 + i) * 64 + lane];
-                U[mb][i] = bfat(UTo[mb], i) - s;
+            for (int ks = 0; ks < 2; ++ks) {
+                const int so = 32 * ks + 8 * g4;
+                acc = mfma_bf16(ld16(WT + (16 * kb + l16) * SB + so), ld16(Pb + (16 * mt + l16) * SB + so), acc);
             }
-            if (more) ld2(UTo[mb], bn + kOffUT + ((size_t)(mb * 4 + tile) * 64 + lane) * 16);
-        }
-
-        // partial of O: (e^gamma q) M0 over this wave's state rows, plus a quarter of P U
-        f16v op[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            op[mb] = f16v{};
-#pragma unroll
-            for (int i = 0; i < 16; ++i) op[mb] = mfma_f32(bfat(QEo[mb], i), M[i], op[mb]);
-            const uint4 pv[2] = {Po[mb], Po[mb]};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) op[mb] = mfma_f32(bfat(pv, i), U[mbk][i0 + i], op[mb]);
-            if (more) {
-                ld2(QEo[mb], bn + kOffQE + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
-                Po[mb] = *reinterpret_cast<const uint4 *>(bn + kOffP + ((size_t)(mb * 2 + mbk) * 64 + lane) * 16 + i0);
+            // lane holds (P W)[t = 16mt + l16][16kb + 4g4 + i]
+            const int t = 16 * mt + l16;
+            float q[4] = {0.f, 0.f, 0.f, 0.f};
+            if (t < L) {
+                const uint2 qv = *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * kb + 4 * g4);
+                q[0] = __uint_as_float(qv.x << 16);
+                q[1] = __uint_as_float(qv.x & 0xffff0000u);
+                q[2] = __uint_as_float(qv.y << 16);
+                q[3] = __uint_as_float(qv.y & 0xffff0000u);
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red_o[((wave * 2 + mb) * 16 + i) * 64 + lane] = op[mb][i];
-        }
-        lds_barrier();
-
-        // O rows: wave w sums the four partials of registers [i0, i0 + 8) of block mbk
-#pragma unroll
-        for (int i = i0; i < i0 + 8; ++i) {
-            const int row = 32 * mbk + kx(i, hh);
-            float s = red_o[((0 * 2 + mbk) * 16 + i) * 64 + lane];
-            s += red_o[((1 * 2 + mbk) * 16 + i) * 64 + lane];
-            s += red_o[((2 * 2 + mbk) * 16 + i) * 64 + lane];
-            s += red_o[((3 * 2 + mbk) * 16 + i) * 64 + lane];
-            if (row < L) X.P.out[((size_t)(r0 + row) * hv + h) * DKP + col] = s;
-        }
-
-        // M <- e^{gamma_L} M0 + (e^{gamma_L - gamma} k)^T U on this wave's rows
-#pragma unroll
-        for (int i = 0; i < 16; ++i) M[i] *= eL;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) M = mfma_f32(bfat(KTo[mb], i), U[mb][i], M);
-            if (more) ld2(KTo[mb], bn + kOffKT + ((size_t)(mb * 4 + wave) * 64 + lane) * 16);
+            const float e = eg[t];
+            uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(wave * 8 + 4 + mt) * 64 + lane) * 8 + 4 * bb);
+            *wq = make_uint2(pack2(fmaf(e, q[0], -acc[0]), fmaf(e, q[1], -acc[1])),
+                             pack2(fmaf(e, q[2], -acc[2]), fmaf(e, q[3], -acc[3])));
         }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st[(size_t)(32 * wave + kx(i, hh)) * DKP + col] = M[i];
+    // U~ in the B-operand layout of the sweep's P U~
+    for (int u = tid; u < NTILE * 2 * 64; u += 256) {
+        const int l = u & 63, tile = u >> 7, kb = (u >> 6) & 1;
+        st16(blk + kOffUB + (size_t)u * 8, ld16(UT + (16 * tile + (l & 15)) * SB + 32 * kb + 8 * (l >> 4)));
+    }
 
     // the prompt's conv tail: its last three raw rows, continuing into the old
-    // tail when the prompt is shorter (one workgroup a prompt, read then write)
-    if (h == 0 && tile == 0 && len > 0) {
-        const int C = X.P.C;
+    // tail when the prompt is shorter (the prologue, which reads the old tail,
+    // has finished: this launch follows it on the stream)
+    if (h == 0 && r0 + L == s1) {
+        const int C = X.P.C, len = s1 - s0;
         uint16_t *tl = X.P.conv_tail + (size_t)pidx * 3 * C;
         for (int ch = tid; ch < C; ch += 256) {
             uint16_t nt[3];
@@ -605,24 +576,139 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     }
 }
 
-size_t prologue_lds(int r)
+// ---------------------------------------------------------------- sweep
+__global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 {
-    const size_t nch = (size_t)(2 + r) * DKP;
-    return sizeof(float) * PRO_ROWS * 2 * DKP + sizeof(float) * 4 * nch +
-           sizeof(uint16_t) * (PRO_ROWS + 3) * nch + sizeof(int) * 2 * PRO_ROWS;
-}
-size_t intra_lds()
-{
-    return sizeof(uint16_t) * 64 * 2 * DKP + sizeof(float) * (2 * 64 * 64 + HB * 64 * 64 + 2 * HB * 64) +
-           sizeof(uint16_t) * HB * 64 * 64;
-}
-size_t sweep_lds() { return sizeof(float) * (2 * 4 * 2 * 16 * 64) + sizeof(int) * 256; }
+    __shared__ f4v red[4][8][64];   // per wave: partial [W; Q'] M0, 8 row blocks
+    __shared__ int order[256];      // prompt of each length rank
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: operand bases stay scalar
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int hv = X.P.hv, n = X.P.n_seqs;
+    // workgroup i runs on XCD i % 8: the 8 tiles of one (prompt, head) go to one XCD
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int tile = q & (NTILE - 1);
+    const int grp = ((q / NTILE) << 3) + xcd;
+    if (grp >= n * hv) return;
+    const int rank = grp / hv, h = grp - rank * hv;
 
-template <typename K>
-hipError_t allow(K kernel, size_t bytes)
-{
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)bytes);
+    // prompts by decreasing length (ties by index): the longest chains start first
+    int pidx = rank;
+    if (n <= 256) {
+        if (tid < n) {
+            const int len = X.P.seq_start[tid + 1] - X.P.seq_start[tid];
+            int rk = 0;
+            for (int p = 0; p < n; ++p) {
+                const int lp = X.P.seq_start[p + 1] - X.P.seq_start[p];
+                rk += (lp > len) || (lp == len && p < tid);
+            }
+            order[rk] = tid;
+        }
+        lds_barrier();
+        pidx = order[rank];
+    }
+    int s0, s1, cid0;
+    if (!prompt_chunks(X, pidx, s0, s1, cid0)) return;
+    const int nck = (s1 - s0 + kChunk - 1) / kChunk;
+    if (nck == 0) return;
+    const int col = 16 * tile + l16;
+
+    // state rows [32 wave, 32 wave + 32), column col; block b register i is
+    // row 32 wave + 16 b + 4 g4 + i (the 16x16 accumulator layout)
+    float *st = X.P.state + ((size_t)pidx * hv + h) * D * D + col;
+    f4v M[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M[b][i] = st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D];
+
+    const size_t cstride = (size_t)hv * kBlockElems;
+    const uint16_t *bp = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
+    const uint16_t *pWQ = bp + kOffWQ + ((size_t)wave * 8 * 64 + lane) * 8;
+    const uint16_t *pKT = bp + kOffKT + ((size_t)wave * 4 * 64 + lane) * 8;
+    const uint16_t *pUA = bp + kOffUA + ((size_t)tile * 2 * 64 + lane) * 8;
+    const uint16_t *pUB = bp + kOffUB + ((size_t)tile * 2 * 64 + lane) * 8;
+    const uint16_t *pPA = bp + kOffPA + ((size_t)wave * 2 * 64 + lane) * 8;
+    const float *pel = X.el + (size_t)cid0 * hv + h;
+
+    uint4 wq[8], kt[4], ua[2], ub[2], pa[2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) wq[m] = ld16(pWQ + m * 512);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + j * 512);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        ua[j] = ld16(pUA + j * 512);
+        ub[j] = ld16(pUB + j * 512);
+        pa[j] = ld16(pPA + j * 512);
+    }
+
+    for (int c = 0; c < nck; ++c) {
+        const int r0 = s0 + c * kChunk;
+        const int L = min(kChunk, s1 - r0);
+        const bool more = c + 1 < nck;
+        const size_t nx = (size_t)(c + 1) * cstride;
+        const float eL = pel[(size_t)c * hv];
+
+        // partial [W; Q'] M0 over this wave's state rows
+        f4v acc[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) acc[m] = mfma_f32(bfe(wq[m], e), M[e >> 2][e & 3], acc[m]);
+        if (more) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) wq[m] = ld16(pWQ + nx + m * 512);
+        }
+        lds_barrier();   // every wave has read the previous chunk's partials
+#pragma unroll
+        for (int m = 0; m < 8; ++m) red[wave][m][lane] = acc[m];
+        lds_barrier();
+
+        // U = U~ - W M0 (all 64 rows, every wave), O rows of block 4 + wave
+        f4v U[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f4v s = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) U[m][i] = bfe(ua[m >> 1], 4 * (m & 1) + i) - s[i];
+        }
+        f4v o = ((red[0][4 + wave][lane] + red[1][4 + wave][lane]) + red[2][4 + wave][lane]) + red[3][4 + wave][lane];
+        o = mfma_bf16(pa[0], ub[0], o);
+        o = mfma_bf16(pa[1], ub[1], o);
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                ua[j] = ld16(pUA + nx + j * 512);
+                ub[j] = ld16(pUB + nx + j * 512);
+                pa[j] = ld16(pPA + nx + j * 512);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * wave + 4 * g4 + i;
+            if (row < L) X.P.out[((size_t)(r0 + row) * hv + h) * D + col] = o[i];
+        }
+
+        // M <- e^{gamma_L} M + K~^T U on this wave's rows
+#pragma unroll
+        for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                M[b] = mfma_f32(bfe(kt[2 * b + (e >> 3)], e & 7), U[e >> 2][e & 3], M[b]);
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + nx + j * 512);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D] = M[b][i];
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -650,7 +736,7 @@ PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int n_seqs, int T)
 
 bool prefill_supported(int hk, int hv, int dk, int dv)
 {
-    return dk == DKP && dv == DKP && hk > 0 && hv % hk == 0 && hv / hk <= 8;
+    return dk == D && dv == D && hk > 0 && hv % hk == 0 && hv / hk <= 8;
 }
 
 size_t prefill_workspace_bytes(int hk, int hv, int dk, int dv, int n_seqs, int total_rows)
@@ -675,17 +761,16 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     X.blk = reinterpret_cast<uint16_t *>(ws + Lo.blk);
     X.el = reinterpret_cast<float *>(ws + Lo.el);
 
-    static const hipError_t e1 = allow(prologue_kernel, prologue_lds(8));
-    static const hipError_t e2 = allow(intra_kernel, intra_lds());
-    static const hipError_t e3 = allow(sweep_kernel, sweep_lds());
-    if (e1 != hipSuccess) return e1;
-    if (e2 != hipSuccess) return e2;
-    if (e3 != hipSuccess) return e3;
+    static const hipError_t e_lds = hipFuncSetAttribute(reinterpret_cast<const void *>(intra_kernel),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kIntraLds);
+    if (e_lds != hipSuccess) return e_lds;
 
-    hipLaunchKernelGGL(prologue_kernel, dim3((P.total_rows + PRO_ROWS - 1) / PRO_ROWS, P.hk), dim3(256),
-                       prologue_lds(X.r), stream, X);
-    hipLaunchKernelGGL(intra_kernel, dim3((unsigned)P.n_seqs * X.max_chunks, P.hk), dim3(256), intra_lds(), stream, X);
-    hipLaunchKernelGGL(sweep_kernel, dim3((unsigned)P.n_seqs * P.hv * (DKP / TILE)), dim3(256), sweep_lds(), stream, X);
+    const unsigned units = (unsigned)(P.C / 8);
+    hipLaunchKernelGGL(prologue_kernel, dim3((P.total_rows + PRO_ROWS - 1) / PRO_ROWS, (units + 255) / 256),
+                       dim3(256), 0, stream, X);
+    hipLaunchKernelGGL(intra_kernel, dim3((unsigned)P.n_seqs * X.max_chunks, P.hv), dim3(256), kIntraLds, stream, X);
+    const unsigned groups = (unsigned)P.n_seqs * P.hv;
+    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), 0, stream, X);
     return hipGetLastError();
 }
 
