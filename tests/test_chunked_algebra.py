@@ -17,6 +17,9 @@ whence D = U~ - W M0 with T = (I + A)^{-1}, U~ = T diag(beta) V and
 W = T diag(beta e^gamma) K.  Outputs and the state leaving the chunk are
     O = diag(e^gamma) Q M0 + P D,  P_tj = e^{gamma_t - gamma_j} q_t^T k_j (j <= t),
     M_L = e^{gamma_L} M0 + (diag(e^{gamma_L - gamma}) K)^T D.
+Since D = U~ - W M0, the output also reads O = Q' M0 + P U~ with
+Q' = diag(e^gamma) Q - P W: every product without M0 can be formed per chunk
+in parallel, and the sequential part needs only [W; Q'] M0 and the update.
 """
 import numpy as np
 import pytest
@@ -24,7 +27,7 @@ import pytest
 import oracle
 
 
-def chunked(alpha, beta, K, Q, V, M0, chunk):
+def chunked(alpha, beta, K, Q, V, M0, chunk, fold_pw=False):
     T = K.shape[0]
     M = M0.copy()
     O = np.zeros((T, V.shape[1]))
@@ -43,11 +46,16 @@ def chunked(alpha, beta, K, Q, V, M0, chunk):
         D = Ut - W @ M
         incl = np.tril(np.ones((L, L), bool))
         P = np.where(incl, np.exp(np.where(incl, diff, 0.0)), 0.0) * (q @ k.T)
-        O[c0:c1] = (np.exp(gam)[:, None] * q) @ M + P @ D
+        if fold_pw:
+            Qp = np.exp(gam)[:, None] * q - P @ W
+            O[c0:c1] = Qp @ M + P @ Ut
+        else:
+            O[c0:c1] = (np.exp(gam)[:, None] * q) @ M + P @ D
         M = np.exp(gam[-1]) * M + (np.exp(gam[-1] - gam)[:, None] * k).T @ D
     return M, O
 
 
+@pytest.mark.parametrize("fold_pw", [False, True])
 @pytest.mark.parametrize("T,chunk,dk,dv,lo,hi,seed", [
     (150, 64, 8, 6, 0.05, 1.0, 0),      # partial last chunk (22 rows)
     (64, 64, 8, 8, 0.05, 1.0, 1),       # exactly one chunk
@@ -55,7 +63,7 @@ def chunked(alpha, beta, K, Q, V, M0, chunk):
     (200, 64, 16, 8, 0.02, 0.2, 3),     # strong decay: cumulative gates reach e^-250
     (5, 64, 4, 4, 0.3, 0.9, 4),         # shorter than a chunk
 ])
-def test_chunked_form_equals_recurrence(T, chunk, dk, dv, lo, hi, seed):
+def test_chunked_form_equals_recurrence(T, chunk, dk, dv, lo, hi, seed, fold_pw):
     rng = np.random.default_rng(seed)
     K = rng.standard_normal((T, dk)); K /= np.linalg.norm(K, axis=1, keepdims=True)
     Q = rng.standard_normal((T, dk)) / np.sqrt(dk)
@@ -64,7 +72,7 @@ def test_chunked_form_equals_recurrence(T, chunk, dk, dv, lo, hi, seed):
     beta = rng.uniform(0.0, 1.0, T)
     M0 = rng.standard_normal((dk, dv)) * 0.05
     M_ref, O_ref, _ = oracle.raw_recurrence(alpha, beta, K, Q, V, M0)
-    M, O = chunked(alpha, beta, K, Q, V, M0, chunk)
+    M, O = chunked(alpha, beta, K, Q, V, M0, chunk, fold_pw)
     scale = max(1.0, np.abs(O_ref).max())
     assert np.max(np.abs(O - O_ref)) < 1e-10 * scale
     assert np.max(np.abs(M - M_ref)) < 1e-10 * max(1.0, np.abs(M_ref).max())
@@ -83,3 +91,37 @@ def test_chunk_size_does_not_change_the_result():
     M64, O64 = chunked(alpha, beta, K, Q, V, M0, 64)
     assert np.max(np.abs(O1 - O64)) < 1e-10 * np.abs(O1).max()
     assert np.max(np.abs(M1 - M64)) < 1e-10 * np.abs(M1).max()
+
+
+def blocked_unit_lower_inverse(A, nb=16):
+    """(I + A)^-1 for strictly lower-triangular A by nb x nb blocks: the
+    diagonal blocks by forward substitution, then
+    T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, one diagonal distance at a time."""
+    n = A.shape[0]
+    m = n // nb
+    blk = lambda X, i, j: X[i * nb:(i + 1) * nb, j * nb:(j + 1) * nb]
+    T = np.zeros_like(A)
+    for i in range(m):
+        Aii = blk(A, i, i)
+        Tii = np.zeros((nb, nb))
+        for t in range(nb):
+            Tii[t] = -Aii[t, :t] @ Tii[:t]
+            Tii[t, t] = 1.0
+        T[i * nb:(i + 1) * nb, i * nb:(i + 1) * nb] = Tii
+    for d in range(1, m):
+        for i in range(d, m):
+            j = i - d
+            S = sum(blk(A, i, k) @ blk(T, k, j) for k in range(j, i))
+            T[i * nb:(i + 1) * nb, j * nb:(j + 1) * nb] = -blk(T, i, i) @ S
+    return T
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_blocked_triangular_inverse(seed):
+    rng = np.random.default_rng(seed)
+    n = 64
+    A = np.tril(rng.standard_normal((n, n)) * 0.3, -1)
+    T = blocked_unit_lower_inverse(A)
+    ref = np.linalg.inv(np.eye(n) + A)
+    assert np.max(np.abs(T - ref)) < 1e-10 * max(1.0, np.abs(ref).max())
+    assert np.array_equal(np.triu(T, 1), np.zeros((n, n)))
