@@ -42,10 +42,13 @@ def window_bytes(shape, n, rows):
 
 def prefill_flops(shape, lengths, chunk=64):
     """Algorithmic flops of one chunked prompt pass, counted on the actual
-    chunk lengths L: bf16 matrix-core products K K^T and Q K^T (per key head),
-    T (beta e^gamma K) and T (beta V) (per value head); fp32 state contractions
-    W M0, (e^gamma Q) M0, (e^{gamma_L - gamma} K)^T U (2 L dk dv each) and P U
-    (2 L^2 dv), per value head."""
+    chunk lengths L (2 flops a multiply-add).  Matrix-core bf16 work inside
+    the chunks: K K^T and Q K^T (2 L^2 dk each, per key head), T (beta e^gamma K)
+    and T (beta V) (2 L^2 dk, 2 L^2 dv) and P U (2 L^2 dv), per value head.
+    fp32 state contractions across chunks, per value head: W M0 and
+    (e^gamma Q) M0, which read the state, and (e^{gamma_L - gamma} K)^T U, which
+    writes it (2 L dk dv each).  Products an implementation adds (P W here)
+    are not counted."""
     dk, dv = shape.dk, shape.dv
     sum_l = sum_l2 = 0
     for n in lengths:
@@ -53,8 +56,8 @@ def prefill_flops(shape, lengths, chunk=64):
             L = min(chunk, n - c0)
             sum_l += L
             sum_l2 += L * L
-    bf16 = shape.hk * 2 * (2 * sum_l2 * dk) + shape.hv * (2 * sum_l2 * dk + 2 * sum_l2 * dv)
-    fp32 = shape.hv * (3 * 2 * sum_l * dk * dv + 2 * sum_l2 * dv)
+    bf16 = shape.hk * 2 * (2 * sum_l2 * dk) + shape.hv * (2 * sum_l2 * dk + 2 * 2 * sum_l2 * dv)
+    fp32 = shape.hv * 3 * 2 * sum_l * dk * dv
     return bf16, fp32
 
 
