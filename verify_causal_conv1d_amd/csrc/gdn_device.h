@@ -12,13 +12,16 @@ typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16f(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (a NaN stays a NaN).
-__device__ __forceinline__ uint16_t f2bf(float f)
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even: gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two fp32 values -> packed bf16 bits (lo in bits 0..15), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const bf2v v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // softplus(x) = log(1 + e^x) without overflow or cancellation.

@@ -70,12 +70,14 @@ constexpr int NTILE = D / 16;   // 16-column state tiles of a head
 //   PA [w 4][kb 2][l][j]        = P[16w + l16][32kb + 8g4 + j]      (bf16 MFMA A operand)
 // Rows past the chunk's end are zero in every array.
 constexpr int kOffWQ = 0, kOffKT = 16384, kOffUA = 24576, kOffUB = 32768, kOffPA = 40960;
+// Word 3 of a raw buffer resource on gfx9-family chips (gfx950 included):
+// 32-bit data format, no swizzle; accesses past num_records are dropped.
+constexpr int kBufferDword3 = 0x00020000;
 constexpr int kBlockElems = 45056;
 
 struct Ctx {
     PrefillArgs P;
     int r;                      // value heads per key head
-    int max_chunks;             // chunks of the longest prompt (bounds the intra grid)
     int nc_total;               // chunk blocks in the workspace
     uint16_t *qk, *v, *blk;
     float *g, *be, *el;
@@ -102,6 +104,34 @@ __device__ bool prompt_chunks(const Ctx &X, int p, int &s0, int &s1, int &cid0)
     return base + (s1 - s0 + kChunk - 1) / kChunk <= X.nc_total;
 }
 
+// The prompt and in-prompt chunk of dense chunk index cid (chunks numbered
+// prompt after prompt).  False if cid is past the last chunk or the layout
+// breaks the rules at or before its prompt (the same prompts prompt_chunks
+// refuses).
+__device__ bool chunk_at(const Ctx &X, int cid, int &p, int &c, int &s0, int &s1)
+{
+    const int T = X.P.total_rows;
+    int base = 0;
+    int prev = X.P.seq_start[0];
+    if (prev < 0) return false;
+    for (int q = 0; q < X.P.n_seqs; ++q) {
+        const int a = X.P.seq_start[q], b = X.P.seq_start[q + 1];
+        if (a != prev || b < a || b > T || b - a > X.P.max_len) return false;
+        prev = b;
+        const int nq = (b - a + kChunk - 1) / kChunk;
+        if (cid < base + nq) {
+            if (base + nq > X.nc_total) return false;
+            p = q;
+            c = cid - base;
+            s0 = a;
+            s1 = b;
+            return true;
+        }
+        base += nq;
+    }
+    return false;
+}
+
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(uint16_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 __device__ __forceinline__ bf8v as_bf8(uint4 v) { return __builtin_bit_cast(bf8v, v); }
@@ -111,11 +141,6 @@ __device__ __forceinline__ float bfe(const uint4 &u, int e)
 {
     const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-}
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi)
-{
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
 
 __device__ __forceinline__ f4v mfma_f32(float a, float b, f4v c)
@@ -298,14 +323,12 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
     const int l16 = lane & 15, g4 = lane >> 4;
     const int l32 = lane & 31, hh = lane >> 5;
     const int h = blockIdx.y, kh = h / X.r;
-    const int pidx = blockIdx.x / X.max_chunks, c = blockIdx.x - pidx * X.max_chunks;
-    int s0, s1, cid0;
-    if (!prompt_chunks(X, pidx, s0, s1, cid0)) return;
+    int pidx, c, s0, s1;
+    if (!chunk_at(X, blockIdx.x, pidx, c, s0, s1)) return;
     const int r0 = s0 + c * kChunk;
-    if (r0 >= s1) return;
     const int L = min(kChunk, s1 - r0);
     const int hv = X.P.hv, hk = X.P.hk;
-    const size_t cidh = (size_t)(cid0 + c) * hv + h;
+    const size_t cidh = (size_t)blockIdx.x * hv + h;
     uint16_t *blk = X.blk + cidh * kBlockElems;
 
     float *An = reinterpret_cast<float *>(lds + kIntraAn);
@@ -343,20 +366,36 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
         if (lane == 0) X.el[cidh] = __expf(gL);
     }
 
-    // ---- K K^T and Q K^T, wave w: the 32 x 32 block (w >> 1, w & 1)
-    f16v S = {}, QK = {};
+    // every global operand of the first phases is requested at once, so the
+    // workgroup pays one memory latency for them
+    constexpr int NB = 8;
+    uint4 ka[D / 16], qa[D / 16], kb[D / 16], raw[NB];
     {
         const int bi = wave >> 1, bj = wave & 1;
         const int ra = 32 * bi + l32, rb = 32 * bj + l32;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const int ko = 16 * ks + 8 * hh;
-            const uint4 ka = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;
-            const uint4 qa = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;
-            const uint4 kb = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ka), as_bf8(kb), S, 0, 0, 0);
-            QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qa), as_bf8(kb), QK, 0, 0, 0);
+            ka[ks] = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;
+            qa[ks] = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;
+            kb[ks] = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;
         }
+        // rows for (beta e^gamma k^)^T and (beta v)^T: lanes take consecutive
+        // rows s, so the transposed LDS writes below are contiguous
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int idx = k * 256 + tid;          // 0..2047: 16 column groups x 64 rows, K then V
+            const int which = idx >> 10, s = idx & 63, q8 = ((idx >> 6) & 15) * 8;
+            raw[k] = s < L ? ld16(which ? Vg + s * vrow + q8 : Kg + s * qkrow + q8) : z4;
+        }
+    }
+
+    // ---- K K^T and Q K^T, wave w: the 32 x 32 block (w >> 1, w & 1)
+    f16v S = {}, QK = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ka[ks]), as_bf8(kb[ks]), S, 0, 0, 0);
+        QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qa[ks]), as_bf8(kb[ks]), QK, 0, 0, 0);
     }
     lds_barrier();   // gamma, beta visible
 
@@ -374,17 +413,8 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             Pb[t * SB + s] = f2bf(dec * QK[i]);
         }
     }
-    // (beta e^gamma k^)^T and (beta v)^T: lanes take consecutive rows s, so the
-    // transposed LDS writes are contiguous
+    // (beta e^gamma k^)^T and (beta v)^T
     {
-        constexpr int NB = 8;
-        uint4 raw[NB];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const int idx = k * 256 + tid;          // 0..2047: 16 column groups x 64 rows, K then V
-            const int which = idx >> 10, s = idx & 63, q8 = ((idx >> 6) & 15) * 8;
-            raw[k] = s < L ? ld16(which ? Vg + s * vrow + q8 : Kg + s * qkrow + q8) : z4;
-        }
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const int idx = k * 256 + tid;
@@ -395,20 +425,33 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             for (int e = 0; e < 8; ++e) dst[e * SB] = f2bf(sc * bfe(raw[k], e));
         }
     }
-    // K~ = e^{gamma_L - gamma} k^ in the sweep's lane order
-    for (int u = tid; u < 1024; u += 256) {
-        const int l = u & 63, ul16 = l & 15, ug4 = l >> 4;
-        const int e_blk = u >> 6;                 // (w, b, mp)
-        const int w = e_blk >> 2, b = (e_blk >> 1) & 1, mp = e_blk & 1;
-        const int kr = 32 * w + 16 * b + ul16;
-        float v[8];
+    // K~ = e^{gamma_L - gamma} k^ in the sweep's lane order (all loads first)
+    {
+        uint16_t kv[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = 16 * (2 * mp + (e >> 2)) + 4 * ug4 + (e & 3);
-            v[e] = t < L ? ekt[t] * bf16f(Kg[t * qkrow + kr]) : 0.0f;
+        for (int r = 0; r < 4; ++r) {
+            const int u = r * 256 + tid;
+            const int l = u & 63, e_blk = u >> 6;    // (w, b, mp)
+            const int kr = 32 * (e_blk >> 2) + 16 * ((e_blk >> 1) & 1) + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 16 * (2 * (e_blk & 1) + (e >> 2)) + 4 * (l >> 4) + (e & 3);
+                kv[r][e] = t < L ? Kg[t * qkrow + kr] : (uint16_t)0;
+            }
         }
-        st16(blk + kOffKT + (size_t)u * 8,
-             make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int u = r * 256 + tid;
+            const int l = u & 63, e_blk = u >> 6;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 16 * (2 * (e_blk & 1) + (e >> 2)) + 4 * (l >> 4) + (e & 3);
+                v[e] = ekt[t] * bf16f(kv[r][e]);
+            }
+            st16(blk + kOffKT + (size_t)u * 8,
+                 make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
+        }
     }
     lds_barrier();
 
@@ -481,6 +524,18 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
     }
     lds_barrier();
 
+    // q^ values the Q' epilogue needs, requested now so the products below
+    // hide their latency: lane holds q^[16mt + l16][16kb + 4g4 .. + 3]
+    uint2 qv[2][4];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int t = 16 * mt + l16;
+            qv[bb][mt] = t < L ? *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * (2 * wave + bb) + 4 * g4)
+                               : make_uint2(0, 0);
+        }
+
     // ---- W^T = (beta e^gamma k^)^T T^T and U~ = T (beta v); wave w takes
     // key column blocks kb = 2w, 2w + 1 of W^T and value tiles 2w, 2w + 1 of U~
     f4v Ud[2][4];
@@ -537,14 +592,9 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             }
             // lane holds (P W)[t = 16mt + l16][16kb + 4g4 + i]
             const int t = 16 * mt + l16;
-            float q[4] = {0.f, 0.f, 0.f, 0.f};
-            if (t < L) {
-                const uint2 qv = *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * kb + 4 * g4);
-                q[0] = __uint_as_float(qv.x << 16);
-                q[1] = __uint_as_float(qv.x & 0xffff0000u);
-                q[2] = __uint_as_float(qv.y << 16);
-                q[3] = __uint_as_float(qv.y & 0xffff0000u);
-            }
+            const uint2 qq = qv[bb][mt];
+            const float q[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xffff0000u),
+                                __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xffff0000u)};
             const float e = eg[t];
             uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(wave * 8 + 4 + mt) * 64 + lane) * 8 + 4 * bb);
             *wq = make_uint2(pack2(fmaf(e, q[0], -acc[0]), fmaf(e, q[1], -acc[1])),
@@ -577,10 +627,107 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
 }
 
 // ---------------------------------------------------------------- sweep
+constexpr int kSweepLds = 2 * 4 * 8 * 64 * 16 + 256 * 4;
+
+// One chunk's sweep operands, as each lane reads them (bf16, 8 a vector).
+struct Operands {
+    uint4 wq[8], kt[4], ua[2], ub[2], pa[2];
+    float el;   // e^{gamma_L}
+    __device__ __forceinline__ void load(const uint16_t *pWQ, const uint16_t *pKT, const uint16_t *pUA,
+                                         const uint16_t *pUB, const uint16_t *pPA, const float *pel,
+                                         size_t off, size_t eoff)
+    {
+        el = pel[eoff];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) wq[m] = ld16(pWQ + off + m * 512);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + off + j * 512);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            ua[j] = ld16(pUA + off + j * 512);
+            ub[j] = ld16(pUB + off + j * 512);
+            pa[j] = ld16(pPA + off + j * 512);
+        }
+    }
+};
+
+struct SweepCtx {
+    const Ctx &X;
+    int wave, lane, l16, g4, h, col, s0, s1, nck;
+    size_t cstride;
+    const float *pel;
+    const uint16_t *pWQ, *pKT, *pUA, *pUB, *pPA;
+    f4v (*red)[4][8][64];
+};
+
+// Chunk c of one (prompt, head, tile): cur holds its operands, nxt receives
+// chunk c + 1's (clamped to the last chunk).  M is this wave's state slice.
+__device__ __forceinline__ void sweep_chunk(const SweepCtx &S, int c, Operands &cur, Operands &nxt, f4v (&M)[2])
+{
+    const int hv = S.X.P.hv;
+    const int r0 = S.s0 + c * kChunk;
+    const int L = min(kChunk, S.s1 - r0);
+    const int cn = min(c + 1, S.nck - 1);
+    nxt.load(S.pWQ, S.pKT, S.pUA, S.pUB, S.pPA, S.pel, (size_t)cn * S.cstride, (size_t)cn * hv);
+    // keep these requests ahead of the chunk's work: they have the whole
+    // chunk to arrive
+    __builtin_amdgcn_sched_barrier(0);
+    const float eL = cur.el;
+
+    // partial [W; Q'] M0 over this wave's state rows
+    f4v acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] = mfma_f32(bfe(cur.wq[m], e), M[e >> 2][e & 3], acc[m]);
+
+    f4v (*rb)[8][64] = S.red[c & 1];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) rb[S.wave][m][S.lane] = acc[m];
+    lds_barrier();
+
+    // U = U~ - W M0 (all 64 rows, every wave), O rows of block 4 + wave
+    f4v U[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const f4v s = ((rb[0][m][S.lane] + rb[1][m][S.lane]) + rb[2][m][S.lane]) + rb[3][m][S.lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[m][i] = bfe(cur.ua[m >> 1], 4 * (m & 1) + i) - s[i];
+    }
+    const int w = S.wave;
+    f4v o = ((rb[0][4 + w][S.lane] + rb[1][4 + w][S.lane]) + rb[2][4 + w][S.lane]) + rb[3][4 + w][S.lane];
+    o = mfma_bf16(cur.pa[0], cur.ub[0], o);
+    o = mfma_bf16(cur.pa[1], cur.ub[1], o);
+    {
+        const size_t orow = (size_t)hv * D;   // floats a packed output row
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            S.X.P.out + (size_t)r0 * orow, 0, (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * S.g4 + i;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[i]), orsrc,
+                                                  (int)(((size_t)row * orow + (size_t)S.h * D + S.col) * 4), 0, 0);
+        }
+    }
+
+    // M <- e^{gamma_L} M + K~^T U on this wave's rows
+#pragma unroll
+    for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) M[b] = mfma_f32(bfe(cur.kt[2 * b + (e >> 3)], e & 7), U[e >> 2][e & 3], M[b]);
+}
+
 __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 {
-    __shared__ f4v red[4][8][64];   // per wave: partial [W; Q'] M0, 8 row blocks
-    __shared__ int order[256];      // prompt of each length rank
+    // per buffer and wave: partial [W; Q'] M0, 8 row blocks; two buffers, so
+    // one barrier a chunk orders both the writes and the previous reads
+    extern __shared__ __align__(16) unsigned char lds[];
+    f4v (*red)[4][8][64] = reinterpret_cast<f4v (*)[4][8][64]>(lds);
+    int *order = reinterpret_cast<int *>(lds + 2 * 4 * 8 * 64 * 16);   // prompt of each length rank
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: operand bases stay scalar
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -631,80 +778,20 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     const uint16_t *pPA = bp + kOffPA + ((size_t)wave * 2 * 64 + lane) * 8;
     const float *pel = X.el + (size_t)cid0 * hv + h;
 
-    uint4 wq[8], kt[4], ua[2], ub[2], pa[2];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) wq[m] = ld16(pWQ + m * 512);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + j * 512);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        ua[j] = ld16(pUA + j * 512);
-        ub[j] = ld16(pUB + j * 512);
-        pa[j] = ld16(pPA + j * 512);
+    // Two operand sets: chunk c computes from one while the other receives
+    // chunk c + 1 (the last chunk requests its own again).  The loop runs two
+    // chunks an iteration with the sets swapped, so no register copy, and no
+    // wait for a load just issued, sits at the loop's back edge.  Output rows
+    // past a chunk's end are dropped by the buffer range check, not a branch.
+    Operands A, B;
+    A.load(pWQ, pKT, pUA, pUB, pPA, pel, 0, 0);
+    const SweepCtx S{X, wave, lane, l16, g4, h, col, s0, s1, nck, cstride, pel, pWQ, pKT, pUA, pUB, pPA, red};
+    int c = 0;
+    for (; c + 1 < nck; c += 2) {
+        sweep_chunk(S, c, A, B, M);
+        sweep_chunk(S, c + 1, B, A, M);
     }
-
-    for (int c = 0; c < nck; ++c) {
-        const int r0 = s0 + c * kChunk;
-        const int L = min(kChunk, s1 - r0);
-        const bool more = c + 1 < nck;
-        const size_t nx = (size_t)(c + 1) * cstride;
-        const float eL = pel[(size_t)c * hv];
-
-        // partial [W; Q'] M0 over this wave's state rows
-        f4v acc[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[m] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int m = 0; m < 8; ++m) acc[m] = mfma_f32(bfe(wq[m], e), M[e >> 2][e & 3], acc[m]);
-        if (more) {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) wq[m] = ld16(pWQ + nx + m * 512);
-        }
-        lds_barrier();   // every wave has read the previous chunk's partials
-#pragma unroll
-        for (int m = 0; m < 8; ++m) red[wave][m][lane] = acc[m];
-        lds_barrier();
-
-        // U = U~ - W M0 (all 64 rows, every wave), O rows of block 4 + wave
-        f4v U[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f4v s = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) U[m][i] = bfe(ua[m >> 1], 4 * (m & 1) + i) - s[i];
-        }
-        f4v o = ((red[0][4 + wave][lane] + red[1][4 + wave][lane]) + red[2][4 + wave][lane]) + red[3][4 + wave][lane];
-        o = mfma_bf16(pa[0], ub[0], o);
-        o = mfma_bf16(pa[1], ub[1], o);
-        if (more) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                ua[j] = ld16(pUA + nx + j * 512);
-                ub[j] = ld16(pUB + nx + j * 512);
-                pa[j] = ld16(pPA + nx + j * 512);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * wave + 4 * g4 + i;
-            if (row < L) X.P.out[((size_t)(r0 + row) * hv + h) * D + col] = o[i];
-        }
-
-        // M <- e^{gamma_L} M + K~^T U on this wave's rows
-#pragma unroll
-        for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                M[b] = mfma_f32(bfe(kt[2 * b + (e >> 3)], e & 7), U[e >> 2][e & 3], M[b]);
-        if (more) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + nx + j * 512);
-        }
-    }
+    if (c < nck) sweep_chunk(S, c, A, B, M);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -752,7 +839,6 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     Ctx X;
     X.P = P;
     X.r = P.hv / P.hk;
-    X.max_chunks = (P.max_len + kChunk - 1) / kChunk;
     X.nc_total = Lo.max_chunks_total;
     X.qk = reinterpret_cast<uint16_t *>(ws + Lo.qk);
     X.v = reinterpret_cast<uint16_t *>(ws + Lo.v);
@@ -764,13 +850,16 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     static const hipError_t e_lds = hipFuncSetAttribute(reinterpret_cast<const void *>(intra_kernel),
                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kIntraLds);
     if (e_lds != hipSuccess) return e_lds;
+    static const hipError_t e_lds2 = hipFuncSetAttribute(reinterpret_cast<const void *>(sweep_kernel),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kSweepLds);
+    if (e_lds2 != hipSuccess) return e_lds2;
 
     const unsigned units = (unsigned)(P.C / 8);
     hipLaunchKernelGGL(prologue_kernel, dim3((P.total_rows + PRO_ROWS - 1) / PRO_ROWS, (units + 255) / 256),
                        dim3(256), 0, stream, X);
-    hipLaunchKernelGGL(intra_kernel, dim3((unsigned)P.n_seqs * X.max_chunks, P.hv), dim3(256), kIntraLds, stream, X);
+    hipLaunchKernelGGL(intra_kernel, dim3((unsigned)X.nc_total, P.hv), dim3(256), kIntraLds, stream, X);
     const unsigned groups = (unsigned)P.n_seqs * P.hv;
-    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), 0, stream, X);
+    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), kSweepLds, stream, X);
     return hipGetLastError();
 }
 
