@@ -58,22 +58,22 @@ constexpr int PRO_ROWS = 32;    // packed rows a prologue workgroup walks
 constexpr int NTILE = D / 16;   // 16-column state tiles of a head
 
 // A chunk-head block of sweep operands (bf16), every sub-array in lane order
-// [..][64 lanes][8 values]; lane l = (l16, g4) = (l & 15, l >> 4), and
+// [..][64 lanes][values]; lane l = (l16, g4) = (l & 15, l >> 4), and
 // accumulator register i of a 16x16 block holds row 4 g4 + i, column l16.
-//   WQ [w 4][m 8][l][4b+i]      = WQ[16m + l16][32w + 16b + 4g4 + i]
-//        WQ = [W; Q'] (128 x dk); the A operand of step (b, i) of the
-//        wave-w partial for output rows 16m..16m+15
+//   WQ [w 4][kb 8][l][8]        e < 4:  W[16w + l16][16kb + 4g4 + e]
+//                               e >= 4: Q'[16w + l16][16kb + 4g4 + e - 4]
+//        the A operands of k-step (kb, i) for output rows 16w..16w+15 of
+//        W M0 and Q' M0; step (kb, i) reads state rows 16kb + 4g4 + i
 //   KT [w 4][b 2][mp 2][l][e]   = K~[16m + 4g4 + i][32w + 16b + l16],
 //        m = 2mp + e/4, i = e%4, K~ = e^{gamma_L - gamma} k^
-//   UA [tile 8][mp 2][l][e]     = U~[16m + 4g4 + i][16tile + l16]   (accumulator layout)
-//   UB [tile 8][kb 2][l][j]     = U~[32kb + 8g4 + j][16tile + l16]  (bf16 MFMA B operand)
-//   PA [w 4][kb 2][l][j]        = P[16w + l16][32kb + 8g4 + j]      (bf16 MFMA A operand)
-// Rows past the chunk's end are zero in every array.
-constexpr int kOffWQ = 0, kOffKT = 16384, kOffUA = 24576, kOffUB = 32768, kOffPA = 40960;
+//   UA [tile 8][w 4][l][4]      = U~[16w + 4g4 + i][16tile + l16]   (accumulator layout)
+// Rows past the chunk's end are zero in every array.  The chunk's P U~ goes
+// straight to the output rows (fp32), where the sweep adds Q' M0.
+constexpr int kOffWQ = 0, kOffKT = 16384, kOffUA = 24576;
+constexpr int kBlockElems = 32768;
 // Word 3 of a raw buffer resource on gfx9-family chips (gfx950 included):
 // 32-bit data format, no swizzle; accesses past num_records are dropped.
 constexpr int kBufferDword3 = 0x00020000;
-constexpr int kBlockElems = 45056;
 
 struct Ctx {
     PrefillArgs P;
@@ -477,11 +477,6 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             for (int cb = w + 1; cb < 4; ++cb) Tb[t * SB + 16 * cb + j] = 0;
         }
     }
-    // P in the sweep's lane order
-    for (int u = tid; u < 512; u += 256) {
-        const int l = u & 63, w = u >> 7, kb = (u >> 6) & 1;
-        st16(blk + kOffPA + (size_t)u * 8, ld16(Pb + (16 * w + (l & 15)) * SB + 32 * kb + 8 * (l >> 4)));
-    }
     lds_barrier();
     // Stage 2: T_{i,i-1} = -B_i A_{i,i-1} B_{i-1}, wave i (An holds -A)
     if (wave >= 1) {
@@ -557,11 +552,10 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
                 // lane holds W[t = 16mt + l16][16kb + 4g4 + i]: WT rows and half of a WQ slot
 #pragma unroll
                 for (int i = 0; i < 4; ++i) WT[(16 * kb + 4 * g4 + i) * SB + 16 * mt + l16] = f2bf(wacc[i]);
-                uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(wave * 8 + mt) * 64 + lane) * 8 + 4 * bb);
+                uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kb) * 64 + lane) * 8);
                 *wq = make_uint2(pack2(wacc[0], wacc[1]), pack2(wacc[2], wacc[3]));
                 // lane holds U~[16mt + 4g4 + i][16 tile + l16], tile = kb: the accumulator layout
-                uint2 *ua = reinterpret_cast<uint2 *>(blk + kOffUA + ((size_t)(kb * 2 + (mt >> 1)) * 64 + lane) * 8 +
-                                                      4 * (mt & 1));
+                uint2 *ua = reinterpret_cast<uint2 *>(blk + kOffUA + ((size_t)(kb * 4 + mt) * 64 + lane) * 4);
                 *ua = make_uint2(pack2(uacc[0], uacc[1]), pack2(uacc[2], uacc[3]));
             }
         }
@@ -596,15 +590,38 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             const float q[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xffff0000u),
                                 __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xffff0000u)};
             const float e = eg[t];
-            uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(wave * 8 + 4 + mt) * 64 + lane) * 8 + 4 * bb);
+            uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kb) * 64 + lane) * 8 + 4);
             *wq = make_uint2(pack2(fmaf(e, q[0], -acc[0]), fmaf(e, q[1], -acc[1])),
                              pack2(fmaf(e, q[2], -acc[2]), fmaf(e, q[3], -acc[3])));
         }
     }
-    // U~ in the B-operand layout of the sweep's P U~
-    for (int u = tid; u < NTILE * 2 * 64; u += 256) {
-        const int l = u & 63, tile = u >> 7, kb = (u >> 6) & 1;
-        st16(blk + kOffUB + (size_t)u * 8, ld16(UT + (16 * tile + (l & 15)) * SB + 32 * kb + 8 * (l >> 4)));
+    // P U~ (bf16 MFMA, fp32 out) into the chunk's output rows: wave w takes
+    // value tiles 2w, 2w + 1; rows past the chunk's end are dropped by the
+    // buffer range check
+    {
+        const size_t orow = (size_t)hv * D;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            X.P.out + (size_t)r0 * orow, 0, (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int tile = 2 * wave + bb;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int so = 32 * ks + 8 * g4;
+                    acc = mfma_bf16(ld16(Pb + (16 * mt + l16) * SB + so), ld16(UT + (16 * tile + l16) * SB + so), acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * mt + 4 * g4 + i;
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(acc[i]), orsrc, (int)(((size_t)row * orow + (size_t)h * D + 16 * tile + l16) * 4),
+                        0, 0);
+                }
+            }
+        }
     }
 
     // the prompt's conv tail: its last three raw rows, continuing into the old
@@ -627,107 +644,23 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
 }
 
 // ---------------------------------------------------------------- sweep
-constexpr int kSweepLds = 2 * 4 * 8 * 64 * 16 + 256 * 4;
+// LDS of a sweep workgroup (floats).  Ms holds the state slice M0 [128][16]
+// for every wave's B operands: element (row 16kb + 4g + i, column n) sits at
+// g*kMsG + n*kMsN + 4kb + i, so a lane's four rows of one k-block are one
+// 16-byte read and the 16 lanes of a row group fall on distinct banks.  Us
+// holds U [64][16] the same way: (row 16m + 4g + i, n) at g*kUsG + n*kUsN + 4m + i.
+constexpr int kMsN = 36, kMsG = 16 * kMsN + 4;
+constexpr int kUsN = 20, kUsG = 16 * kUsN + 4;
+constexpr int kSweepMs = 4 * kMsG, kSweepUs = 4 * kUsG;
 
-// One chunk's sweep operands, as each lane reads them (bf16, 8 a vector).
-struct Operands {
-    uint4 wq[8], kt[4], ua[2], ub[2], pa[2];
-    float el;   // e^{gamma_L}
-    __device__ __forceinline__ void load(const uint16_t *pWQ, const uint16_t *pKT, const uint16_t *pUA,
-                                         const uint16_t *pUB, const uint16_t *pPA, const float *pel,
-                                         size_t off, size_t eoff)
-    {
-        el = pel[eoff];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) wq[m] = ld16(pWQ + off + m * 512);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + off + j * 512);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            ua[j] = ld16(pUA + off + j * 512);
-            ub[j] = ld16(pUB + off + j * 512);
-            pa[j] = ld16(pPA + off + j * 512);
-        }
-    }
-};
-
-struct SweepCtx {
-    const Ctx &X;
-    int wave, lane, l16, g4, h, col, s0, s1, nck;
-    size_t cstride;
-    const float *pel;
-    const uint16_t *pWQ, *pKT, *pUA, *pUB, *pPA;
-    f4v (*red)[4][8][64];
-};
-
-// Chunk c of one (prompt, head, tile): cur holds its operands, nxt receives
-// chunk c + 1's (clamped to the last chunk).  M is this wave's state slice.
-__device__ __forceinline__ void sweep_chunk(const SweepCtx &S, int c, Operands &cur, Operands &nxt, f4v (&M)[2])
-{
-    const int hv = S.X.P.hv;
-    const int r0 = S.s0 + c * kChunk;
-    const int L = min(kChunk, S.s1 - r0);
-    const int cn = min(c + 1, S.nck - 1);
-    nxt.load(S.pWQ, S.pKT, S.pUA, S.pUB, S.pPA, S.pel, (size_t)cn * S.cstride, (size_t)cn * hv);
-    // keep these requests ahead of the chunk's work: they have the whole
-    // chunk to arrive
-    __builtin_amdgcn_sched_barrier(0);
-    const float eL = cur.el;
-
-    // partial [W; Q'] M0 over this wave's state rows
-    f4v acc[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[m] = mfma_f32(bfe(cur.wq[m], e), M[e >> 2][e & 3], acc[m]);
-
-    f4v (*rb)[8][64] = S.red[c & 1];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) rb[S.wave][m][S.lane] = acc[m];
-    lds_barrier();
-
-    // U = U~ - W M0 (all 64 rows, every wave), O rows of block 4 + wave
-    f4v U[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const f4v s = ((rb[0][m][S.lane] + rb[1][m][S.lane]) + rb[2][m][S.lane]) + rb[3][m][S.lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) U[m][i] = bfe(cur.ua[m >> 1], 4 * (m & 1) + i) - s[i];
-    }
-    const int w = S.wave;
-    f4v o = ((rb[0][4 + w][S.lane] + rb[1][4 + w][S.lane]) + rb[2][4 + w][S.lane]) + rb[3][4 + w][S.lane];
-    o = mfma_bf16(cur.pa[0], cur.ub[0], o);
-    o = mfma_bf16(cur.pa[1], cur.ub[1], o);
-    {
-        const size_t orow = (size_t)hv * D;   // floats a packed output row
-        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-            S.X.P.out + (size_t)r0 * orow, 0, (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * S.g4 + i;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[i]), orsrc,
-                                                  (int)(((size_t)row * orow + (size_t)S.h * D + S.col) * 4), 0, 0);
-        }
-    }
-
-    // M <- e^{gamma_L} M + K~^T U on this wave's rows
-#pragma unroll
-    for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) M[b] = mfma_f32(bfe(cur.kt[2 * b + (e >> 3)], e & 7), U[e >> 2][e & 3], M[b]);
-}
+__device__ __forceinline__ f4v lds4(const float *p) { return *reinterpret_cast<const f4v *>(p); }
+__device__ __forceinline__ void lds4w(float *p, f4v v) { *reinterpret_cast<f4v *>(p) = v; }
 
 __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 {
-    // per buffer and wave: partial [W; Q'] M0, 8 row blocks; two buffers, so
-    // one barrier a chunk orders both the writes and the previous reads
-    extern __shared__ __align__(16) unsigned char lds[];
-    f4v (*red)[4][8][64] = reinterpret_cast<f4v (*)[4][8][64]>(lds);
-    int *order = reinterpret_cast<int *>(lds + 2 * 4 * 8 * 64 * 16);   // prompt of each length rank
+    __shared__ __align__(16) float Ms[kSweepMs];
+    __shared__ __align__(16) float Us[kSweepUs];
+    __shared__ int order[256];      // prompt of each length rank
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: operand bases stay scalar
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -760,38 +693,120 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     if (nck == 0) return;
     const int col = 16 * tile + l16;
 
-    // state rows [32 wave, 32 wave + 32), column col; block b register i is
-    // row 32 wave + 16 b + 4 g4 + i (the 16x16 accumulator layout)
+    // this wave updates state rows [32 wave, 32 wave + 32): block b register i
+    // is row 32 wave + 16 b + 4 g4 + i (the 16x16 accumulator layout); every
+    // wave reads all 128 rows from Ms
     float *st = X.P.state + ((size_t)pidx * hv + h) * D * D + col;
     f4v M[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) M[b][i] = st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D];
+        lds4w(Ms + g4 * kMsG + l16 * kMsN + 4 * (2 * wave + b), M[b]);
+    }
 
     const size_t cstride = (size_t)hv * kBlockElems;
     const uint16_t *bp = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
     const uint16_t *pWQ = bp + kOffWQ + ((size_t)wave * 8 * 64 + lane) * 8;
     const uint16_t *pKT = bp + kOffKT + ((size_t)wave * 4 * 64 + lane) * 8;
-    const uint16_t *pUA = bp + kOffUA + ((size_t)tile * 2 * 64 + lane) * 8;
-    const uint16_t *pUB = bp + kOffUB + ((size_t)tile * 2 * 64 + lane) * 8;
-    const uint16_t *pPA = bp + kOffPA + ((size_t)wave * 2 * 64 + lane) * 8;
+    const uint16_t *pUA = bp + kOffUA + ((size_t)(tile * 4 + wave) * 64 + lane) * 4;
     const float *pel = X.el + (size_t)cid0 * hv + h;
+    const size_t orow = (size_t)hv * D;   // floats a packed output row
+    // this lane's output elements: rows 16 wave + 4 g4 + i of the chunk (the
+    // per-chunk kernel left P U~ there), column col of head h
+    auto out_rsrc = [&](int c) {
+        const int r0 = s0 + c * kChunk;
+        const int L = min(kChunk, s1 - r0);
+        return __builtin_amdgcn_make_buffer_rsrc(X.P.out + (size_t)r0 * orow, 0,
+                                                 (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
+    };
+    int ooff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ooff[i] = (int)(((size_t)(16 * wave + 4 * g4 + i) * orow + (size_t)h * D + col) * 4);
 
-    // Two operand sets: chunk c computes from one while the other receives
-    // chunk c + 1 (the last chunk requests its own again).  The loop runs two
-    // chunks an iteration with the sets swapped, so no register copy, and no
-    // wait for a load just issued, sits at the loop's back edge.  Output rows
-    // past a chunk's end are dropped by the buffer range check, not a branch.
-    Operands A, B;
-    A.load(pWQ, pKT, pUA, pUB, pPA, pel, 0, 0);
-    const SweepCtx S{X, wave, lane, l16, g4, h, col, s0, s1, nck, cstride, pel, pWQ, pKT, pUA, pUB, pPA, red};
-    int c = 0;
-    for (; c + 1 < nck; c += 2) {
-        sweep_chunk(S, c, A, B, M);
-        sweep_chunk(S, c + 1, B, A, M);
+    uint4 wq[8], kt[4];
+    uint2 ua;
+    float eL;
+    f4v oin;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) wq[kb] = ld16(pWQ + kb * 512);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + j * 512);
+    ua = *reinterpret_cast<const uint2 *>(pUA);
+    eL = pel[0];
+    {
+        const __amdgpu_buffer_rsrc_t r = out_rsrc(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oin[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ooff[i], 0, 0));
     }
-    if (c < nck) sweep_chunk(S, c, A, B, M);
+    lds_barrier();   // Ms complete
+
+    // The loop is branch-free, so the compiler's memory-counter waits track
+    // each operand exactly: each operand of chunk c + 1 is requested right
+    // after its last use in chunk c (the last chunk requests its own again),
+    // and output rows past a chunk's end are dropped by the buffer range check.
+    for (int c = 0; c < nck; ++c) {
+        const int cn = min(c + 1, nck - 1);
+        const size_t nx = (size_t)cn * cstride;
+        const size_t nel = (size_t)cn * hv;
+
+        // rows [16 wave, 16 wave + 16) of W M0 and Q' M0, over all 128 state
+        // rows; O starts from the chunk's P U~
+        f4v aU = {0.f, 0.f, 0.f, 0.f}, aO = oin;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const f4v mv = lds4(Ms + g4 * kMsG + l16 * kMsN + 4 * kb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                aU = mfma_f32(bfe(wq[kb], i), mv[i], aU);
+                aO = mfma_f32(bfe(wq[kb], 4 + i), mv[i], aO);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) wq[kb] = ld16(pWQ + nx + kb * 512);
+
+        // U = U~ - W M0 for rows 16 wave + 4 g4 + i, shared through Us;
+        // O = P U~ + Q' M0 for the same rows
+        f4v U;
+        U[0] = __uint_as_float(ua.x << 16) - aU[0];
+        U[1] = __uint_as_float(ua.x & 0xffff0000u) - aU[1];
+        U[2] = __uint_as_float(ua.y << 16) - aU[2];
+        U[3] = __uint_as_float(ua.y & 0xffff0000u) - aU[3];
+        lds4w(Us + g4 * kUsG + l16 * kUsN + 4 * wave, U);
+        {
+            const __amdgpu_buffer_rsrc_t r = out_rsrc(c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(aO[i]), r, ooff[i], 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        ua = *reinterpret_cast<const uint2 *>(pUA + nx);
+        {
+            const __amdgpu_buffer_rsrc_t r = out_rsrc(cn);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oin[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ooff[i], 0, 0));
+        }
+        lds_barrier();   // Us complete; every wave is done reading Ms
+
+        // M <- e^{gamma_L} M + K~^T U on this wave's rows, then into Ms
+#pragma unroll
+        for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f4v uv = lds4(Us + g4 * kUsG + l16 * kUsN + 4 * m);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) M[b] = mfma_f32(bfe(kt[2 * b + (m >> 1)], 4 * (m & 1) + i), uv[i], M[b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + nx + j * 512);
+        eL = pel[nel];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) lds4w(Ms + g4 * kMsG + l16 * kMsN + 4 * (2 * wave + b), M[b]);
+        lds_barrier();   // Ms complete; every wave is done reading Us
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -850,16 +865,14 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     static const hipError_t e_lds = hipFuncSetAttribute(reinterpret_cast<const void *>(intra_kernel),
                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kIntraLds);
     if (e_lds != hipSuccess) return e_lds;
-    static const hipError_t e_lds2 = hipFuncSetAttribute(reinterpret_cast<const void *>(sweep_kernel),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kSweepLds);
-    if (e_lds2 != hipSuccess) return e_lds2;
+
 
     const unsigned units = (unsigned)(P.C / 8);
     hipLaunchKernelGGL(prologue_kernel, dim3((P.total_rows + PRO_ROWS - 1) / PRO_ROWS, (units + 255) / 256),
                        dim3(256), 0, stream, X);
     hipLaunchKernelGGL(intra_kernel, dim3((unsigned)X.nc_total, P.hv), dim3(256), kIntraLds, stream, X);
     const unsigned groups = (unsigned)P.n_seqs * P.hv;
-    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), kSweepLds, stream, X);
+    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), 0, stream, X);
     return hipGetLastError();
 }
 
