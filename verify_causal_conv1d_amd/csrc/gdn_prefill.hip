@@ -24,11 +24,13 @@
 //             alpha and beta as fp32.
 //   intra     per (chunk, value head), independent: K K^T and Q K^T on bf16
 //             MFMA, T by 16 x 16 blocks (fp32 forward substitution on the
-//             diagonal, fp32 MFMA off it), then W^T, U~ and (P W)^T on bf16
-//             MFMA.  Products are formed transposed where
-//             that puts each lane's accumulator values exactly where the
-//             sweep's lanes read them, so most operands leave straight from
-//             registers; everything is stored in the sweep's lane order.
+//             diagonal, fp32 MFMA off it), then W^T, W, U~, (P W)^T and P U~
+//             on bf16 MFMA.  k^ and v are transposed by an exact MFMA with a
+//             0/1 selection operand, and every later product takes a k order
+//             in which one product's accumulator registers are the next one's
+//             operand, so nothing is transposed through LDS; products are
+//             formed transposed where that puts each lane's values where the
+//             sweep's lanes read them, and everything leaves in that order.
 //   sweep     per (prompt, value head, 16 state columns), 4 waves, wave w
 //             holding state rows [32w, 32w + 32) as fp32 MFMA accumulators
 //             (v_mfma_f32_16x16x4_f32).  Per chunk: partial [W; Q'] M0 over
@@ -306,17 +308,46 @@ __device__ __forceinline__ f4v neg_diag_times(const float *An, int i, f4v s, int
 
 constexpr int SB = 72;   // bf16 row stride of the [.][64] LDS arrays (144 B: rows 4 banks apart)
 
-// LDS of an intra workgroup (bytes)
-constexpr int kIntraAn = 0;                       // fp32 [64][64] -A; later WT bf16 [128][SB]
-constexpr int kIntraPb = 128 * SB * 2;            // bf16 [64][SB]  P
-constexpr int kIntraTb = kIntraPb + 64 * SB * 2;  // bf16 [64][SB]  T
-constexpr int kIntraKb = kIntraTb + 64 * SB * 2;  // bf16 [128][SB] (beta e^gamma k^)^T
-constexpr int kIntraVb = kIntraKb + 128 * SB * 2; // bf16 [128][SB] (beta v)^T; later U~^T
-constexpr int kIntraVec = kIntraVb + 128 * SB * 2;
+// LDS of an intra workgroup (bytes): 44 KiB, three workgroups a CU
+constexpr int kIntraAn = 0;                        // fp32 [64][64]: -A, and T blocks later stages read
+constexpr int kIntraPb = 64 * 64 * 4;              // bf16 [64][SB]  P
+constexpr int kIntraT1 = kIntraPb + 64 * SB * 2;   // bf16 [64][SB]  T' = T diag(beta e^gamma)
+constexpr int kIntraT2 = kIntraT1 + 64 * SB * 2;   // bf16 [64][SB]  T'' = T diag(beta)
+constexpr int kIntraVec = kIntraT2 + 64 * SB * 2;  // fp32 [4][64]   gamma, beta, e^gamma, e^{gamma_L - gamma}
 constexpr int kIntraLds = kIntraVec + 4 * 64 * 4;
-static_assert(64 * 64 * 4 <= kIntraPb, "An fits its region");
 
-__global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
+// Operands with a permuted k order.  A bf16 MFMA k-step ks reads, in lane
+// group g4, the 8 contraction indices s = 32 ks + 4 g4 + {0..3} and
+// s = 32 ks + 16 + 4 g4 + {0..3}: exactly the rows that the accumulator
+// registers of the 16x16 blocks 2 ks and 2 ks + 1 hold in that lane group.
+// A and B of one product use the same order, so an accumulator block pair
+// feeds the next product straight from registers.
+__device__ __forceinline__ uint4 pack_perm(f4v lo, f4v hi)
+{
+    return make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+}
+// the same 8 indices of a bf16 LDS row
+__device__ __forceinline__ uint4 lds_perm(const uint16_t *row, int ks, int g4)
+{
+    const uint2 lo = *reinterpret_cast<const uint2 *>(row + 32 * ks + 4 * g4);
+    const uint2 hi = *reinterpret_cast<const uint2 *>(row + 32 * ks + 16 + 4 * g4);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+// B operand of X[16 rows][32 cols] times this = X[., 16 hb .. 16 hb + 16): a
+// bf16 0/1 selection.  The product, exact, leaves register i of lane
+// (l16, g4) holding X[4 g4 + i][16 hb + l16]: a transpose of the loaded rows.
+__device__ __forceinline__ uint4 select_cols(int hb, int l16, int g4)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int k0 = 8 * g4 + 2 * p;
+        w[p] = ((k0 == 16 * hb + l16) ? 0x3F80u : 0u) | ((k0 + 1 == 16 * hb + l16) ? 0x3F800000u : 0u);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -332,12 +363,9 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
     uint16_t *blk = X.blk + cidh * kBlockElems;
 
     float *An = reinterpret_cast<float *>(lds + kIntraAn);
-    uint16_t *WT = reinterpret_cast<uint16_t *>(lds + kIntraAn);
     uint16_t *Pb = reinterpret_cast<uint16_t *>(lds + kIntraPb);
-    uint16_t *Tb = reinterpret_cast<uint16_t *>(lds + kIntraTb);
-    uint16_t *KbT = reinterpret_cast<uint16_t *>(lds + kIntraKb);
-    uint16_t *VbT = reinterpret_cast<uint16_t *>(lds + kIntraVb);
-    uint16_t *UT = VbT;
+    uint16_t *T1 = reinterpret_cast<uint16_t *>(lds + kIntraT1);
+    uint16_t *T2 = reinterpret_cast<uint16_t *>(lds + kIntraT2);
     float *gam = reinterpret_cast<float *>(lds + kIntraVec);
     float *bet = gam + 64, *eg = bet + 64, *ekt = eg + 64;
 
@@ -347,6 +375,29 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
     const uint16_t *Vg = X.v + ((size_t)r0 * hv + h) * D;
     const size_t vrow = (size_t)hv * D;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
+
+    // ---- every global operand is requested at once, so the workgroup pays
+    // one memory latency for them:
+    //  ka, qa, kb: K K^T and Q K^T, wave w computing the 32 x 32 block (w >> 1, w & 1)
+    //  kr, vr: rows 16 mt + l16, columns [32w, 32w + 32) of k^ and v (transposed below)
+    uint4 ka[D / 16], qa[D / 16], kb[D / 16], kr[4], vr[4];
+    {
+        const int bi = wave >> 1, bj = wave & 1;
+        const int ra = 32 * bi + l32, rb = 32 * bj + l32;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const int ko = 16 * ks + 8 * hh;
+            ka[ks] = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;
+            qa[ks] = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;
+            kb[ks] = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int t = 16 * mt + l16;
+            kr[mt] = t < L ? ld16(Kg + t * qkrow + 32 * wave + 8 * g4) : z4;
+            vr[mt] = t < L ? ld16(Vg + t * vrow + 32 * wave + 8 * g4) : z4;
+        }
+    }
 
     // ---- gamma (inclusive in-chunk scan of log alpha), beta and the decays
     if (wave == 0) {
@@ -366,36 +417,25 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
         if (lane == 0) X.el[cidh] = __expf(gL);
     }
 
-    // every global operand of the first phases is requested at once, so the
-    // workgroup pays one memory latency for them
-    constexpr int NB = 8;
-    uint4 ka[D / 16], qa[D / 16], kb[D / 16], raw[NB];
-    {
-        const int bi = wave >> 1, bj = wave & 1;
-        const int ra = 32 * bi + l32, rb = 32 * bj + l32;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const int ko = 16 * ks + 8 * hh;
-            ka[ks] = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;
-            qa[ks] = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;
-            kb[ks] = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;
-        }
-        // rows for (beta e^gamma k^)^T and (beta v)^T: lanes take consecutive
-        // rows s, so the transposed LDS writes below are contiguous
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const int idx = k * 256 + tid;          // 0..2047: 16 column groups x 64 rows, K then V
-            const int which = idx >> 10, s = idx & 63, q8 = ((idx >> 6) & 15) * 8;
-            raw[k] = s < L ? ld16(which ? Vg + s * vrow + q8 : Kg + s * qkrow + q8) : z4;
-        }
-    }
-
-    // ---- K K^T and Q K^T, wave w: the 32 x 32 block (w >> 1, w & 1)
+    // ---- K K^T and Q K^T; the transposed fragments of k^ and v, packed in
+    // the permuted k order: kp[hb][ks] element j holds
+    // k^[32 ks + 4 g4 + (j & 3) + 16 (j >> 2)][32 w + 16 hb + l16], vp likewise
     f16v S = {}, QK = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ka[ks]), as_bf8(kb[ks]), S, 0, 0, 0);
         QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qa[ks]), as_bf8(kb[ks]), QK, 0, 0, 0);
+    }
+    uint4 kp[2][2], vp[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const uint4 sel = select_cols(hb, l16, g4);
+        const f4v z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            kp[hb][ks] = pack_perm(mfma_bf16(kr[2 * ks], sel, z), mfma_bf16(kr[2 * ks + 1], sel, z));
+            vp[hb][ks] = pack_perm(mfma_bf16(vr[2 * ks], sel, z), mfma_bf16(vr[2 * ks + 1], sel, z));
+        }
     }
     lds_barrier();   // gamma, beta visible
 
@@ -413,50 +453,35 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             Pb[t * SB + s] = f2bf(dec * QK[i]);
         }
     }
-    // (beta e^gamma k^)^T and (beta v)^T
-    {
+    // K~ = e^{gamma_L - gamma} k^ in the sweep's lane order, from the fragments:
+    // KT[w][hb][mp][l][e] = K~[16 m + 4 g4 + i][32 w + 16 hb + l16], m = 2 mp + e / 4,
+    // which is element e of kp[hb][mp] scaled
 #pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const int idx = k * 256 + tid;
-            const int which = idx >> 10, s = idx & 63, q8 = ((idx >> 6) & 15) * 8;
-            const float sc = which ? bet[s] : bet[s] * eg[s];
-            uint16_t *dst = (which ? VbT : KbT) + q8 * SB + s;
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dst[e * SB] = f2bf(sc * bfe(raw[k], e));
-        }
-    }
-    // K~ = e^{gamma_L - gamma} k^ in the sweep's lane order (all loads first)
-    {
-        uint16_t kv[4][8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int u = r * 256 + tid;
-            const int l = u & 63, e_blk = u >> 6;    // (w, b, mp)
-            const int kr = 32 * (e_blk >> 2) + 16 * ((e_blk >> 1) & 1) + (l & 15);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 16 * (2 * (e_blk & 1) + (e >> 2)) + 4 * (l >> 4) + (e & 3);
-                kv[r][e] = t < L ? Kg[t * qkrow + kr] : (uint16_t)0;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int u = r * 256 + tid;
-            const int l = u & 63, e_blk = u >> 6;
+        for (int mp = 0; mp < 2; ++mp) {
             float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 16 * (2 * (e_blk & 1) + (e >> 2)) + 4 * (l >> 4) + (e & 3);
-                v[e] = ekt[t] * bf16f(kv[r][e]);
-            }
-            st16(blk + kOffKT + (size_t)u * 8,
+            for (int e = 0; e < 8; ++e) v[e] = ekt[32 * mp + 16 * (e >> 2) + 4 * g4 + (e & 3)] * bfe(kp[hb][mp], e);
+            st16(blk + kOffKT + ((size_t)((wave * 2 + hb) * 2 + mp) * 64 + lane) * 8,
                  make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
         }
+    // q^[16 mt + l16][16 (2w + hb) + 4 g4 .. + 3] for Q', requested now for the end
+    uint2 qv[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int t = 16 * mt + l16;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+            qv[hb][mt] = t < L ? *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * (2 * wave + hb) + 4 * g4)
+                               : make_uint2(0, 0);
     }
     lds_barrier();
 
-    // ---- T = (I + A)^-1.  Stage 1: wave w inverts diagonal block w (every
-    // lane group computes column l16; group g4 stores rows 4 g4 .. 4 g4 + 3)
+    // ---- T = (I + A)^-1 by 16 x 16 blocks, stored scaled by columns as
+    // T' = T diag(beta e^gamma) and T'' = T diag(beta) (bf16).  Stage 1: wave w
+    // inverts diagonal block w (every lane group computes column l16; group
+    // g4 stores rows 4 g4 .. 4 g4 + 3)
     {
         const int j = l16, w = wave;
         float Tc[16];
@@ -468,27 +493,41 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
             for (int s = 0; s < t; ++s) acc = fmaf(row[s], Tc[s], acc);
             Tc[t] = acc;
         }
+        const float b1 = bet[16 * w + j] * eg[16 * w + j], b2 = bet[16 * w + j];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float v = g4 == 0 ? Tc[i] : g4 == 1 ? Tc[4 + i] : g4 == 2 ? Tc[8 + i] : Tc[12 + i];
             const int t = 16 * w + 4 * g4 + i;
             An[t * 64 + 16 * w + j] = v;
-            Tb[t * SB + 16 * w + j] = f2bf(v);
-            for (int cb = w + 1; cb < 4; ++cb) Tb[t * SB + 16 * cb + j] = 0;
+            T1[t * SB + 16 * w + j] = f2bf(v * b1);
+            T2[t * SB + 16 * w + j] = f2bf(v * b2);
+            for (int cb = w + 1; cb < 4; ++cb) {
+                T1[t * SB + 16 * cb + j] = 0;
+                T2[t * SB + 16 * cb + j] = 0;
+            }
         }
     }
     lds_barrier();
+    // store a finished 16 x 16 block (i, j) of T, accumulator layout, scaled
+    auto put_t = [&](int i, int jb, const f4v &z) {
+        const float b1 = bet[16 * jb + l16] * eg[16 * jb + l16], b2 = bet[16 * jb + l16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * i + 4 * g4 + r;
+            T1[t * SB + 16 * jb + l16] = f2bf(z[r] * b1);
+            T2[t * SB + 16 * jb + l16] = f2bf(z[r] * b2);
+        }
+    };
     // Stage 2: T_{i,i-1} = -B_i A_{i,i-1} B_{i-1}, wave i (An holds -A)
     if (wave >= 1) {
         const int i = wave;
         f4v x = {0.f, 0.f, 0.f, 0.f};
         x = mm_blocks(An, i, i - 1, i - 1, i - 1, x, l16, g4);   // -A_{i,i-1} B_{i-1}
         const f4v z = -neg_diag_times(An, i, x, l16, g4);
+        put_t(i, i - 1, z);
+        if (i < 3) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * i + 4 * g4 + r;
-            Tb[t * SB + 16 * (i - 1) + l16] = f2bf(z[r]);
-            if (i < 3) An[(16 * (i - 1) + 4 * g4 + r) * 64 + 16 * i + l16] = z[r];   // T_10 -> (0,1), T_21 -> (1,2)
+            for (int r = 0; r < 4; ++r) An[(16 * (i - 1) + 4 * g4 + r) * 64 + 16 * i + l16] = z[r];   // T_10 -> (0,1), T_21 -> (1,2)
         }
     }
     lds_barrier();
@@ -499,11 +538,10 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
         x = mm_blocks(An, i, i - 2, i - 2, i - 2, x, l16, g4);
         x = mm_blocks(An, i, i - 1, i - 2, i - 1, x, l16, g4);   // T_{i-1,i-2} is kept in block (i-2, i-1)
         const f4v z = -neg_diag_times(An, i, x, l16, g4);
+        put_t(i, i - 2, z);
+        if (i == 2) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * i + 4 * g4 + r;
-            Tb[t * SB + 16 * (i - 2) + l16] = f2bf(z[r]);
-            if (i == 2) An[(4 * g4 + r) * 64 + 32 + l16] = z[r];   // T_20 -> (0,2)
+            for (int r = 0; r < 4; ++r) An[(4 * g4 + r) * 64 + 32 + l16] = z[r];   // T_20 -> (0,2)
         }
     }
     lds_barrier();
@@ -513,113 +551,80 @@ __global__ void __launch_bounds__(256) intra_kernel(const Ctx X)
         x = mm_blocks(An, 3, 0, 0, 0, x, l16, g4);
         x = mm_blocks(An, 3, 1, 0, 1, x, l16, g4);
         x = mm_blocks(An, 3, 2, 0, 2, x, l16, g4);
-        const f4v z = -neg_diag_times(An, 3, x, l16, g4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Tb[(48 + 4 * g4 + r) * SB + l16] = f2bf(z[r]);
+        put_t(3, 0, -neg_diag_times(An, 3, x, l16, g4));
     }
     lds_barrier();
 
-    // q^ values the Q' epilogue needs, requested now so the products below
-    // hide their latency: lane holds q^[16mt + l16][16kb + 4g4 .. + 3]
-    uint2 qv[2][4];
+    // ---- the products, wave w on key column blocks kb = 2w + hb and value
+    // tiles 2w + hb (hb = 0, 1), with the permuted k order throughout:
+    //  W^T = k^T T'^T  (kb, mt) -> the W half of the sweep's WQ
+    //  W   = T' k^     (mt, kb) -> kept: its register pairs are the A operand of (P W)^T
+    //  U~  = T'' v     (mt, tile) -> the sweep's UA, and kept for P U~
+    uint4 wp[2][2], up[2][2];   // W and U~ block pairs, packed in the permuted k order
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+    for (int hb = 0; hb < 2; ++hb) {
+        const int kbk = 2 * wave + hb;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int t = 16 * mt + l16;
-            qv[bb][mt] = t < L ? *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * (2 * wave + bb) + 4 * g4)
-                               : make_uint2(0, 0);
-        }
-
-    // ---- W^T = (beta e^gamma k^)^T T^T and U~ = T (beta v); wave w takes
-    // key column blocks kb = 2w, 2w + 1 of W^T and value tiles 2w, 2w + 1 of U~
-    f4v Ud[2][4];
-    {
+        for (int kq = 0; kq < 2; ++kq) {
+            f4v wpair[2], upair[2];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int kb = 2 * wave + bb;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f4v wacc = {}, uacc = {};
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int mt = 2 * kq + h2;
+                f4v wt = {0.f, 0.f, 0.f, 0.f}, w = wt, u = wt;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const int so = 32 * ks + 8 * g4;
-                    const uint4 tr = ld16(Tb + (16 * mt + l16) * SB + so);
-                    wacc = mfma_bf16(ld16(KbT + (16 * kb + l16) * SB + so), tr, wacc);
-                    uacc = mfma_bf16(tr, ld16(VbT + (16 * kb + l16) * SB + so), uacc);
+                    const uint4 t1 = lds_perm(T1 + (16 * mt + l16) * SB, ks, g4);
+                    const uint4 t2 = lds_perm(T2 + (16 * mt + l16) * SB, ks, g4);
+                    wt = mfma_bf16(kp[hb][ks], t1, wt);
+                    w = mfma_bf16(t1, kp[hb][ks], w);
+                    u = mfma_bf16(t2, vp[hb][ks], u);
                 }
-                Ud[bb][mt] = uacc;
-                // lane holds W[t = 16mt + l16][16kb + 4g4 + i]: WT rows and half of a WQ slot
-#pragma unroll
-                for (int i = 0; i < 4; ++i) WT[(16 * kb + 4 * g4 + i) * SB + 16 * mt + l16] = f2bf(wacc[i]);
-                uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kb) * 64 + lane) * 8);
-                *wq = make_uint2(pack2(wacc[0], wacc[1]), pack2(wacc[2], wacc[3]));
-                // lane holds U~[16mt + 4g4 + i][16 tile + l16], tile = kb: the accumulator layout
-                uint2 *ua = reinterpret_cast<uint2 *>(blk + kOffUA + ((size_t)(kb * 4 + mt) * 64 + lane) * 4);
-                *ua = make_uint2(pack2(uacc[0], uacc[1]), pack2(uacc[2], uacc[3]));
+                wpair[h2] = w;
+                upair[h2] = u;
+                // wt: lane holds W[16 mt + l16][16 kbk + 4 g4 + i]; u: U~[16 mt + 4 g4 + i][16 kbk + l16]
+                *reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kbk) * 64 + lane) * 8) =
+                    make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
+                *reinterpret_cast<uint2 *>(blk + kOffUA + ((size_t)(kbk * 4 + mt) * 64 + lane) * 4) =
+                    make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
             }
+            wp[hb][kq] = pack_perm(wpair[0], wpair[1]);
+            up[hb][kq] = pack_perm(upair[0], upair[1]);
         }
     }
-    lds_barrier();   // every read of (beta v)^T done
+    //  Q'^T = (e^gamma q^)^T - W^T P^T  (kb, mt) -> the Q' half of WQ
+    //  P U~                             (mt, tile) -> the chunk's output rows (fp32);
+    //  rows past the chunk's end are dropped by the buffer range check
+    const size_t orow = (size_t)hv * D;
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        X.P.out + (size_t)r0 * orow, 0, (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        const int tile = 2 * wave + bb;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            uint2 *dst = reinterpret_cast<uint2 *>(UT + (16 * tile + l16) * SB + 16 * mt + 4 * g4);
-            *dst = make_uint2(pack2(Ud[bb][mt][0], Ud[bb][mt][1]), pack2(Ud[bb][mt][2], Ud[bb][mt][3]));
-        }
-    }
-    lds_barrier();
-
-    // ---- Q'^T = (e^gamma q^)^T - W^T P^T, the lower half of WQ
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        const int kb = 2 * wave + bb;
+    for (int hb = 0; hb < 2; ++hb) {
+        const int kbk = 2 * wave + hb;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            f4v acc = {};
+            f4v pw = {0.f, 0.f, 0.f, 0.f}, pu = pw;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int so = 32 * ks + 8 * g4;
-                acc = mfma_bf16(ld16(WT + (16 * kb + l16) * SB + so), ld16(Pb + (16 * mt + l16) * SB + so), acc);
+                const uint4 pr = lds_perm(Pb + (16 * mt + l16) * SB, ks, g4);
+                pw = mfma_bf16(wp[hb][ks], pr, pw);
+                pu = mfma_bf16(pr, up[hb][ks], pu);
             }
-            // lane holds (P W)[t = 16mt + l16][16kb + 4g4 + i]
+            // pw: lane holds (P W)[t = 16 mt + l16][16 kbk + 4 g4 + i]
             const int t = 16 * mt + l16;
-            const uint2 qq = qv[bb][mt];
+            const uint2 qq = qv[hb][mt];
             const float q[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xffff0000u),
                                 __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xffff0000u)};
             const float e = eg[t];
-            uint2 *wq = reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kb) * 64 + lane) * 8 + 4);
-            *wq = make_uint2(pack2(fmaf(e, q[0], -acc[0]), fmaf(e, q[1], -acc[1])),
-                             pack2(fmaf(e, q[2], -acc[2]), fmaf(e, q[3], -acc[3])));
-        }
-    }
-    // P U~ (bf16 MFMA, fp32 out) into the chunk's output rows: wave w takes
-    // value tiles 2w, 2w + 1; rows past the chunk's end are dropped by the
-    // buffer range check
-    {
-        const size_t orow = (size_t)hv * D;
-        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-            X.P.out + (size_t)r0 * orow, 0, (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
+            *reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kbk) * 64 + lane) * 8 + 4) =
+                make_uint2(pack2(fmaf(e, q[0], -pw[0]), fmaf(e, q[1], -pw[1])),
+                           pack2(fmaf(e, q[2], -pw[2]), fmaf(e, q[3], -pw[3])));
+            // pu: lane holds (P U~)[16 mt + 4 g4 + i][16 kbk + l16]
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int tile = 2 * wave + bb;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int so = 32 * ks + 8 * g4;
-                    acc = mfma_bf16(ld16(Pb + (16 * mt + l16) * SB + so), ld16(UT + (16 * tile + l16) * SB + so), acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * mt + 4 * g4 + i;
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __float_as_uint(acc[i]), orsrc, (int)(((size_t)row * orow + (size_t)h * D + 16 * tile + l16) * 4),
-                        0, 0);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g4 + i;
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(pu[i]), orsrc, (int)(((size_t)row * orow + (size_t)h * D + 16 * kbk + l16) * 4), 0,
+                    0);
             }
         }
     }
