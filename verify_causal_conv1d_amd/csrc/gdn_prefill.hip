@@ -16,11 +16,11 @@
 // one fused contraction [W; Q'] M0 and the update.
 //
 // Three launches on the caller's stream:
-//   prologue  a thread owns 8 channels and walks 32 packed rows with the
-//             last three raw rows in registers: causal conv (taps from the
-//             prompt's own earlier rows or its tail) + SiLU, then per row the
-//             q/k L2 norms over the 16 lanes of a head; gates per (row, value
-//             head).  q^, k^, v are stored as bf16 (matrix-core operands), log
+//   prologue  a thread owns 8 channels and walks 32 rows of one prompt
+//             with the last three raw rows in registers: causal conv (taps
+//             from the prompt's own earlier rows or its tail) + SiLU, then per
+//             row the q/k L2 norms over the 16 lanes of a head; gates per
+//             (row, value head).  q^, k^, v are stored as bf16 (matrix-core operands), log
 //             alpha and beta as fp32.
 //   intra     per (chunk, value head), independent: K K^T and Q K^T on bf16
 //             MFMA, T by 16 x 16 blocks (fp32 forward substitution on the
@@ -156,35 +156,45 @@ __device__ __forceinline__ f4v mfma_bf16(uint4 a, uint4 b, f4v c)
 }
 
 // ---------------------------------------------------------------- prologue
+// Block bid of PRO_ROWS rows, numbered prompt after prompt (a block never
+// crosses a prompt start): its prompt p and rows [r0, r1).  False past the
+// last block, or where the layout breaks the rules (as chunk_at).
+__device__ bool pro_block_at(const Ctx &X, int bid, int &p, int &s0, int &r0, int &r1)
+{
+    const int T = X.P.total_rows;
+    int base = 0;
+    int prev = X.P.seq_start[0];
+    if (prev < 0) return false;
+    for (int q = 0; q < X.P.n_seqs; ++q) {
+        const int a = X.P.seq_start[q], b = X.P.seq_start[q + 1];
+        if (a != prev || b < a || b > T || b - a > X.P.max_len) return false;
+        prev = b;
+        const int nq = (b - a + PRO_ROWS - 1) / PRO_ROWS;
+        if (bid < base + nq) {
+            p = q;
+            s0 = a;
+            r0 = a + (bid - base) * PRO_ROWS;
+            r1 = min(b, r0 + PRO_ROWS);
+            return true;
+        }
+        base += nq;
+    }
+    return false;
+}
+
 __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
 {
-    __shared__ int rstart[PRO_ROWS];   // prompt start of each row, -1 outside every valid prompt
-    __shared__ int rprompt[PRO_ROWS];
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * PRO_ROWS;
-    const int T = X.P.total_rows, C = X.P.C, hv = X.P.hv, hk = X.P.hk;
-    const int nrows = min(PRO_ROWS, T - t0);
-
-    if (tid < nrows) {
-        const int t = t0 + tid;
-        int lo = 0, hi = X.P.n_seqs - 1;   // the last p with seq_start[p] <= t
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (X.P.seq_start[mid] <= t) lo = mid; else hi = mid - 1;
-        }
-        const int s0 = X.P.seq_start[lo], s1 = X.P.seq_start[lo + 1];
-        const bool ok = s0 >= 0 && s0 <= t && t < s1 && s1 <= T && s1 - s0 <= X.P.max_len;
-        rstart[tid] = ok ? s0 : -1;
-        rprompt[tid] = lo;
-    }
-    lds_barrier();
+    const int C = X.P.C, hv = X.P.hv, hk = X.P.hk;
+    int pidx, s0, r0, r1;
+    if (!pro_block_at(X, blockIdx.x, pidx, s0, r0, r1)) return;
+    const int nrows = r1 - r0;
 
     // gates of every (row, value head): log alpha and beta
     if (blockIdx.y == 0) {
         for (int idx = tid; idx < nrows * hv; idx += 256) {
             const int i = idx / hv, h = idx - i * hv;
-            if (rstart[i] < 0) continue;
-            const size_t o = (size_t)(t0 + i) * hv + h;
+            const size_t o = (size_t)(r0 + i) * hv + h;
             X.g[o] = log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]);
             X.be[o] = sigmoid_f(bf16f(X.P.b[o]));
         }
@@ -209,39 +219,27 @@ __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
         w[e][0] = wv.x; w[e][1] = wv.y; w[e][2] = wv.z; w[e][3] = wv.w;
     }
 
+    // the window before row r0: x_{r0-d} is row r0 - d of the prompt, or row
+    // 3 + r0 - d - s0 of its tail (unconditional loads from computed sources)
     const uint16_t *col = X.P.qkv + c0;
-    uint4 x1 = make_uint4(0, 0, 0, 0), x2 = x1, x3 = x1;   // x_{t-1}, x_{t-2}, x_{t-3}
-    int cur = -2;                                          // prompt start the window belongs to
+    const uint16_t *tl = X.P.conv_tail + (size_t)pidx * 3 * C + c0;
+    uint4 x1, x2, x3;   // x_{t-1}, x_{t-2}, x_{t-3}
+    {
+        const int u1 = r0 - 1, u2 = r0 - 2, u3 = r0 - 3;
+        x1 = ld16(u1 >= s0 ? col + (size_t)u1 * C : tl + (size_t)(3 + u1 - s0) * C);
+        x2 = ld16(u2 >= s0 ? col + (size_t)u2 * C : tl + (size_t)(3 + u2 - s0) * C);
+        x3 = ld16(u3 >= s0 ? col + (size_t)u3 * C : tl + (size_t)(3 + u3 - s0) * C);
+    }
     constexpr int B = 8;
     for (int i0 = 0; i0 < nrows; i0 += B) {
+        // a batch of rows, all requested before any is used (rows past the
+        // block's end re-read its last row and are not stored)
         uint4 xb[B];
 #pragma unroll
-        for (int k = 0; k < B; ++k)
-            if (i0 + k < nrows && rstart[i0 + k] >= 0) xb[k] = ld16(col + (size_t)(t0 + i0 + k) * C);
+        for (int k = 0; k < B; ++k) xb[k] = ld16(col + (size_t)min(r0 + i0 + k, r1 - 1) * C);
 #pragma unroll
         for (int k = 0; k < B; ++k) {
-            const int i = i0 + k;
-            if (i >= nrows) break;
-            const int s0 = rstart[i];
-            const int t = t0 + i;
-            if (s0 < 0) {
-                cur = -2;
-                continue;
-            }
-            if (s0 != cur || i == 0) {
-                // (re)build the window of row t: earlier rows of its prompt, else its tail
-                const uint16_t *tl = X.P.conv_tail + (size_t)rprompt[i] * 3 * C + c0;
-                uint4 xs[3];
-#pragma unroll
-                for (int d = 1; d <= 3; ++d) {
-                    const int src = t - d;
-                    xs[d - 1] = src >= s0 ? ld16(col + (size_t)src * C) : ld16(tl + (size_t)(3 + src - s0) * C);
-                }
-                x1 = xs[0];
-                x2 = xs[1];
-                x3 = xs[2];
-                cur = s0;
-            }
+            const int t = r0 + i0 + k;
             const uint4 xt = xb[k];
             float a[8];
             float ss = 0.0f;
@@ -254,21 +252,19 @@ __global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
                 a[e] = silu_f(y);
                 ss = fmaf(a[e], a[e], ss);
             }
-            float sc = 1.0f;
-            if (kind < 2) {
-                // sum over the 16 lanes of this head (all of them take this branch)
-                ss += __shfl_xor(ss, 1);
-                ss += __shfl_xor(ss, 2);
-                ss += __shfl_xor(ss, 4);
-                ss += __shfl_xor(ss, 8);
-                sc = (1.0f / sqrtf(ss + 1e-6f)) * qscale;
-            }
+            // sum over the 16 lanes of this head (v lanes compute it too and
+            // ignore it, so the shuffles stay outside any branch)
+            ss += __shfl_xor(ss, 1);
+            ss += __shfl_xor(ss, 2);
+            ss += __shfl_xor(ss, 4);
+            ss += __shfl_xor(ss, 8);
+            const float sc = kind < 2 ? (1.0f / sqrtf(ss + 1e-6f)) * qscale : 1.0f;
             uint4 o;
             o.x = pack2(a[0] * sc, a[1] * sc);
             o.y = pack2(a[2] * sc, a[3] * sc);
             o.z = pack2(a[4] * sc, a[5] * sc);
             o.w = pack2(a[6] * sc, a[7] * sc);
-            st16(dst + (size_t)t * dst_row, o);
+            if (t < r1) st16(dst + (size_t)t * dst_row, o);
             x3 = x2;
             x2 = x1;
             x1 = xt;
@@ -873,7 +869,8 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
 
 
     const unsigned units = (unsigned)(P.C / 8);
-    hipLaunchKernelGGL(prologue_kernel, dim3((P.total_rows + PRO_ROWS - 1) / PRO_ROWS, (units + 255) / 256),
+    // 32-row blocks that never cross a prompt start: at most T/32 + n of them
+    hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(P.total_rows / PRO_ROWS + P.n_seqs), (units + 255) / 256),
                        dim3(256), 0, stream, X);
     hipLaunchKernelGGL(intra_kernel, dim3((unsigned)X.nc_total, P.hv), dim3(256), kIntraLds, stream, X);
     const unsigned groups = (unsigned)P.n_seqs * P.hv;
