@@ -376,23 +376,24 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
     // one memory latency for them:
     //  ka, qa, kb: K K^T and Q K^T, wave w computing the 32 x 32 block (w >> 1, w & 1)
     //  kr, vr: rows 16 mt + l16, columns [32w, 32w + 32) of k^ and v (transposed below)
-    uint4 ka[D / 16], qa[D / 16], kb[D / 16], kr[4], vr[4];
-    {
-        const int bi = wave >> 1, bj = wave & 1;
-        const int ra = 32 * bi + l32, rb = 32 * bj + l32;
+    // (in two halves of the contraction, so that half the K K^T / Q K^T
+    // operands are in flight at once)
+    const int ra = 32 * (wave >> 1) + l32, rb = 32 * (wave & 1) + l32;
+    uint4 ka[D / 32], qa[D / 32], kb[D / 32], kr[4], vr[4];
+#define GDN_LOAD_HALF(half)                                                \
+    _Pragma("unroll") for (int k2 = 0; k2 < D / 32; ++k2)                  \
+    {                                                                      \
+        const int ko = 16 * ((half) * (D / 32) + k2) + 8 * hh;             \
+        ka[k2] = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;                 \
+        qa[k2] = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;                 \
+        kb[k2] = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;                 \
+    }
+    GDN_LOAD_HALF(0)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const int ko = 16 * ks + 8 * hh;
-            ka[ks] = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;
-            qa[ks] = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;
-            kb[ks] = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int t = 16 * mt + l16;
-            kr[mt] = t < L ? ld16(Kg + t * qkrow + 32 * wave + 8 * g4) : z4;
-            vr[mt] = t < L ? ld16(Vg + t * vrow + 32 * wave + 8 * g4) : z4;
-        }
+    for (int mt = 0; mt < 4; ++mt) {
+        const int t = 16 * mt + l16;
+        kr[mt] = t < L ? ld16(Kg + t * qkrow + 32 * wave + 8 * g4) : z4;
+        vr[mt] = t < L ? ld16(Vg + t * vrow + 32 * wave + 8 * g4) : z4;
     }
 
     // ---- gamma (inclusive in-chunk scan of log alpha), beta and the decays
@@ -418,10 +419,18 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
     // k^[32 ks + 4 g4 + (j & 3) + 16 (j >> 2)][32 w + 16 hb + l16], vp likewise
     f16v S = {}, QK = {};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ka[ks]), as_bf8(kb[ks]), S, 0, 0, 0);
-        QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qa[ks]), as_bf8(kb[ks]), QK, 0, 0, 0);
+    for (int half = 0; half < 2; ++half) {
+        if (half) {
+            __builtin_amdgcn_sched_barrier(0);
+            GDN_LOAD_HALF(1)
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < D / 32; ++k2) {
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ka[k2]), as_bf8(kb[k2]), S, 0, 0, 0);
+            QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qa[k2]), as_bf8(kb[k2]), QK, 0, 0, 0);
+        }
     }
+#undef GDN_LOAD_HALF
     uint4 kp[2][2], vp[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -488,6 +497,8 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
 #pragma unroll
             for (int s = 0; s < t; ++s) acc = fmaf(row[s], Tc[s], acc);
             Tc[t] = acc;
+            // one row's reads at a time: hoisting all 120 would hold them in registers
+            __builtin_amdgcn_sched_barrier(0);
         }
         const float b1 = bet[16 * w + j] * eg[16 * w + j], b2 = bet[16 * w + j];
 #pragma unroll
@@ -582,6 +593,8 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
                     make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
                 *reinterpret_cast<uint2 *>(blk + kOffUA + ((size_t)(kbk * 4 + mt) * 64 + lane) * 4) =
                     make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
+                // bound how far the scheduler hoists the next block's LDS reads
+                __builtin_amdgcn_sched_barrier(0);
             }
             wp[hb][kq] = pack_perm(wpair[0], wpair[1]);
             up[hb][kq] = pack_perm(upair[0], upair[1]);
@@ -622,6 +635,7 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
                     __float_as_uint(pu[i]), orsrc, (int)(((size_t)row * orow + (size_t)h * D + 16 * kbk + l16) * 4), 0,
                     0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
