@@ -44,6 +44,9 @@ struct CommitArgs {
     float *state;
 };
 
+// Rows a verify window may hold.
+constexpr int kMaxWindowRows = 16;
+
 // LDS one row-kernel workgroup may use (gfx950 has 160 KiB a CU).
 constexpr size_t kRowsMaxLds = 160 * 1024;
 

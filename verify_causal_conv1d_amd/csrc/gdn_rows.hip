@@ -83,7 +83,9 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     float *galpha = reinterpret_cast<float *>(raw + (3 + mr) * nch);  // [mr][vpw]
     float *gbeta = galpha + mr * A.vpw;                             // [mr][vpw]
     int *anc = reinterpret_cast<int *>(gbeta + mr * A.vpw);         // [mr][4]
-    int *bad = anc + mr * 4;
+    int *order = anc + mr * 4;                                      // [mr] processing order
+    int *sub = order + mr;                                          // [mr] subtree sizes, then next free slot
+    int *bad = sub + mr;
 
     // ---- this wave's tile of the state
     const int waves_per_head = A.dv / 64;
@@ -111,6 +113,38 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
         for (int d = 1; d <= 3; ++d) {
             i = (i >= 0) ? anc[i * 4] : i - 1;
             anc[tid * 4 + d] = i;
+        }
+    }
+    // Processing order.  A chain runs in row order.  A tree runs in depth-
+    // first preorder (children by increasing index): every row still follows
+    // its parent, and a row's parent is the row just done except after a
+    // leaf, so the parent state is re-read from its snapshot (leaves - 1)
+    // times instead of once for every row whose parent is not the row
+    // before it.  Each row's arithmetic is the same in any order.
+    if (tid == 0) {
+        if (A.mode == MODE_TREE) {
+            // subtree sizes (parents have smaller indices than children) ...
+            for (int i = 0; i < len; ++i) sub[i] = 1;
+            for (int i = len - 1; i > 0; --i)
+                if (anc[i * 4] >= 0) sub[anc[i * 4]] += sub[i];
+            // ... then preorder slots: a row takes its parent's next free slot
+            // and reserves its own subtree after it
+            int next_root = 0;
+            for (int i = 0; i < len; ++i) {
+                const int p = anc[i * 4];
+                int pos;
+                if (p < 0) {
+                    pos = next_root;
+                    next_root += sub[i];
+                } else {
+                    pos = sub[p];
+                    sub[p] += sub[i];
+                }
+                order[pos] = i;
+                sub[i] = pos + 1;   // from now on: this row's next free slot
+            }
+        } else {
+            for (int i = 0; i < len; ++i) order[i] = i;
         }
     }
 
@@ -256,7 +290,8 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
 
     // ---- the recurrence, row after row, on the tile held in registers
     int prev = -1;
-    for (int t = 0; t < len; ++t) {
+    for (int k = 0; k < len; ++k) {
+        const int t = order[k];
         const int p = anc[t * 4];
         if (p != prev) {
             // a tree row whose parent is not the row just done: reload the
@@ -368,7 +403,7 @@ size_t rows_lds_bytes(const RowsArgs &A)
            + sizeof(float) * 4 * nch                 // conv weights
            + sizeof(uint16_t) * (3 + mr) * nch       // raw rows
            + sizeof(float) * 2 * mr * A.vpw          // gates
-           + sizeof(int) * (4 * mr + 1);             // ancestors, flag
+           + sizeof(int) * (6 * mr + 1);             // ancestors, order, subtree sizes, flag
 }
 
 namespace {
