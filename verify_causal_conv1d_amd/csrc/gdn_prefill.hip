@@ -343,7 +343,7 @@ __device__ __forceinline__ uint4 select_cols(int hb, int l16, int g4)
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
+__global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -375,11 +375,11 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
     // ---- every global operand is requested at once, so the workgroup pays
     // one memory latency for them:
     //  ka, qa, kb: K K^T and Q K^T, wave w computing the 32 x 32 block (w >> 1, w & 1)
-    //  kr, vr: rows 16 mt + l16, columns [32w, 32w + 32) of k^ and v (transposed below)
+    //  kr: rows 16 mt + l16, columns [32w, 32w + 32) of k^ (transposed below)
     // (in two halves of the contraction, so that half the K K^T / Q K^T
     // operands are in flight at once)
     const int ra = 32 * (wave >> 1) + l32, rb = 32 * (wave & 1) + l32;
-    uint4 ka[D / 32], qa[D / 32], kb[D / 32], kr[4], vr[4];
+    uint4 ka[D / 32], qa[D / 32], kb[D / 32], kr[4];
 #define GDN_LOAD_HALF(half)                                                \
     _Pragma("unroll") for (int k2 = 0; k2 < D / 32; ++k2)                  \
     {                                                                      \
@@ -393,7 +393,6 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
     for (int mt = 0; mt < 4; ++mt) {
         const int t = 16 * mt + l16;
         kr[mt] = t < L ? ld16(Kg + t * qkrow + 32 * wave + 8 * g4) : z4;
-        vr[mt] = t < L ? ld16(Vg + t * vrow + 32 * wave + 8 * g4) : z4;
     }
 
     // ---- gamma (inclusive in-chunk scan of log alpha), beta and the decays
@@ -431,16 +430,14 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
         }
     }
 #undef GDN_LOAD_HALF
-    uint4 kp[2][2], vp[2][2];
+    uint4 kp[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const uint4 sel = select_cols(hb, l16, g4);
         const f4v z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < 2; ++ks)
             kp[hb][ks] = pack_perm(mfma_bf16(kr[2 * ks], sel, z), mfma_bf16(kr[2 * ks + 1], sel, z));
-            vp[hb][ks] = pack_perm(mfma_bf16(vr[2 * ks], sel, z), mfma_bf16(vr[2 * ks + 1], sel, z));
-        }
     }
     lds_barrier();   // gamma, beta visible
 
@@ -471,16 +468,6 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
             st16(blk + kOffKT + ((size_t)((wave * 2 + hb) * 2 + mp) * 64 + lane) * 8,
                  make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
         }
-    // q^[16 mt + l16][16 (2w + hb) + 4 g4 .. + 3] for Q', requested now for the end
-    uint2 qv[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int t = 16 * mt + l16;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-            qv[hb][mt] = t < L ? *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * (2 * wave + hb) + 4 * g4)
-                               : make_uint2(0, 0);
-    }
     lds_barrier();
 
     // ---- T = (I + A)^-1 by 16 x 16 blocks, stored scaled by columns as
@@ -562,11 +549,35 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(const Ctx X)
     }
     lds_barrier();
 
+    // v rows 16 mt + l16, columns [32w, 32w + 32), and q^[16 mt + l16][16 (2w + hb)
+    // + 4 g4 .. + 3] for Q': requested only now (holding them through the
+    // solve would cost registers; other workgroups on the CU cover the wait)
+    uint4 vr[4];
+    uint2 qv[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int t = 16 * mt + l16;
+        vr[mt] = t < L ? ld16(Vg + t * vrow + 32 * wave + 8 * g4) : z4;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+            qv[hb][mt] = t < L ? *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * (2 * wave + hb) + 4 * g4)
+                               : make_uint2(0, 0);
+    }
+
     // ---- the products, wave w on key column blocks kb = 2w + hb and value
     // tiles 2w + hb (hb = 0, 1), with the permuted k order throughout:
     //  W^T = k^T T'^T  (kb, mt) -> the W half of the sweep's WQ
     //  W   = T' k^     (mt, kb) -> kept: its register pairs are the A operand of (P W)^T
     //  U~  = T'' v     (mt, tile) -> the sweep's UA, and kept for P U~
+    uint4 vp[2][2];   // v fragments, packed like kp
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const uint4 sel = select_cols(hb, l16, g4);
+        const f4v z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            vp[hb][ks] = pack_perm(mfma_bf16(vr[2 * ks], sel, z), mfma_bf16(vr[2 * ks + 1], sel, z));
+    }
     uint4 wp[2][2], up[2][2];   // W and U~ block pairs, packed in the permuted k order
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
