@@ -311,6 +311,8 @@ constexpr int kIntraT1 = kIntraPb + 64 * SB * 2;   // bf16 [64][SB]  T' = T diag
 constexpr int kIntraT2 = kIntraT1 + 64 * SB * 2;   // bf16 [64][SB]  T'' = T diag(beta)
 constexpr int kIntraVec = kIntraT2 + 64 * SB * 2;  // fp32 [4][64]   gamma, beta, e^gamma, e^{gamma_L - gamma}
 constexpr int kIntraLds = kIntraVec + 4 * 64 * 4;
+constexpr int KSB = 136;   // bf16 row stride of the staged k^ / q^ rows (272 B: rows 4 banks apart)
+static_assert(2 * 64 * KSB * 2 <= kIntraVec, "staged k^ and q^ fit below the gate vectors");
 
 // Operands with a permuted k order.  A bf16 MFMA k-step ks reads, in lane
 // group g4, the 8 contraction indices s = 32 ks + 4 g4 + {0..3} and
@@ -372,27 +374,25 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     const size_t vrow = (size_t)hv * D;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
 
-    // ---- every global operand is requested at once, so the workgroup pays
-    // one memory latency for them:
-    //  ka, qa, kb: K K^T and Q K^T, wave w computing the 32 x 32 block (w >> 1, w & 1)
-    //  kr: rows 16 mt + l16, columns [32w, 32w + 32) of k^ (transposed below)
-    // (in two halves of the contraction, so that half the K K^T / Q K^T
-    // operands are in flight at once)
-    const int ra = 32 * (wave >> 1) + l32, rb = 32 * (wave & 1) + l32;
-    uint4 ka[D / 32], qa[D / 32], kb[D / 32], kr[4];
-#define GDN_LOAD_HALF(half)                                                \
-    _Pragma("unroll") for (int k2 = 0; k2 < D / 32; ++k2)                  \
-    {                                                                      \
-        const int ko = 16 * ((half) * (D / 32) + k2) + 8 * hh;             \
-        ka[k2] = ra < L ? ld16(Kg + ra * qkrow + ko) : z4;                 \
-        qa[k2] = ra < L ? ld16(Qg + ra * qkrow + ko) : z4;                 \
-        kb[k2] = rb < L ? ld16(Kg + rb * qkrow + ko) : z4;                 \
-    }
-    GDN_LOAD_HALF(0)
+    // ---- the chunk's k^ and q^ rows are staged once in LDS (in the space the
+    // solve's arrays use later): 16-byte loads, eight a thread, all in flight
+    // together; rows past the chunk's end are zero
+    uint16_t *Ks = reinterpret_cast<uint16_t *>(lds + kIntraAn);   // [64][KSB] k^
+    uint16_t *Qs = Ks + 64 * KSB;                                  // [64][KSB] q^
+    {
+        uint4 r[8];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int t = 16 * mt + l16;
-        kr[mt] = t < L ? ld16(Kg + t * qkrow + 32 * wave + 8 * g4) : z4;
+        for (int k = 0; k < 8; ++k) {
+            const int idx = k * 256 + tid;               // 0..2047: K rows then Q rows
+            const int which = idx >> 10, t = (idx >> 4) & 63, c8 = (idx & 15) * 8;
+            r[k] = t < L ? ld16((which ? Qg : Kg) + t * qkrow + c8) : z4;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int idx = k * 256 + tid;
+            const int which = idx >> 10, t = (idx >> 4) & 63, c8 = (idx & 15) * 8;
+            st16((which ? Qs : Ks) + t * KSB + c8, r[k]);
+        }
     }
 
     // ---- gamma (inclusive in-chunk scan of log alpha), beta and the decays
@@ -413,23 +413,22 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         if (lane == 0) X.el[cidh] = __expf(gL);
     }
 
-    // ---- K K^T and Q K^T; the transposed fragments of k^ and v, packed in
-    // the permuted k order: kp[hb][ks] element j holds
-    // k^[32 ks + 4 g4 + (j & 3) + 16 (j >> 2)][32 w + 16 hb + l16], vp likewise
+    lds_barrier();   // k^, q^ staged; gamma, beta visible
+
+    // ---- K K^T and Q K^T, wave w: the 32 x 32 block (w >> 1, w & 1); the
+    // transposed fragments of k^, packed in the permuted k order: kp[hb][ks]
+    // element j holds k^[32 ks + 4 g4 + (j & 3) + 16 (j >> 2)][32 w + 16 hb + l16]
     f16v S = {}, QK = {};
+    {
+        const int ra = 32 * (wave >> 1) + l32, rb = 32 * (wave & 1) + l32;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (half) {
-            __builtin_amdgcn_sched_barrier(0);
-            GDN_LOAD_HALF(1)
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < D / 32; ++k2) {
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ka[k2]), as_bf8(kb[k2]), S, 0, 0, 0);
-            QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qa[k2]), as_bf8(kb[k2]), QK, 0, 0, 0);
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const int ko = 16 * ks + 8 * hh;
+            const uint4 kb = ld16(Ks + rb * KSB + ko);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ld16(Ks + ra * KSB + ko)), as_bf8(kb), S, 0, 0, 0);
+            QK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ld16(Qs + ra * KSB + ko)), as_bf8(kb), QK, 0, 0, 0);
         }
     }
-#undef GDN_LOAD_HALF
     uint4 kp[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -437,9 +436,10 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         const f4v z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            kp[hb][ks] = pack_perm(mfma_bf16(kr[2 * ks], sel, z), mfma_bf16(kr[2 * ks + 1], sel, z));
+            kp[hb][ks] = pack_perm(mfma_bf16(ld16(Ks + (32 * ks + l16) * KSB + 32 * wave + 8 * g4), sel, z),
+                                   mfma_bf16(ld16(Ks + (32 * ks + 16 + l16) * KSB + 32 * wave + 8 * g4), sel, z));
     }
-    lds_barrier();   // gamma, beta visible
+    lds_barrier();   // every read of the staged rows done: -A and P may overwrite them
 
     // -A (strictly lower, fp32) and P (lower with diagonal, bf16)
     {
@@ -754,17 +754,23 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     uint2 ua;
     float eL;
     f4v oin;
+    // first chunk's operands, requested in the order the loop requests the
+    // next chunk's (wq; ua, oin; kt, eL), so the memory-counter waits at the
+    // loop head see one request order on both of its entries
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) wq[kb] = ld16(pWQ + kb * 512);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + j * 512);
+    __builtin_amdgcn_sched_barrier(0);
     ua = *reinterpret_cast<const uint2 *>(pUA);
-    eL = pel[0];
     {
         const __amdgpu_buffer_rsrc_t r = out_rsrc(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) oin[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ooff[i], 0, 0));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + j * 512);
+    eL = pel[0];
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();   // Ms complete
 
     // The loop is branch-free, so the compiler's memory-counter waits track
@@ -776,9 +782,8 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         const size_t nx = (size_t)cn * cstride;
         const size_t nel = (size_t)cn * hv;
 
-        // rows [16 wave, 16 wave + 16) of W M0 and Q' M0, over all 128 state
-        // rows; O starts from the chunk's P U~
-        f4v aU = {0.f, 0.f, 0.f, 0.f}, aO = oin;
+        // rows [16 wave, 16 wave + 16) of W M0 and Q' M0, over all 128 state rows
+        f4v aU = {0.f, 0.f, 0.f, 0.f}, aO = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
             const f4v mv = lds4(Ms + g4 * kMsG + l16 * kMsN + 4 * kb);
@@ -788,23 +793,26 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
                 aO = mfma_f32(bfe(wq[kb], 4 + i), mv[i], aO);
             }
         }
+        // O = P U~ + Q' M0 for rows 16 wave + 4 g4 + i, stored before the next
+        // chunk's loads are issued (no load that a later wait needs is then
+        // queued behind a store)
+        {
+            const __amdgpu_buffer_rsrc_t r = out_rsrc(c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(aO[i] + oin[i]), r, ooff[i], 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) wq[kb] = ld16(pWQ + nx + kb * 512);
 
-        // U = U~ - W M0 for rows 16 wave + 4 g4 + i, shared through Us;
-        // O = P U~ + Q' M0 for the same rows
+        // U = U~ - W M0 for the same rows, shared through Us
         f4v U;
         U[0] = __uint_as_float(ua.x << 16) - aU[0];
         U[1] = __uint_as_float(ua.x & 0xffff0000u) - aU[1];
         U[2] = __uint_as_float(ua.y << 16) - aU[2];
         U[3] = __uint_as_float(ua.y & 0xffff0000u) - aU[3];
         lds4w(Us + g4 * kUsG + l16 * kUsN + 4 * wave, U);
-        {
-            const __amdgpu_buffer_rsrc_t r = out_rsrc(c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(aO[i]), r, ooff[i], 0, 0);
-        }
         __builtin_amdgcn_sched_barrier(0);
         ua = *reinterpret_cast<const uint2 *>(pUA + nx);
         {
