@@ -131,3 +131,26 @@ def test_prefill_then_steps_continue_the_stream():
     assert max_rel_err_segments(np.stack(outs), o_ref[90:93], [0, 3]) <= TOL_PREFILL
     assert max_rel_err(st.cpu().numpy(), st_ref, 2) <= TOL_PREFILL
     assert np.array_equal(bits16(tl), tl_ref)
+
+
+@pytest.mark.parametrize("shape_name,length,cut", [("small27b", 700, 256), ("small27b", 130, 64),
+                                                   ("27b", 4722, 4096)])
+def test_prefill_resumed_at_chunk_grid_is_bitwise(shape_name, length, cut):
+    """A prompt passed in two parts, cut at a chunk boundary, gives bit for bit
+    what one pass gives: outputs, final state and conv tail (a pass resumed at
+    a grid point computes what a fresh pass does: page "kept prompt states in
+    host memory", commit notes on the family's snapshots and on resuming)."""
+    shape = SMALL_27B_HEADS if shape_name == "small27b" else gi.QWEN_27B
+    b = gi.make_batch(shape, [length], seed=38)
+    announce(f"prefill resumed at a chunk boundary: {shape_name} {length} cut at {cut}")
+    out, tail, state = run_prefill(b)
+    first = gi.Batch(shape=shape, params=b.params, row_start=torch.tensor([0, cut], dtype=torch.int32),
+                     qkv=b.qkv[:cut], a=b.a[:cut], b=b.b[:cut], tail=b.tail, state=b.state)
+    o1, t1, s1 = run_prefill(first)
+    second = gi.Batch(shape=shape, params=b.params,
+                      row_start=torch.tensor([0, length - cut], dtype=torch.int32),
+                      qkv=b.qkv[cut:], a=b.a[cut:], b=b.b[cut:], tail=t1.cpu(), state=s1.cpu())
+    o2, t2, s2 = run_prefill(second)
+    assert torch.equal(torch.cat([o1, o2]), out), "outputs differ from the single pass"
+    assert torch.equal(s2, state), "final state differs from the single pass"
+    assert torch.equal(t2, tail), "conv tail differs from the single pass"
