@@ -83,7 +83,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify27b",
-                    choices=["verify27b", "tree27b", "ragged27b", "prefill27b"])
+                    choices=["verify27b", "tree27b", "ragged27b", "window2b", "step", "prefill27b"])
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a captured HIP graph of the calls (launch-bound workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -110,6 +112,8 @@ def main():
 
     if args.workload == "prefill27b":
         return bench_prefill(args, torch, gdn, gi, dev)
+    if args.workload == "step":
+        return bench_step(args, torch, gdn, gi, dev)
 
     shape, lengths, kw = gi.workload(args.workload)
     tree = args.workload == "tree27b"
@@ -140,6 +144,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.graph:
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        step = graph.replay
 
     for _ in range(args.warmup):
         step()
@@ -188,7 +200,9 @@ def main():
         "config": {
             "workload": {"verify27b": "16 streams x 16-row verify window, per-row state and tail recorded",
                          "tree27b": "16 streams x 16-node random draft trees, per-node state and tail recorded",
-                         "ragged27b": "16 streams, ragged windows U{1..16}, per-row recording"}[args.workload],
+                         "ragged27b": "16 streams, ragged windows U{1..16}, per-row recording",
+                         "window2b": "1 stream x 16-row verify window on the 2B-like layer, per-row recording",
+                         }[args.workload] + (" (captured HIP graph replays)" if args.graph else ""),
             "layer": {"hk": shape.hk, "hv": shape.hv, "dk": shape.dk, "dv": shape.dv, "conv_width": 4},
             "streams": n, "rows": R, "seed": kw["seed"],
         },
@@ -205,6 +219,54 @@ def main():
             "kernel": "rows_kernel<128>",
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_step(args, torch, gdn, gi, dev):
+    """One-row decode steps on the small layer (1 stream): latency-bound, so
+    the figure is microseconds a step, eager and from captured graph replays
+    (64 steps a graph); the roofline line gives the algorithmic bytes and the
+    time they would take at the HBM peak."""
+    shape, lengths, kw = gi.workload("step")
+    b = gi.make_batch(shape, lengths, **kw)
+    params = gdn.LayerParams.from_host(b.params, dev)
+    qkv, a, bb = b.qkv.to(dev), b.a.to(dev), b.b.to(dev)
+    tail, state = b.tail.to(dev), b.state.to(dev)
+    out = torch.empty((1, shape.hv, shape.dv), dtype=torch.float32, device=dev)
+
+    def one():
+        gdn.conv_step(shape, params, qkv, a, bb, tail, state, out)
+
+    per_graph = 64
+    one()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            one()
+    wall_e, avg_e, med_e = timed(torch, dev, one, args.steps, args.warmup)
+    wall_g, avg_g, med_g = timed(torch, dev, graph.replay, max(1, args.steps // 8), 2)
+    us_graph = med_g * 1e3 / per_graph
+    nbytes = window_bytes(shape, 1, 1)   # one row: its state and tail written back instead of recorded
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(b, False, min(args.cpu_seconds, 3.0))
+    line = {
+        "metric": "GDN one-row decode step latency",
+        "value": round(med_e * 1e3, 3), "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_e * 1e3 / args.steps, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 (bf16 inputs)", "data": "synthetic",
+        "config": {"workload": "1 stream, one-row step, state and tail updated in place",
+                   "layer": {"hk": shape.hk, "hv": shape.hv, "dk": shape.dk, "dv": shape.dv, "conv_width": 4},
+                   "seed": kw["seed"]},
+        "eager_us_median": round(med_e * 1e3, 3), "graph_us_per_step": round(us_graph, 3),
+        "graph_steps_per_s": round(1e6 / us_graph, 1),
+        "roofline": {"bound": "latency", "algorithmic_bytes_per_step": nbytes,
+                     "ideal_us_at_hbm_peak": round(nbytes / (HBM_PEAK_GBS * 1e3), 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
