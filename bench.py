@@ -332,7 +332,7 @@ def bench_prefill(args, torch, gdn, gi, dev):
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFS,
             "unit": "TFLOP/s", "frac": round(ideal_s / (avg_ms * 1e-3), 4), "traffic": None,
-            "kernel": "whole pass (prologue, intra, sweep)",
+            "kernel": "whole pass (intra, sweep)",
             "flops_bf16": f_bf16, "flops_fp32": f_fp32,
             "note": "achieved counts bf16 flops at the fp32/bf16 peak ratio; frac = ideal time "
                     "(bf16 flops at 2.5 PF + fp32 flops at 157.3 TF) over the measured pass",

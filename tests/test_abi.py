@@ -158,14 +158,13 @@ def test_prefill_workspace_bytes(L):
     sh = _shape()
     n, T, hk, hv, d = 4, 8306, 16, 48, 128
     need = L.gdn_prefill_workspace_bytes(C.byref(sh), n, T)
-    # per row: q^/k^ and v (bf16), log alpha and beta (fp32); per chunk and
-    # value head (at most T/64 + n chunks): the sweep's bf16 operand block
-    # ([W; Q']: 128 x dk; e^{gamma_L - gamma} k^: 64 x dk; U~: 64 x dv) and
-    # e^{gamma_L} (fp32)
+    # per chunk and value head (at most T/64 + n chunks): the sweep's bf16
+    # operand block ([W; Q']: 128 x dk; e^{gamma_L - gamma} k^: 64 x dk;
+    # U~: 64 x dv) and e^{gamma_L} (fp32); nothing per row
     nc = T // 64 + n
     blk = (128 * d + 64 * d + 64 * d) * 2
-    lower = T * (hk * 2 * d * 2 + hv * d * 2 + hv * 4 * 2) + nc * hv * (blk + 4)
-    assert lower <= need <= lower + 8 * 256
+    lower = nc * hv * (blk + 4)
+    assert lower <= need <= lower + 2 * 256
     assert L.gdn_prefill_workspace_bytes(C.byref(_shape(dk=64)), 4, 100) == 0
 
 

@@ -51,6 +51,20 @@ __device__ __forceinline__ float sum_rows4(float x)
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Sum over each 16-lane row of the wave with DPP lane moves (no LDS round
+// trip); every lane of the row gets the same bits, the bits of the xor
+// butterfly over masks 1, 2, 4, 8.  quad_perm [1,0,3,2] and [2,3,0,1] sum each
+// quad, row_half_mirror the two quads of each half-row (every lane of a quad
+// holds the quad's sum), row_mirror the two half-rows.
+__device__ __forceinline__ float sum_row16(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
 // Sum over all 64 lanes (butterfly, the same bits in every lane).
 __device__ __forceinline__ float sum_wave(float x)
 {

@@ -21,18 +21,13 @@ struct PrefillArgs {
     void *workspace;
 };
 
-// Byte offsets of the workspace arrays.  Per packed row t:
-//   qk  bf16 [T][hk][2*dk]  q^ (scaled) then k^ of each key head
-//   v   bf16 [T][hv][dv]    SiLU'd values
-//   g   f32  [T][hv]        log alpha
-//   be  f32  [T][hv]        beta
-// Per chunk (dense index over the prompts' chunks, at most T/64 + n_seqs) and
-// value head, the sweep's matrix-core operands, each already in the lane order
-// the sweep's MFMAs read:
-//   blk bf16 [NC][hv][kBlockElems]  W, e^gamma q^, e^{gamma_L - gamma} k^, P, U~
+// Byte offsets of the workspace arrays.  Per chunk (dense index over the
+// prompts' chunks, at most T/64 + n_seqs) and value head, the sweep's
+// matrix-core operands, each already in the lane order the sweep's MFMAs read:
+//   blk bf16 [NC][hv][kBlockElems]  W, Q' = e^gamma q^ - P W, e^{gamma_L - gamma} k^, U~
 //   el  f32  [NC][hv]               e^{gamma_L} of the chunk
 struct PrefillLayout {
-    size_t qk, v, g, be, blk, el, total;
+    size_t blk, el, total;
     int max_chunks_total;
 };
 

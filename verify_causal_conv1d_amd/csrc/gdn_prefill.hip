@@ -15,15 +15,12 @@
 // into the parallel per-chunk kernel, and leaves the sequential sweep with
 // one fused contraction [W; Q'] M0 and the update.
 //
-// Three launches on the caller's stream:
-//   prologue  a thread owns 8 channels and walks 32 rows of one prompt
-//             with the last three raw rows in registers: causal conv (taps
-//             from the prompt's own earlier rows or its tail) + SiLU, then per
-//             row the q/k L2 norms over the 16 lanes of a head; gates per
-//             (row, value head).  q^, k^, v are stored as bf16 (matrix-core operands), log
-//             alpha and beta as fp32.
-//   intra     per (chunk, value head), independent: K K^T and Q K^T on bf16
-//             MFMA, T by 16 x 16 blocks (fp32 forward substitution on the
+// Two launches on the caller's stream:
+//   intra     per (chunk, value head), independent: the causal conv (taps
+//             from the prompt's own earlier rows or its tail) + SiLU of the
+//             chunk's q, k and v channels straight from the packed rows, the
+//             q/k L2 norms over the 16 lanes of a head, and the gates; then
+//             K K^T and Q K^T on bf16 MFMA, T by 16 x 16 blocks (fp32 forward substitution on the
 //             diagonal, fp32 MFMA off it), then W^T, W, U~, (P W)^T and P U~
 //             on bf16 MFMA.  k^ and v are transposed by an exact MFMA with a
 //             0/1 selection operand, and every later product takes a k order
@@ -31,22 +28,22 @@
 //             operand, so nothing is transposed through LDS; products are
 //             formed transposed where that puts each lane's values where the
 //             sweep's lanes read them, and everything leaves in that order.
-//   sweep     per (prompt, value head, 16 state columns), 4 waves, wave w
-//             holding state rows [32w, 32w + 32) as fp32 MFMA accumulators
-//             (v_mfma_f32_16x16x4_f32).  Per chunk: partial [W; Q'] M0 over
-//             the wave's rows with the accumulator itself as the B operand,
-//             one LDS reduction across the 4 waves, U = U~ - W M0,
-//             O = Q' M0 + P U~ (P U~ on bf16 MFMA), and the update
-//             M = e^{gamma_L} M + K~^T U, again with U's accumulator as B.
-//             Sequential over the prompt's chunks, operands of chunk c + 1
-//             fetched while chunk c computes; the state never leaves the
-//             chip.  The 8 column tiles of one (prompt, head) share their
-//             operands and are placed on one XCD (workgroup i runs on XCD
-//             i mod 8) so that they meet in that XCD's L2; prompts run
-//             longest first.
+//   sweep     per (prompt, value head, 16 state columns), 4 waves; wave w
+//             keeps state rows [32w, 32w + 32) as two fp32 16 x 16 MFMA
+//             accumulators (v_mfma_f32_16x16x4_f32) and copies them to LDS,
+//             where every wave reads all of M0.  Per chunk: rows
+//             [16w, 16w + 16) of W M0 and Q' M0 over the 128 state rows,
+//             O = Q' M0 + P U~ (P U~ left in the output rows by the
+//             per-chunk kernel), U = U~ - W M0 shared through LDS, then
+//             M = e^{gamma_L} M + K~^T U on the wave's rows.  Sequential over
+//             the prompt's chunks, operands of chunk c + 1 fetched while
+//             chunk c computes; the state never leaves the chip.  The 8
+//             column tiles of one (prompt, head) share their operands and
+//             are placed on one XCD (workgroup i runs on XCD i mod 8) so
+//             that they meet in that XCD's L2; prompts run longest first.
 // The prompt's final state replaces the stream's state, and its last three raw
 // rows (or a mix with the old tail for prompts shorter than three rows) its
-// conv tail, in place (prompt passes update the stream in place: page
+// conv tail, in place, both by the sweep, after every read of the old tail (prompt passes update the stream in place: page
 // "perf(qwen3_5 cuda): deliver the first token before drafting", commit note
 // on tree-shaped verify windows).
 #include "gdn_device.h"
@@ -56,7 +53,6 @@ namespace gdn {
 namespace {
 
 constexpr int D = 128;          // dk = dv of this pass
-constexpr int PRO_ROWS = 32;    // packed rows a prologue workgroup walks
 constexpr int NTILE = D / 16;   // 16-column state tiles of a head
 
 // A chunk-head block of sweep operands (bf16), every sub-array in lane order
@@ -81,8 +77,8 @@ struct Ctx {
     PrefillArgs P;
     int r;                      // value heads per key head
     int nc_total;               // chunk blocks in the workspace
-    uint16_t *qk, *v, *blk;
-    float *g, *be, *el;
+    uint16_t *blk;
+    float *el;
 };
 
 // Rows of prompt p, and the dense index of its first chunk.  False if p or an
@@ -155,121 +151,12 @@ __device__ __forceinline__ f4v mfma_bf16(uint4 a, uint4 b, f4v c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------- prologue
-// Block bid of PRO_ROWS rows, numbered prompt after prompt (a block never
-// crosses a prompt start): its prompt p and rows [r0, r1).  False past the
-// last block, or where the layout breaks the rules (as chunk_at).
-__device__ bool pro_block_at(const Ctx &X, int bid, int &p, int &s0, int &r0, int &r1)
+// SiLU on the hardware's approximate exp2 and reciprocal (about 1 ulp each,
+// no IEEE division sequence): every SiLU value of this pass is rounded to a
+// bf16 matrix operand right after, 2^16 times coarser.
+__device__ __forceinline__ float silu_fast(float y)
 {
-    const int T = X.P.total_rows;
-    int base = 0;
-    int prev = X.P.seq_start[0];
-    if (prev < 0) return false;
-    for (int q = 0; q < X.P.n_seqs; ++q) {
-        const int a = X.P.seq_start[q], b = X.P.seq_start[q + 1];
-        if (a != prev || b < a || b > T || b - a > X.P.max_len) return false;
-        prev = b;
-        const int nq = (b - a + PRO_ROWS - 1) / PRO_ROWS;
-        if (bid < base + nq) {
-            p = q;
-            s0 = a;
-            r0 = a + (bid - base) * PRO_ROWS;
-            r1 = min(b, r0 + PRO_ROWS);
-            return true;
-        }
-        base += nq;
-    }
-    return false;
-}
-
-__global__ void __launch_bounds__(256) prologue_kernel(const Ctx X)
-{
-    const int tid = threadIdx.x;
-    const int C = X.P.C, hv = X.P.hv, hk = X.P.hk;
-    int pidx, s0, r0, r1;
-    if (!pro_block_at(X, blockIdx.x, pidx, s0, r0, r1)) return;
-    const int nrows = r1 - r0;
-
-    // gates of every (row, value head): log alpha and beta
-    if (blockIdx.y == 0) {
-        for (int idx = tid; idx < nrows * hv; idx += 256) {
-            const int i = idx / hv, h = idx - i * hv;
-            const size_t o = (size_t)(r0 + i) * hv + h;
-            X.g[o] = log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]);
-            X.be[o] = sigmoid_f(bf16f(X.P.b[o]));
-        }
-    }
-
-    const int c0 = (blockIdx.y * 256 + tid) * 8;   // this thread's 8 channels
-    if (c0 >= C) return;                            // no barrier below
-    // role: 16 consecutive lanes form one head of 128 channels
-    const int nq = hk * D;
-    const int kind = c0 < nq ? 0 : (c0 < 2 * nq ? 1 : 2);   // q, k, v
-    const int hc = kind == 2 ? c0 - 2 * nq : c0 - kind * nq;
-    const int head = hc / D, off = hc - head * D;
-    uint16_t *dst = kind == 2 ? X.v + (size_t)head * D + off
-                              : X.qk + ((size_t)head * 2 + kind) * D + off;
-    const size_t dst_row = kind == 2 ? (size_t)hv * D : (size_t)hk * 2 * D;
-    const float qscale = kind == 0 ? 1.0f / sqrtf((float)D) : 1.0f;
-
-    float w[8][4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float4 wv = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)(c0 + e) * 4);
-        w[e][0] = wv.x; w[e][1] = wv.y; w[e][2] = wv.z; w[e][3] = wv.w;
-    }
-
-    // the window before row r0: x_{r0-d} is row r0 - d of the prompt, or row
-    // 3 + r0 - d - s0 of its tail (unconditional loads from computed sources)
-    const uint16_t *col = X.P.qkv + c0;
-    const uint16_t *tl = X.P.conv_tail + (size_t)pidx * 3 * C + c0;
-    uint4 x1, x2, x3;   // x_{t-1}, x_{t-2}, x_{t-3}
-    {
-        const int u1 = r0 - 1, u2 = r0 - 2, u3 = r0 - 3;
-        x1 = ld16(u1 >= s0 ? col + (size_t)u1 * C : tl + (size_t)(3 + u1 - s0) * C);
-        x2 = ld16(u2 >= s0 ? col + (size_t)u2 * C : tl + (size_t)(3 + u2 - s0) * C);
-        x3 = ld16(u3 >= s0 ? col + (size_t)u3 * C : tl + (size_t)(3 + u3 - s0) * C);
-    }
-    constexpr int B = 8;
-    for (int i0 = 0; i0 < nrows; i0 += B) {
-        // a batch of rows, all requested before any is used (rows past the
-        // block's end re-read its last row and are not stored)
-        uint4 xb[B];
-#pragma unroll
-        for (int k = 0; k < B; ++k) xb[k] = ld16(col + (size_t)min(r0 + i0 + k, r1 - 1) * C);
-#pragma unroll
-        for (int k = 0; k < B; ++k) {
-            const int t = r0 + i0 + k;
-            const uint4 xt = xb[k];
-            float a[8];
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float y = w[e][0] * bfe(x3, e);
-                y = fmaf(w[e][1], bfe(x2, e), y);
-                y = fmaf(w[e][2], bfe(x1, e), y);
-                y = fmaf(w[e][3], bfe(xt, e), y);
-                a[e] = silu_f(y);
-                ss = fmaf(a[e], a[e], ss);
-            }
-            // sum over the 16 lanes of this head (v lanes compute it too and
-            // ignore it, so the shuffles stay outside any branch)
-            ss += __shfl_xor(ss, 1);
-            ss += __shfl_xor(ss, 2);
-            ss += __shfl_xor(ss, 4);
-            ss += __shfl_xor(ss, 8);
-            const float sc = kind < 2 ? (1.0f / sqrtf(ss + 1e-6f)) * qscale : 1.0f;
-            uint4 o;
-            o.x = pack2(a[0] * sc, a[1] * sc);
-            o.y = pack2(a[2] * sc, a[3] * sc);
-            o.z = pack2(a[4] * sc, a[5] * sc);
-            o.w = pack2(a[6] * sc, a[7] * sc);
-            if (t < r1) st16(dst + (size_t)t * dst_row, o);
-            x3 = x2;
-            x2 = x1;
-            x1 = xt;
-        }
-    }
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * y));
 }
 
 // ---------------------------------------------------------------- intra
@@ -351,13 +238,21 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int h = blockIdx.y, kh = h / X.r;
+    // workgroup i runs on XCD i % 8.  The r value heads of one (chunk, key
+    // head), which read the same q and k rows, are consecutive workgroups of
+    // one XCD, so those rows are fetched into that XCD's L2 once.
+    const int r = X.r, hk = X.P.hk;
+    const int xcd = blockIdx.x & 7, qi = blockIdx.x >> 3;
+    const int unit = (qi / r) * 8 + xcd;              // (chunk, key head)
+    if (unit >= X.nc_total * hk) return;
+    const int cid = unit / hk, kh = unit - cid * hk;
+    const int h = kh * r + (qi - (qi / r) * r);
     int pidx, c, s0, s1;
-    if (!chunk_at(X, blockIdx.x, pidx, c, s0, s1)) return;
+    if (!chunk_at(X, cid, pidx, c, s0, s1)) return;
     const int r0 = s0 + c * kChunk;
     const int L = min(kChunk, s1 - r0);
-    const int hv = X.P.hv, hk = X.P.hk;
-    const size_t cidh = (size_t)blockIdx.x * hv + h;
+    const int hv = X.P.hv;
+    const size_t cidh = (size_t)cid * hv + h;
     uint16_t *blk = X.blk + cidh * kBlockElems;
 
     float *An = reinterpret_cast<float *>(lds + kIntraAn);
@@ -367,39 +262,64 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     float *gam = reinterpret_cast<float *>(lds + kIntraVec);
     float *bet = gam + 64, *eg = bet + 64, *ekt = eg + 64;
 
-    const size_t qkrow = (size_t)hk * 2 * D;              // elements a packed row of q^|k^
-    const uint16_t *Qg = X.qk + ((size_t)r0 * hk + kh) * 2 * D;
-    const uint16_t *Kg = Qg + D;
-    const uint16_t *Vg = X.v + ((size_t)r0 * hv + h) * D;
-    const size_t vrow = (size_t)hv * D;
+    const int C = X.P.C, nq = hk * D;
+    const uint16_t *tail = X.P.conv_tail + (size_t)pidx * 3 * C;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
+    // packed row u (>= r0 - 3) of channel group ch: the prompt's own row, or
+    // row 3 + u - s0 of its conv tail before the prompt's first row
+    auto raw_row = [&](int ch, int u) {
+        return ld16(u >= s0 ? X.P.qkv + (size_t)u * C + ch : tail + (size_t)(3 + u - s0) * C + ch);
+    };
 
-    // ---- the chunk's k^ and q^ rows are staged once in LDS (in the space the
-    // solve's arrays use later): 16-byte loads, eight a thread, all in flight
-    // together; rows past the chunk's end are zero
+    // ---- the chunk's k^ and q^ rows, staged once in LDS (in the space the
+    // solve's arrays use later).  Thread (which, c8) of 32 walks 8 consecutive
+    // rows of 8 channels: the window's 11 raw rows requested together, then per
+    // row causal conv + SiLU and the L2 norm over the 16 lanes of the head.
+    // Rows past the chunk's end are zero (their raw rows are clamped to the
+    // chunk's last row and never used).
     uint16_t *Ks = reinterpret_cast<uint16_t *>(lds + kIntraAn);   // [64][KSB] k^
-    uint16_t *Qs = Ks + 64 * KSB;                                  // [64][KSB] q^
+    uint16_t *Qs = Ks + 64 * KSB;                                  // [64][KSB] q^ (scaled)
     {
-        uint4 r[8];
+        const int which = (tid >> 4) & 1;                 // 0: k, 1: q
+        const int c8 = (tid & 15) * 8, t0 = 8 * (tid >> 5);
+        const int ch = (which ? 0 : nq) + kh * D + c8;
+        float w[8][4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int idx = k * 256 + tid;               // 0..2047: K rows then Q rows
-            const int which = idx >> 10, t = (idx >> 4) & 63, c8 = (idx & 15) * 8;
-            r[k] = t < L ? ld16((which ? Qg : Kg) + t * qkrow + c8) : z4;
+        for (int e = 0; e < 8; ++e) {
+            const float4 wv = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)(ch + e) * 4);
+            w[e][0] = wv.x; w[e][1] = wv.y; w[e][2] = wv.z; w[e][3] = wv.w;
         }
+        uint4 x[11];   // raw rows t0 - 3 .. t0 + 7 of the chunk
+#pragma unroll
+        for (int k = 0; k < 11; ++k) x[k] = raw_row(ch, min(r0 + t0 + k - 3, r0 + L - 1));
+        const float qscale = which ? 1.0f / sqrtf((float)D) : 1.0f;
+        uint16_t *dst = (which ? Qs : Ks) + c8;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int idx = k * 256 + tid;
-            const int which = idx >> 10, t = (idx >> 4) & 63, c8 = (idx & 15) * 8;
-            st16((which ? Qs : Ks) + t * KSB + c8, r[k]);
+            float a[8];
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = w[e][0] * bfe(x[k], e);
+                y = fmaf(w[e][1], bfe(x[k + 1], e), y);
+                y = fmaf(w[e][2], bfe(x[k + 2], e), y);
+                y = fmaf(w[e][3], bfe(x[k + 3], e), y);
+                a[e] = silu_fast(y);
+                ss = fmaf(a[e], a[e], ss);
+            }
+            ss = sum_row16(ss);   // over the 16 lanes of the head
+            const float sc = __builtin_amdgcn_rsqf(ss + 1e-6f) * qscale;   // approximate 1/sqrt, as SiLU
+            const uint4 o = make_uint4(pack2(a[0] * sc, a[1] * sc), pack2(a[2] * sc, a[3] * sc),
+                                       pack2(a[4] * sc, a[5] * sc), pack2(a[6] * sc, a[7] * sc));
+            st16(dst + (t0 + k) * KSB, t0 + k < L ? o : z4);
         }
     }
 
-    // ---- gamma (inclusive in-chunk scan of log alpha), beta and the decays
+    // ---- gates: gamma (inclusive in-chunk scan of log alpha), beta and the decays
     if (wave == 0) {
         const size_t o = (size_t)(r0 + lane) * hv + h;
-        float gl = lane < L ? X.g[o] : 0.0f;
-        const float bl = lane < L ? X.be[o] : 0.0f;
+        float gl = lane < L ? log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]) : 0.0f;
+        const float bl = lane < L ? sigmoid_f(bf16f(X.P.b[o])) : 0.0f;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const float up = __shfl_up(gl, d);
@@ -439,6 +359,16 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             kp[hb][ks] = pack_perm(mfma_bf16(ld16(Ks + (32 * ks + l16) * KSB + 32 * wave + 8 * g4), sel, z),
                                    mfma_bf16(ld16(Ks + (32 * ks + 16 + l16) * KSB + 32 * wave + 8 * g4), sel, z));
     }
+    // q^[16 mt + l16][16 (2w + hb) + 4 g4 .. + 3], for Q' after the solve, is
+    // parked in the very slot of the operand block that Q' takes later: the
+    // same lane reads it back and overwrites it (held in registers through
+    // the solve it would spill)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+            *reinterpret_cast<uint2 *>(blk + kOffWQ + ((mt * 8 + 2 * wave + hb) * 64 + lane) * 8 + 4) =
+                *reinterpret_cast<const uint2 *>(Qs + (16 * mt + l16) * KSB + 16 * (2 * wave + hb) + 4 * g4);
     lds_barrier();   // every read of the staged rows done: -A and P may overwrite them
 
     // -A (strictly lower, fp32) and P (lower with diagonal, bf16)
@@ -465,7 +395,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = ekt[32 * mp + 16 * (e >> 2) + 4 * g4 + (e & 3)] * bfe(kp[hb][mp], e);
-            st16(blk + kOffKT + ((size_t)((wave * 2 + hb) * 2 + mp) * 64 + lane) * 8,
+            st16(blk + kOffKT + (((wave * 2 + hb) * 2 + mp) * 64 + lane) * 8,
                  make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
         }
     lds_barrier();
@@ -549,20 +479,58 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     }
     lds_barrier();
 
-    // v rows 16 mt + l16, columns [32w, 32w + 32), and q^[16 mt + l16][16 (2w + hb)
-    // + 4 g4 .. + 3] for Q': requested only now (holding them through the
-    // solve would cost registers; other workgroups on the CU cover the wait)
+    // ---- v of value head h: causal conv + SiLU from the raw rows, requested
+    // only now (other workgroups on the CU cover the wait), staged as bf16 in
+    // the space of -A, which the solve no longer reads.  Vs row t holds 16
+    // groups of 8 channels, group c at position c ^ (t & 15), so that both the
+    // row-wise writes and the column-wise reads below meet 16 distinct banks.
+    // Thread (c, rows 4 j .. 4 j + 3) holds the 7 raw rows it needs.
+    uint16_t *Vs = reinterpret_cast<uint16_t *>(lds + kIntraAn);   // [64][128]
+    {
+        const int cg = tid & 15, t0 = 4 * (tid >> 4);
+        const int ch = 2 * nq + h * D + 8 * cg;
+        uint4 x[7];   // raw rows t0 - 3 .. t0 + 3 of the chunk
+#pragma unroll
+        for (int k = 0; k < 7; ++k) x[k] = raw_row(ch, min(r0 + t0 + k - 3, r0 + L - 1));
+        float w[8][4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float4 wv = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)(ch + e) * 4);
+            w[e][0] = wv.x; w[e][1] = wv.y; w[e][2] = wv.z; w[e][3] = wv.w;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = t0 + k;
+            float a[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = w[e][0] * bfe(x[k], e);
+                y = fmaf(w[e][1], bfe(x[k + 1], e), y);
+                y = fmaf(w[e][2], bfe(x[k + 2], e), y);
+                y = fmaf(w[e][3], bfe(x[k + 3], e), y);
+                a[e] = silu_fast(y);
+            }
+            const uint4 o = make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
+            st16(Vs + t * D + 8 * (cg ^ (t & 15)), t < L ? o : z4);
+        }
+    }
+    lds_barrier();
+    // v rows 16 mt + l16, channels [32w + 8 g4, + 8)
     uint4 vr[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) vr[mt] = ld16(Vs + (16 * mt + l16) * D + 8 * ((4 * wave + g4) ^ l16));
+    // the parked q^ values, read back from memory.  The empty asm clobbers
+    // memory, so the parking store's registers are not forwarded, and passes
+    // the lane's offset through, so that the parking addresses are not kept
+    // alive through the solve for reuse here.
+    int qoff = kOffWQ + lane * 8 + 4;
+    asm volatile("" : "+v"(qoff) : : "memory");
     uint2 qv[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int t = 16 * mt + l16;
-        vr[mt] = t < L ? ld16(Vg + t * vrow + 32 * wave + 8 * g4) : z4;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-            qv[hb][mt] = t < L ? *reinterpret_cast<const uint2 *>(Qg + t * qkrow + 16 * (2 * wave + hb) + 4 * g4)
-                               : make_uint2(0, 0);
-    }
+            qv[hb][mt] = *reinterpret_cast<const uint2 *>(blk + qoff + (mt * 8 + 2 * wave + hb) * 512);
 
     // ---- the products, wave w on key column blocks kb = 2w + hb and value
     // tiles 2w + hb (hb = 0, 1), with the permuted k order throughout:
@@ -600,9 +568,9 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
                 wpair[h2] = w;
                 upair[h2] = u;
                 // wt: lane holds W[16 mt + l16][16 kbk + 4 g4 + i]; u: U~[16 mt + 4 g4 + i][16 kbk + l16]
-                *reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kbk) * 64 + lane) * 8) =
+                *reinterpret_cast<uint2 *>(blk + kOffWQ + ((mt * 8 + kbk) * 64 + lane) * 8) =
                     make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
-                *reinterpret_cast<uint2 *>(blk + kOffUA + ((size_t)(kbk * 4 + mt) * 64 + lane) * 4) =
+                *reinterpret_cast<uint2 *>(blk + kOffUA + ((kbk * 4 + mt) * 64 + lane) * 4) =
                     make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
                 // bound how far the scheduler hoists the next block's LDS reads
                 __builtin_amdgcn_sched_barrier(0);
@@ -635,7 +603,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             const float q[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xffff0000u),
                                 __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xffff0000u)};
             const float e = eg[t];
-            *reinterpret_cast<uint2 *>(blk + kOffWQ + ((size_t)(mt * 8 + kbk) * 64 + lane) * 8 + 4) =
+            *reinterpret_cast<uint2 *>(blk + kOffWQ + ((mt * 8 + kbk) * 64 + lane) * 8 + 4) =
                 make_uint2(pack2(fmaf(e, q[0], -pw[0]), fmaf(e, q[1], -pw[1])),
                            pack2(fmaf(e, q[2], -pw[2]), fmaf(e, q[3], -pw[3])));
             // pu: lane holds (P U~)[16 mt + 4 g4 + i][16 kbk + l16]
@@ -647,24 +615,6 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
                     0);
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // the prompt's conv tail: its last three raw rows, continuing into the old
-    // tail when the prompt is shorter (the prologue, which reads the old tail,
-    // has finished: this launch follows it on the stream)
-    if (h == 0 && r0 + L == s1) {
-        const int C = X.P.C, len = s1 - s0;
-        uint16_t *tl = X.P.conv_tail + (size_t)pidx * 3 * C;
-        for (int ch = tid; ch < C; ch += 256) {
-            uint16_t nt[3];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const int m = len - 3 + j;   // local row of new tail row j
-                nt[j] = m >= 0 ? X.P.qkv[(size_t)(s0 + m) * C + ch] : tl[(size_t)(m + 3) * C + ch];
-            }
-#pragma unroll
-            for (int j = 0; j < 3; ++j) tl[(size_t)j * C + ch] = nt[j];
         }
     }
 }
@@ -845,6 +795,27 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D] = M[b][i];
+
+    // the prompt's conv tail: its last three raw rows, continuing into the old
+    // tail when the prompt is shorter.  Every read of the old tail (the
+    // per-chunk kernel's) has finished: this launch follows it on the stream.
+    // The (head, tile) workgroups of the prompt split the channel groups; one
+    // thread reads all three old rows of a group before it writes any.
+    {
+        const int C = X.P.C, len = s1 - s0;
+        uint16_t *tl = X.P.conv_tail + (size_t)pidx * 3 * C;
+        const int units = C / 8, part = hv * NTILE;
+        for (int u = h * NTILE + tile + part * tid; u < units; u += part * 256) {
+            uint4 nt[3];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int m = len - 3 + j;   // local row of new tail row j
+                nt[j] = ld16(m >= 0 ? X.P.qkv + (size_t)(s0 + m) * C + 8 * u : tl + (size_t)(m + 3) * C + 8 * u);
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j) st16(tl + (size_t)j * C + 8 * u, nt[j]);
+        }
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -856,14 +827,9 @@ PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int n_seqs, int T)
     PrefillLayout Lo = {};
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
-    const size_t t = (size_t)T;
     // each prompt adds at most one partial chunk to floor(T / 64) whole ones
     Lo.max_chunks_total = T / kChunk + n_seqs;
     const size_t nc = (size_t)Lo.max_chunks_total;
-    Lo.qk = take(t * hk * 2 * dk * 2);
-    Lo.v = take(t * hv * dv * 2);
-    Lo.g = take(t * hv * 4);
-    Lo.be = take(t * hv * 4);
     Lo.blk = take(nc * hv * kBlockElems * 2);
     Lo.el = take(nc * hv * 4);
     Lo.total = o;
@@ -889,10 +855,6 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     X.P = P;
     X.r = P.hv / P.hk;
     X.nc_total = Lo.max_chunks_total;
-    X.qk = reinterpret_cast<uint16_t *>(ws + Lo.qk);
-    X.v = reinterpret_cast<uint16_t *>(ws + Lo.v);
-    X.g = reinterpret_cast<float *>(ws + Lo.g);
-    X.be = reinterpret_cast<float *>(ws + Lo.be);
     X.blk = reinterpret_cast<uint16_t *>(ws + Lo.blk);
     X.el = reinterpret_cast<float *>(ws + Lo.el);
 
@@ -901,11 +863,8 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     if (e_lds != hipSuccess) return e_lds;
 
 
-    const unsigned units = (unsigned)(P.C / 8);
-    // 32-row blocks that never cross a prompt start: at most T/32 + n of them
-    hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(P.total_rows / PRO_ROWS + P.n_seqs), (units + 255) / 256),
-                       dim3(256), 0, stream, X);
-    hipLaunchKernelGGL(intra_kernel, dim3((unsigned)X.nc_total, P.hv), dim3(256), kIntraLds, stream, X);
+    const unsigned units = (unsigned)X.nc_total * P.hk;   // (chunk, key head) pairs
+    hipLaunchKernelGGL(intra_kernel, dim3(8 * X.r * ((units + 7) / 8)), dim3(256), kIntraLds, stream, X);
     const unsigned groups = (unsigned)P.n_seqs * P.hv;
     hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), 0, stream, X);
     return hipGetLastError();
