@@ -13,5 +13,5 @@ stated readings and are, as conventions, parity unpinned.
 """
 from .gdn_oracle import (  # noqa: F401
     OracleShape, lib, gates, conv_silu, raw_recurrence, window, tree, prefill, commit,
-    max_threads,
+    replay, commit_replay, max_threads,
 )

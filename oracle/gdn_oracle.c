@@ -28,6 +28,12 @@
  *     of 16 rows: page "perf(qwen27 cuda): reduce repeated-prompt TTFT", commit
  *     note on the qwen3_5 checkpoint with the 27B's shapes.
  *   - The prompt oracle is the plain recurrence, row after row.
+ *   - Instead of every row's state, a verify pass may log each row's decay,
+ *     write and key, and keeping a row then replays the kept path onto the
+ *     stream's recurrence (and the kept rows' raw inputs become the conv
+ *     tail): same page, commit note on tree-shaped verify windows.  Reading:
+ *     the write of row t is the vector delta_t with M_t = alpha_t M_p +
+ *     khat_t delta_t^T, i.e. delta_t = beta_t (v_t - alpha_t M_p^T khat_t).
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   conv is a cross-correlation, y_t = sum_j w[c][j] x_{t-3+j}[c], no bias;
@@ -196,6 +202,9 @@ typedef struct {
     float *snap32;                 /* [rows][hv][dk][dv] or NULL                  */
     double *final_state;           /* [hv][dk][dv] or NULL                        */
     uint16_t *final_tail;          /* [3][C] or NULL                              */
+    double *log_alpha;             /* [rows][hv] or NULL: each row's decay        */
+    double *log_delta;             /* [rows][hv][dv] or NULL: each row's write    */
+    double *log_key;               /* [rows][hk][dk] or NULL: each row's khat     */
 } stream_job;
 
 /* Per-row tails of a stream (bf16 bits): node tails follow the parents. */
@@ -238,6 +247,14 @@ static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
                     qhat, khat, v, &alpha, &beta);
         delta_step(dk, dv, khat, qhat, v, alpha, beta, cur,
                    tmp, jb->o + ((size_t)i * s->hv + h) * dv);
+        /* the log: tmp holds k^T M of the row's starting state */
+        if (jb->log_alpha) jb->log_alpha[(size_t)i * s->hv + h] = alpha;
+        if (jb->log_delta)
+            for (int j = 0; j < dv; ++j)
+                jb->log_delta[((size_t)i * s->hv + h) * dv + j] = beta * (v[j] - alpha * tmp[j]);
+        if (jb->log_key && h % (s->hv / s->hk) == 0)   /* one value head per key head writes it */
+            memcpy(jb->log_key + ((size_t)i * s->hk + h / (s->hv / s->hk)) * dk, khat,
+                   sizeof(double) * dk);
         if (is_tree) memcpy(states + (size_t)i * msz, cur, sizeof(double) * msz);
         const size_t off = ((size_t)i * s->hv + h) * msz;
         if (jb->snap64) memcpy(jb->snap64 + off, cur, sizeof(double) * msz);
@@ -298,13 +315,15 @@ static void fill_job(stream_job *jb, const oracle_shape *s, const float *conv_w,
  * row_start [n+1] (host), qkv [R][C] bf16 bits, a, b [R][hv] bf16 bits, tail
  * [n][3][C] bf16 bits, state [n][hv][dk][dv] fp64.  Outputs (any may be NULL
  * but o): o [R][hv][dv] fp64, tail_snap [R][3][C], snap64 / snap32
- * [R][hv][dk][dv].  Returns 0, or -1 on a malformed layout.
+ * [R][hv][dk][dv], and the log: log_alpha [R][hv], log_delta [R][hv][dv],
+ * log_key [R][hk][dk].  Returns 0, or -1 on a malformed layout.
  */
 int gdn_oracle_window(const oracle_shape *s, const float *conv_w, const float *a_log,
                       const float *dt_bias, int32_t n, const int32_t *row_start,
                       const int32_t *parent, const uint16_t *qkv, const uint16_t *a,
                       const uint16_t *b, const uint16_t *tail, const double *state,
-                      double *o, uint16_t *tail_snap, double *snap64, float *snap32)
+                      double *o, uint16_t *tail_snap, double *snap64, float *snap32,
+                      double *log_alpha, double *log_delta, double *log_key)
 {
     if (s->hk <= 0 || s->hv <= 0 || s->hv % s->hk || s->dk <= 0 || s->dv <= 0 || n < 0)
         return -1;
@@ -324,6 +343,9 @@ int gdn_oracle_window(const oracle_shape *s, const float *conv_w, const float *a
         if (tail_snap) jobs[st].tail_snap = tail_snap + (size_t)r0 * TAIL * C;
         if (snap64) jobs[st].snap64 = snap64 + (size_t)r0 * s->hv * msz;
         if (snap32) jobs[st].snap32 = snap32 + (size_t)r0 * s->hv * msz;
+        if (log_alpha) jobs[st].log_alpha = log_alpha + (size_t)r0 * s->hv;
+        if (log_delta) jobs[st].log_delta = log_delta + (size_t)r0 * s->hv * s->dv;
+        if (log_key) jobs[st].log_key = log_key + (size_t)r0 * s->hk * s->dk;
     }
     run_streams(jobs, n, s->hv);
     free(jobs);
@@ -385,6 +407,82 @@ int gdn_oracle_commit(const oracle_shape *s, int32_t n, int32_t total_rows,
         memcpy(state + (size_t)st * ssz, snap64 + (size_t)r * ssz, sizeof(double) * ssz);
         memcpy(tail + (size_t)st * TAIL * C, tail_snap + (size_t)r * TAIL * C,
                sizeof(uint16_t) * TAIL * C);
+    }
+    return 0;
+}
+
+/* Replay of logged rows onto one head's state M [dk][dv], in the given order:
+ * M <- alpha_t M + khat_t delta_t^T for each row t (the step of the
+ * recurrence, given its logged write). */
+void gdn_oracle_replay(int32_t dk, int32_t dv, int32_t n, const double *alpha, const double *delta,
+                       const double *key, double *M)
+{
+    for (int t = 0; t < n; ++t)
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) {
+                double *m = &M[(size_t)i * dv + j];
+                *m = alpha[t] * *m + key[(size_t)t * dk + i] * delta[(size_t)t * dv + j];
+            }
+}
+
+/*
+ * Commit by replay.  accept[s] is the packed index of stream s's kept row
+ * (within its window [row_start[s], row_start[s+1])) or -1 to keep the stream
+ * as it is.  The kept path runs from the stream's state to that row through
+ * the parents (parent == NULL: the window's rows in order); every head of
+ * the state gets the path's logged rows replayed in path order, and the conv
+ * tail becomes the last three raw rows along the path, continuing into the
+ * old tail for a path of fewer than three rows.  Logs as gdn_oracle_window
+ * writes them; state fp64 [n][hv][dk][dv] and tail [n][3][C] in/out.
+ * Returns 0, or -1 on a malformed layout or accepted row.
+ */
+int gdn_oracle_commit_replay(const oracle_shape *s, int32_t n, const int32_t *row_start,
+                             const int32_t *parent, const int32_t *accept, const uint16_t *qkv,
+                             const double *log_alpha, const double *log_delta,
+                             const double *log_key, uint16_t *tail, double *state)
+{
+    if (s->hk <= 0 || s->hv <= 0 || s->hv % s->hk || s->dk <= 0 || s->dv <= 0 || n < 0)
+        return -1;
+    const int C = channels(s), dk = s->dk, dv = s->dv, r = s->hv / s->hk;
+    const size_t msz = (size_t)dk * dv;
+    for (int st = 0; st < n; ++st) {
+        const int r0 = row_start[st], r1 = row_start[st + 1];
+        if (r1 < r0) return -1;
+        const int acc = accept[st];
+        if (acc == -1) continue;
+        if (acc < r0 || acc >= r1) return -1;
+        /* the path, leaf first, then reversed */
+        int path[64], len = 0;
+        for (int i = acc - r0; i >= 0; i = parent ? parent[r0 + i] : i - 1) {
+            if (len == 64 || (parent && parent[r0 + i] >= i)) return -1;
+            path[len++] = i;
+        }
+        for (int a = 0, b = len - 1; a < b; ++a, --b) {
+            const int t = path[a]; path[a] = path[b]; path[b] = t;
+        }
+        double *al = malloc(sizeof(double) * len), *de = malloc(sizeof(double) * len * dv);
+        double *ke = malloc(sizeof(double) * len * dk);
+        for (int h = 0; h < s->hv; ++h) {
+            for (int q = 0; q < len; ++q) {
+                const size_t row = (size_t)r0 + path[q];
+                al[q] = log_alpha[row * s->hv + h];
+                memcpy(de + (size_t)q * dv, log_delta + (row * s->hv + h) * dv, sizeof(double) * dv);
+                memcpy(ke + (size_t)q * dk, log_key + (row * s->hk + h / r) * dk, sizeof(double) * dk);
+            }
+            gdn_oracle_replay(dk, dv, len, al, de, ke, state + ((size_t)st * s->hv + h) * msz);
+        }
+        free(al); free(de); free(ke);
+        /* new tail (x_{t-2}, x_{t-1}, x_t) along the path: path row q - 2 + j,
+         * or old tail row len + j for q - 2 + j < 0 */
+        uint16_t *tl = tail + (size_t)st * TAIL * C;
+        uint16_t *nt = malloc(sizeof(uint16_t) * TAIL * C);
+        for (int j = 0; j < TAIL; ++j) {
+            const int q = len - TAIL + j;
+            const uint16_t *src = q >= 0 ? qkv + (size_t)(r0 + path[q]) * C : tl + (size_t)(len + j) * C;
+            memcpy(nt + (size_t)j * C, src, sizeof(uint16_t) * C);
+        }
+        memcpy(tl, nt, sizeof(uint16_t) * TAIL * C);
+        free(nt);
     }
     return 0;
 }

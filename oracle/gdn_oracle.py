@@ -34,12 +34,15 @@ def lib():
             L.gdn_oracle_gates.argtypes = [C.c_double] * 4 + [P, P]
             L.gdn_oracle_conv_silu.argtypes = [i32, P, P, P, P]
             L.gdn_oracle_raw_recurrence.argtypes = [i32, i32, i32] + [P] * 9
-            L.gdn_oracle_window.argtypes = [P, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P]
+            L.gdn_oracle_window.argtypes = [P, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
             L.gdn_oracle_window.restype = i32
             L.gdn_oracle_prefill.argtypes = [P, P, P, P, i32, P, P, P, P, P, P, P]
             L.gdn_oracle_prefill.restype = i32
             L.gdn_oracle_commit.argtypes = [P, i32, i32, P, P, P, P, P]
             L.gdn_oracle_commit.restype = i32
+            L.gdn_oracle_replay.argtypes = [i32, i32, i32, P, P, P, P]
+            L.gdn_oracle_commit_replay.argtypes = [P, i32, P, P, P, P, P, P, P, P, P]
+            L.gdn_oracle_commit_replay.restype = i32
             L.gdn_oracle_max_threads.restype = i32
             _lib = L
     return _lib
@@ -100,7 +103,7 @@ def raw_recurrence(alpha, beta, khat, qhat, v, M0, keep_all=False):
 
 
 def _window(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, state,
-            snap64, snap32, tail_snap):
+            snap64, snap32, tail_snap, log):
     row_start = _c(row_start, np.int32)
     n = row_start.shape[0] - 1
     R = int(row_start[-1]) if n > 0 else 0
@@ -109,33 +112,69 @@ def _window(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, s
     ts = np.zeros((R, 3, Cn), np.uint16) if tail_snap else None
     s64 = np.zeros((R, shape.hv, shape.dk, shape.dv), np.float64) if snap64 else None
     s32 = np.zeros((R, shape.hv, shape.dk, shape.dv), np.float32) if snap32 else None
+    la = np.zeros((R, shape.hv), np.float64) if log else None
+    ld = np.zeros((R, shape.hv, shape.dv), np.float64) if log else None
+    lk = np.zeros((R, shape.hk, shape.dk), np.float64) if log else None
     sh = _shape(shape)
     rc = lib().gdn_oracle_window(
         C.byref(sh), _p(_c(conv_w, np.float32)), _p(_c(a_log, np.float32)),
         _p(_c(dt_bias, np.float32)), n, _p(row_start),
         _p(None if parent is None else _c(parent, np.int32)),
         _p(_c(qkv, np.uint16)), _p(_c(a, np.uint16)), _p(_c(b, np.uint16)),
-        _p(_c(tail, np.uint16)), _p(_c(state, np.float64)), _p(o), _p(ts), _p(s64), _p(s32))
+        _p(_c(tail, np.uint16)), _p(_c(state, np.float64)), _p(o), _p(ts), _p(s64), _p(s32),
+        _p(la), _p(ld), _p(lk))
     if rc != 0:
         raise ValueError("oracle refused the layout")
-    return dict(o=o, tail_snap=ts, snap64=s64, snap32=s32)
+    return dict(o=o, tail_snap=ts, snap64=s64, snap32=s32, log_alpha=la, log_delta=ld, log_key=lk)
 
 
 def window(shape, conv_w, a_log, dt_bias, row_start, qkv, a, b, tail, state, *,
-           snap64=True, snap32=False, tail_snap=True):
+           snap64=True, snap32=False, tail_snap=True, log=False):
     """Verify windows: each stream's rows form a chain.  Returns a dict with
-    ``o`` [R][hv][dv], ``tail_snap`` [R][3][C] (uint16), and the per-row
-    states ``snap64`` (fp64) and/or ``snap32`` (rounded to fp32)."""
+    ``o`` [R][hv][dv], ``tail_snap`` [R][3][C] (uint16), the per-row
+    states ``snap64`` (fp64) and/or ``snap32`` (rounded to fp32), and with
+    ``log`` each row's decay ``log_alpha`` [R][hv], write ``log_delta``
+    [R][hv][dv] and key ``log_key`` [R][hk][dk]."""
     return _window(shape, conv_w, a_log, dt_bias, row_start, None, qkv, a, b, tail, state,
-                   snap64, snap32, tail_snap)
+                   snap64, snap32, tail_snap, log)
 
 
 def tree(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, state, *,
-         snap64=True, snap32=False, tail_snap=True):
+         snap64=True, snap32=False, tail_snap=True, log=False):
     """Tree windows: ``parent`` [R] holds each row's parent as a local index
     in its stream's window (-1 = the stream's own state and tail)."""
     return _window(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, state,
-                   snap64, snap32, tail_snap)
+                   snap64, snap32, tail_snap, log)
+
+
+def replay(alpha, delta, key, M):
+    """Logged rows replayed onto one head's state M [dk][dv] (fp64, a new
+    array): M <- alpha_t M + key_t delta_t^T for t in order."""
+    key = _c(np.atleast_2d(key), np.float64)
+    delta = _c(np.atleast_2d(delta), np.float64)
+    out = np.array(M, dtype=np.float64, copy=True, order="C")
+    dk, dv = out.shape
+    lib().gdn_oracle_replay(dk, dv, key.shape[0], _p(_c(np.atleast_1d(alpha), np.float64)),
+                            _p(delta), _p(key), _p(out))
+    return out
+
+
+def commit_replay(shape, row_start, parent, accept, qkv, log_alpha, log_delta, log_key, tail, state):
+    """Returns (tail, state) after replaying each stream's kept path (accept:
+    packed row index within the stream's window, or -1)."""
+    row_start = _c(row_start, np.int32)
+    accept = _c(accept, np.int32)
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    tl = np.array(tail, dtype=np.uint16, copy=True, order="C")
+    sh = _shape(shape)
+    rc = lib().gdn_oracle_commit_replay(
+        C.byref(sh), accept.shape[0], _p(row_start),
+        _p(None if parent is None else _c(parent, np.int32)), _p(accept), _p(_c(qkv, np.uint16)),
+        _p(_c(log_alpha, np.float64)), _p(_c(log_delta, np.float64)), _p(_c(log_key, np.float64)),
+        _p(tl), _p(st))
+    if rc != 0:
+        raise ValueError("oracle refused the layout or the accepted rows")
+    return tl, st
 
 
 def prefill(shape, conv_w, a_log, dt_bias, seq_start, qkv, a, b, tail, state):
