@@ -5,9 +5,11 @@ dk=dv=128), every row's state and conv tail recorded.
 
 One step = one gdn_recur_window call over the packed 256 rows, inputs already
 resident in HBM.  Prints ONE JSON line (see the keys below).  Extra workloads
-(``--workload tree27b`` ...) print the same line for that workload.
+(``--workload tree27b`` ...) print the same line for that workload; ``--log``
+times the logging pass (gdn_recur_log) instead of the recording one, and its
+commit by replay.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--log]
 """
 from __future__ import annotations
 
@@ -25,19 +27,43 @@ MFMA_BF16_PEAK_TFS = 2500.0     # MI355X dense bf16 matrix peak, published
 MFMA_FP32_PEAK_TFS = 157.3      # MI355X fp32 matrix peak, published
 
 
-def window_bytes(shape, n, rows):
+def window_bytes(shape, n, rows, logged=False):
     """Algorithmic HBM bytes of one window / tree call: every input read once,
-    every output written once."""
+    every output written once.  Recorded: every row's state and tail; logged:
+    every row's decay, write and key (fp32) instead."""
     C = shape.channels
     S = shape.hv * shape.dk * shape.dv * 4
+    if logged:
+        per_row_out = (shape.hv + shape.hv * shape.dv + shape.hk * shape.dk) * 4
+    else:
+        per_row_out = S + 3 * C * 2      # state and tail snapshots
     return (n * S                        # stream states in
-            + rows * S                   # per-row state snapshots out
             + n * 3 * C * 2              # conv tails in
-            + rows * 3 * C * 2           # per-row tail snapshots out
+            + rows * per_row_out         # per-row record or log out
             + rows * C * 2               # packed qkv rows in
             + rows * shape.hv * 2 * 2    # a, b in
             + rows * shape.hv * shape.dv * 4   # o out
             + C * 4 * 4 + 2 * shape.hv * 4)    # conv weights, A_log, dt_bias
+
+
+def workload_name(name, logged, graph):
+    desc = {"verify27b": "16 streams x 16-row verify window",
+            "tree27b": "16 streams x 16-node random draft trees",
+            "ragged27b": "16 streams, ragged windows U{1..16}",
+            "window2b": "1 stream x 16-row verify window on the 2B-like layer"}[name]
+    desc += (", per-row decay, write and key logged" if logged else ", per-row state and tail recorded")
+    return desc + (" (captured HIP graph replays)" if graph else "")
+
+
+def replay_bytes(shape, n, path_rows):
+    """Algorithmic HBM bytes of one commit by replay: every kept stream's
+    state read and written, its path's log entries and raw rows read, its
+    tail written (the old tail is read only for paths under three rows and
+    is not counted)."""
+    C = shape.channels
+    S = shape.hv * shape.dk * shape.dv * 4
+    per_row = (shape.hv + shape.hv * shape.dv + shape.hk * shape.dk) * 4
+    return n * (2 * S + 3 * C * 2) + path_rows * (per_row + C * 2) + 4 * (2 * n + 1)
 
 
 def prefill_flops(shape, lengths, chunk=64):
@@ -86,6 +112,9 @@ def main():
                     choices=["verify27b", "tree27b", "ragged27b", "window2b", "step", "prefill27b"])
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of the calls (launch-bound workloads)")
+    ap.add_argument("--log", action="store_true",
+                    help="window workloads: log every row's decay, write and key (gdn_recur_log) "
+                         "instead of recording its state and tail; the commit by replay is timed too")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -125,12 +154,20 @@ def main():
     tail, state = b.tail.to(dev), b.state.to(dev)
     parent = b.parent.to(dev) if tree else None
     out = torch.empty((R, shape.hv, shape.dv), dtype=torch.float32, device=dev)
-    tsnap = torch.empty((R, 3, shape.channels), dtype=torch.bfloat16, device=dev)
-    ssnap = torch.empty((R, shape.hv, shape.dk, shape.dv), dtype=torch.float32, device=dev)
     max_rows = max(lengths)
+    if args.log:
+        la = torch.empty((R, shape.hv), dtype=torch.float32, device=dev)
+        ld = torch.empty((R, shape.hv, shape.dv), dtype=torch.float32, device=dev)
+        lk = torch.empty((R, shape.hk, shape.dk), dtype=torch.float32, device=dev)
+    else:
+        tsnap = torch.empty((R, 3, shape.channels), dtype=torch.bfloat16, device=dev)
+        ssnap = torch.empty((R, shape.hv, shape.dk, shape.dv), dtype=torch.float32, device=dev)
 
     def step():
-        if tree:
+        if args.log:
+            gdn.recur_log(shape, params, row_start, qkv, a, bb, tail, state, out, la, ld, lk,
+                          max_rows=max_rows, parent=parent)
+        elif tree:
             gdn.recur_tree(shape, params, row_start, parent, qkv, a, bb, tail, state, out, tsnap,
                            ssnap, max_rows=max_rows)
         else:
@@ -175,14 +212,37 @@ def main():
     avg_ms = sum(kernel_ms) / len(kernel_ms)
     med_ms = kernel_ms[len(kernel_ms) // 2]
 
-    bytes_per_launch = window_bytes(shape, n, R)
+    bytes_per_launch = window_bytes(shape, n, R, logged=args.log)
     achieved_gbs = bytes_per_launch / (avg_ms * 1e-3) / 1e9
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = R * args.steps / wall
 
+    replay = None
+    if args.log:
+        # each stream keeps its last row (chains) or its drawn leaf (trees),
+        # replayed onto copies of the states: a commit's kernel time, alone
+        if tree:
+            acc = b.accept
+        else:
+            acc = b.row_start[1:] - 1
+        acc_d = acc.to(dtype=torch.int32, device=dev)
+        path_rows = sum(len(gi.path_to_root(b.parent[int(b.row_start[s]):int(b.row_start[s + 1])].tolist(),
+                                            int(acc[s]) - int(b.row_start[s])))
+                        for s in range(n))
+        tail_c, state_c = tail.clone(), state.clone()
+
+        def commit():
+            gdn.commit_replay(shape, row_start, acc_d, qkv, la, ld, lk, tail_c, state_c,
+                              max_rows=max_rows, parent=parent)
+
+        _, c_avg, c_med = timed(torch, dev, commit, args.steps, args.warmup)
+        rb = replay_bytes(shape, n, path_rows)
+        replay = {"kernel": "replay_kernel", "ms_avg": round(c_avg, 5), "ms_median": round(c_med, 5),
+                  "algorithmic_bytes": rb, "hbm_gbs": round(rb / (c_avg * 1e-3) / 1e9, 1)}
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(b, tree, args.cpu_seconds)
+        cpu = cpu_baseline(b, tree, args.cpu_seconds, logged=args.log)
 
     line = {
         "metric": "GDN layer tokens/s and achieved HBM GB/s at 16 streams x 16-row verify",
@@ -198,11 +258,7 @@ def main():
         "dtype": "f32 (bf16 inputs)",
         "data": "synthetic",
         "config": {
-            "workload": {"verify27b": "16 streams x 16-row verify window, per-row state and tail recorded",
-                         "tree27b": "16 streams x 16-node random draft trees, per-node state and tail recorded",
-                         "ragged27b": "16 streams, ragged windows U{1..16}, per-row recording",
-                         "window2b": "1 stream x 16-row verify window on the 2B-like layer, per-row recording",
-                         }[args.workload] + (" (captured HIP graph replays)" if args.graph else ""),
+            "workload": workload_name(args.workload, args.log, args.graph),
             "layer": {"hk": shape.hk, "hv": shape.hv, "dk": shape.dk, "dv": shape.dv, "conv_width": 4},
             "streams": n, "rows": R, "seed": kw["seed"],
         },
@@ -215,12 +271,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(f"rows_kernel<128>/{args.workload}"),
+            "traffic": measured_traffic(f"rows_kernel<128>/{args.workload}" + ("_log" if args.log else "")),
             "kernel": "rows_kernel<128>",
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "cpu_baseline": cpu,
     }
+    if replay is not None:
+        line["commit_by_replay"] = replay
     print(json.dumps(line), flush=True)
 
 
@@ -366,9 +424,10 @@ def cpu_baseline_prefill(b, budget_s):
                                         f"fp64, {el:.1f} s wall"}
 
 
-def cpu_baseline(b, tree, budget_s):
+def cpu_baseline(b, tree, budget_s, logged=False):
     """The fp64 oracle, as it stands, on the same inputs: whole calls repeated
-    until about ``budget_s`` seconds of wall time have passed."""
+    until about ``budget_s`` seconds of wall time have passed (recording every
+    row's state, or logging every row, as the timed GPU call does)."""
     import numpy as np
     import oracle
     from verify_causal_conv1d_amd import inputs as gi
@@ -379,13 +438,13 @@ def cpu_baseline(b, tree, budget_s):
     calls = 0
     t0 = time.perf_counter()
     while True:
+        kw = dict(snap64=False, snap32=not logged, tail_snap=not logged, log=logged)
         if tree:
             oracle.tree(b.shape, h["conv_w"], h["a_log"], h["dt_bias"], h["row_start"],
-                        b.parent.numpy(), h["qkv"], h["a"], h["b"], h["tail"], h["state"],
-                        snap64=False, snap32=True)
+                        b.parent.numpy(), h["qkv"], h["a"], h["b"], h["tail"], h["state"], **kw)
         else:
             oracle.window(b.shape, h["conv_w"], h["a_log"], h["dt_bias"], h["row_start"],
-                          h["qkv"], h["a"], h["b"], h["tail"], h["state"], snap64=False, snap32=True)
+                          h["qkv"], h["a"], h["b"], h["tail"], h["state"], **kw)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s or calls >= 10000:

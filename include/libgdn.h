@@ -156,6 +156,46 @@ int gdn_commit(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,
                uint16_t *conv_tail, float *state, void *stream);
 
 /*
+ * Verify windows or trees that LOG every row instead of recording its state
+ * and tail: a verify logs its rows' decay, write and key, and keeping a row
+ * replays the kept path onto the recurrence (page "perf(qwen3_5 cuda):
+ * deliver the first token before drafting", commit note on tree-shaped verify
+ * windows).  Same arguments as gdn_recur_tree, with parent == NULL for chain
+ * windows, and in place of tail_snap / state_snap:
+ *   log_alpha [total_rows][hv] fp32      alpha of each (row, value head)
+ *   log_delta [total_rows][hv][dv] fp32  the row's write delta, with
+ *             M_row = alpha M_parent + khat delta^T in the stored form M = S^T
+ *             (delta = beta (v - alpha M_parent^T khat))
+ *   log_key   [total_rows][hk][dk] fp32  khat of each (row, key head)
+ * out equals, bit for bit, what gdn_recur_window / gdn_recur_tree write; the
+ * log is about 1/100 of the recorded states' bytes at dk = dv = 128, and no
+ * per-row state is ever written.
+ */
+int gdn_recur_log(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
+                  int32_t total_rows, int32_t max_rows, const int32_t *row_start,
+                  const int32_t *parent, const uint16_t *qkv, const uint16_t *a,
+                  const uint16_t *b, const uint16_t *conv_tail, const float *state, float *out,
+                  float *log_alpha, float *log_delta, float *log_key, void *stream);
+
+/*
+ * Commit by replay after gdn_recur_log (same page and note: keeping replays
+ * the kept path in one pass and moves a tree's kept rows down).
+ * accept_row [n] int32, device: the packed index of the stream's kept row,
+ * within its window [row_start[s], row_start[s+1]), or -1 to keep the stream
+ * as it is; any other value, or a layout that breaks gdn_recur_log's rules,
+ * skips the stream.  The kept path (the row and its ancestors, root first) is
+ * replayed onto state, and the path's last three raw rows from qkv,
+ * continuing into the old tail, become conv_tail.  row_start, parent, qkv and
+ * the log are those of the gdn_recur_log call.  The result equals, bit for
+ * bit, gdn_commit of the same row after gdn_recur_window / gdn_recur_tree.
+ */
+int gdn_commit_replay(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,
+                      int32_t max_rows, const int32_t *row_start, const int32_t *parent,
+                      const int32_t *accept_row, const uint16_t *qkv, const float *log_alpha,
+                      const float *log_delta, const float *log_key, uint16_t *conv_tail,
+                      float *state, void *stream);
+
+/*
  * Bytes of device workspace gdn_prefill_chunked needs for n_seqs prompts of
  * total_rows rows in all (0 if the shape is refused).
  */

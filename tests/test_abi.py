@@ -137,6 +137,31 @@ def test_commit_refusals(L):
     assert L.gdn_commit(C.byref(sh), 2, 10, P16, P16, P16, P16, P_ODD, None) == gdn.GDN_EINVAL
 
 
+def test_log_refusals(L):
+    sh, pa = _shape(), _params()
+
+    def log(n=16, total=256, max_rows=16, parent=None, la=P16, ld=P16, lk=P16):
+        return L.gdn_recur_log(C.byref(sh), C.byref(pa), n, total, max_rows, P16, parent, P16, P16,
+                               P16, P16, P16, P16, la, ld, lk, None)
+    assert log(la=None) == gdn.GDN_EINVAL and "log_alpha" in L.gdn_last_error().decode()
+    assert log(ld=P_ODD) == gdn.GDN_EINVAL and "log_delta" in L.gdn_last_error().decode()
+    assert log(lk=None) == gdn.GDN_EINVAL and "log_key" in L.gdn_last_error().decode()
+    assert log(max_rows=17) == gdn.GDN_EINVAL
+    assert log(total=257) == gdn.GDN_EINVAL
+    assert log(n=0, total=0) == gdn.GDN_OK
+
+    def replay(n=16, total=256, max_rows=16, rs=P16, acc=P16, la=P16, state=P16):
+        return L.gdn_commit_replay(C.byref(sh), n, total, max_rows, rs, None, acc, P16, la, P16, P16,
+                                   P16, state, None)
+    assert replay(rs=None) == gdn.GDN_EINVAL and "row_start" in L.gdn_last_error().decode()
+    assert replay(acc=None) == gdn.GDN_EINVAL and "accept_row" in L.gdn_last_error().decode()
+    assert replay(la=None) == gdn.GDN_EINVAL and "log_alpha" in L.gdn_last_error().decode()
+    assert replay(state=P_ODD) == gdn.GDN_EINVAL and "state" in L.gdn_last_error().decode()
+    assert replay(max_rows=0) == gdn.GDN_EINVAL
+    assert replay(n=-1) == gdn.GDN_EINVAL
+    assert replay(n=0, total=0, rs=None, acc=None) == gdn.GDN_OK
+
+
 def test_prefill_refusals(L):
     sh, pa = _shape(), _params()
 

@@ -92,11 +92,20 @@ int launched(hipError_t e)
     return GDN_OK;
 }
 
+// What a verify pass leaves besides o: every row's recorded tail and state,
+// or (logged) every row's decay, write and key.
+struct PassOutputs {
+    uint16_t *tail_snap;
+    float *state_snap;
+    bool logged;
+    float *log_alpha, *log_delta, *log_key;
+};
+
 int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
                    int32_t total_rows, int32_t max_rows, const int32_t *row_start,
                    const int32_t *parent, bool tree, const uint16_t *qkv, const uint16_t *a,
                    const uint16_t *b, const uint16_t *conv_tail, const float *state, float *out,
-                   uint16_t *tail_snap, float *state_snap, void *stream)
+                   const PassOutputs &po, void *stream)
 {
     int rc = check_shape(shape);
     if (rc) return rc;
@@ -119,8 +128,17 @@ int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
     REQUIRE_PTR(conv_tail);
     REQUIRE_PTR(state);
     REQUIRE_PTR(out);
-    REQUIRE_PTR(tail_snap);
-    REQUIRE_PTR(state_snap);
+    if (po.logged) {
+        const float *log_alpha = po.log_alpha, *log_delta = po.log_delta, *log_key = po.log_key;
+        REQUIRE_PTR(log_alpha);
+        REQUIRE_PTR(log_delta);
+        REQUIRE_PTR(log_key);
+    } else {
+        const uint16_t *tail_snap = po.tail_snap;
+        const float *state_snap = po.state_snap;
+        REQUIRE_PTR(tail_snap);
+        REQUIRE_PTR(state_snap);
+    }
     gdn::RowsArgs A = rows_args(shape, params);
     A.vpw = heads_per_block(A.r, A.dv);
     A.n_streams = n_streams;
@@ -135,8 +153,12 @@ int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
     A.tail_in = conv_tail;
     A.state_in = state;
     A.out = out;
-    A.tail_snap = tail_snap;
-    A.state_snap = state_snap;
+    A.tail_snap = po.tail_snap;
+    A.state_snap = po.state_snap;
+    A.logged = po.logged ? 1 : 0;
+    A.log_alpha = po.log_alpha;
+    A.log_delta = po.log_delta;
+    A.log_key = po.log_key;
     if ((long long)n_streams * A.hk * (A.r / A.vpw) > 0x7fffffffLL)
         return fail(GDN_EUNSUPPORTED, "too many streams for one launch");
     if (gdn::rows_lds_bytes(A) > gdn::kRowsMaxLds)
@@ -212,8 +234,9 @@ int gdn_recur_window(const gdn_shape *shape, const gdn_params *params, int32_t n
                      const uint16_t *conv_tail, const float *state, float *out,
                      uint16_t *tail_snap, float *state_snap, void *stream)
 {
+    const PassOutputs po = {tail_snap, state_snap, false, nullptr, nullptr, nullptr};
     return window_or_tree(shape, params, n_streams, total_rows, max_rows, row_start, nullptr, false,
-                          qkv, a, b, conv_tail, state, out, tail_snap, state_snap, stream);
+                          qkv, a, b, conv_tail, state, out, po, stream);
 }
 
 int gdn_recur_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
@@ -222,8 +245,66 @@ int gdn_recur_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
                    const uint16_t *conv_tail, const float *state, float *out, uint16_t *tail_snap,
                    float *state_snap, void *stream)
 {
+    const PassOutputs po = {tail_snap, state_snap, false, nullptr, nullptr, nullptr};
     return window_or_tree(shape, params, n_streams, total_rows, max_rows, row_start, parent, true,
-                          qkv, a, b, conv_tail, state, out, tail_snap, state_snap, stream);
+                          qkv, a, b, conv_tail, state, out, po, stream);
+}
+
+int gdn_recur_log(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,
+                  int32_t total_rows, int32_t max_rows, const int32_t *row_start, const int32_t *parent,
+                  const uint16_t *qkv, const uint16_t *a, const uint16_t *b, const uint16_t *conv_tail,
+                  const float *state, float *out, float *log_alpha, float *log_delta, float *log_key,
+                  void *stream)
+{
+    const PassOutputs po = {nullptr, nullptr, true, log_alpha, log_delta, log_key};
+    return window_or_tree(shape, params, n_streams, total_rows, max_rows, row_start, parent,
+                          parent != nullptr, qkv, a, b, conv_tail, state, out, po, stream);
+}
+
+int gdn_commit_replay(const gdn_shape *shape, int32_t n_streams, int32_t total_rows, int32_t max_rows,
+                      const int32_t *row_start, const int32_t *parent, const int32_t *accept_row,
+                      const uint16_t *qkv, const float *log_alpha, const float *log_delta,
+                      const float *log_key, uint16_t *conv_tail, float *state, void *stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (n_streams < 0) return fail(GDN_EINVAL, "n_streams %d is negative", n_streams);
+    if (total_rows < 0) return fail(GDN_EINVAL, "total_rows %d is negative", total_rows);
+    if (max_rows < 1 || max_rows > GDN_MAX_WINDOW_ROWS)
+        return fail(GDN_EINVAL, "max_rows %d is outside 1..%d", max_rows, GDN_MAX_WINDOW_ROWS);
+    if ((long long)n_streams * shape->hv > 0x7fffffffLL)
+        return fail(GDN_EUNSUPPORTED, "too many streams for one launch");
+    if (n_streams == 0 || total_rows == 0) {
+        g_err[0] = '\0';
+        return GDN_OK;
+    }
+    if (!row_start) return fail(GDN_EINVAL, "row_start is NULL");
+    if (!accept_row) return fail(GDN_EINVAL, "accept_row is NULL");
+    REQUIRE_PTR(qkv);
+    REQUIRE_PTR(log_alpha);
+    REQUIRE_PTR(log_delta);
+    REQUIRE_PTR(log_key);
+    REQUIRE_PTR(conv_tail);
+    REQUIRE_PTR(state);
+    gdn::ReplayArgs A = {};
+    A.hk = shape->hk;
+    A.hv = shape->hv;
+    A.dk = shape->dk;
+    A.dv = shape->dv;
+    A.C = 2 * shape->hk * shape->dk + shape->hv * shape->dv;
+    A.n_streams = n_streams;
+    A.total_rows = total_rows;
+    A.max_rows = max_rows;
+    A.row_start = row_start;
+    A.parent = parent;
+    A.accept = accept_row;
+    A.qkv = qkv;
+    A.log_alpha = log_alpha;
+    A.log_delta = log_delta;
+    A.log_key = log_key;
+    A.tail = conv_tail;
+    A.state = state;
+    return launched(gdn::launch_replay(A, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_commit(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,

@@ -8,8 +8,8 @@
 namespace gdn {
 
 enum RowsMode : int32_t {
-    MODE_WINDOW = 0,  // chain windows, every row recorded
-    MODE_TREE = 1,    // tree windows, every row recorded
+    MODE_WINDOW = 0,  // chain windows, every row recorded or logged
+    MODE_TREE = 1,    // tree windows, every row recorded or logged
     MODE_STEP = 2,    // one row per stream, state and tail updated in place
 };
 
@@ -29,8 +29,12 @@ struct RowsArgs {
     const float *state_in;
     float *state_out;          // MODE_STEP: in place (== state_in)
     float *out;
-    uint16_t *tail_snap;       // [total_rows][3][C] (window / tree)
-    float *state_snap;         // [total_rows][hv][dk][dv] (window / tree)
+    uint16_t *tail_snap;       // [total_rows][3][C] (window / tree, recorded)
+    float *state_snap;         // [total_rows][hv][dk][dv] (window / tree, recorded)
+    int32_t logged;            // window / tree: log each row instead of recording it
+    float *log_alpha;          // [total_rows][hv]      decay
+    float *log_delta;          // [total_rows][hv][dv]  write
+    float *log_key;            // [total_rows][hk][dk]  khat
 };
 
 struct CommitArgs {
@@ -40,6 +44,19 @@ struct CommitArgs {
     const int32_t *accept;
     const uint16_t *tail_snap;
     const float *state_snap;
+    uint16_t *tail;
+    float *state;
+};
+
+// Commit by replay of the logged kept paths.
+struct ReplayArgs {
+    int32_t hk, hv, dk, dv, C;
+    int32_t n_streams, total_rows, max_rows;
+    const int32_t *row_start;
+    const int32_t *parent;     // NULL: chains
+    const int32_t *accept;
+    const uint16_t *qkv;
+    const float *log_alpha, *log_delta, *log_key;
     uint16_t *tail;
     float *state;
 };
@@ -56,5 +73,6 @@ size_t rows_lds_bytes(const RowsArgs &A);
 
 hipError_t launch_rows(const RowsArgs &A, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &A, hipStream_t stream);
+hipError_t launch_replay(const ReplayArgs &A, hipStream_t stream);
 
 }  // namespace gdn

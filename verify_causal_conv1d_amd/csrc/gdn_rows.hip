@@ -21,6 +21,17 @@
 //             gfx950 lane-swap instructions.  No barrier inside the row loop,
 //             and no global load except a tree row's parent-state reload.
 //
+// Logged windows and trees (page "perf(qwen3_5 cuda): deliver the first token
+// before drafting", commit note on tree-shaped verify windows: a verify logs
+// its rows' decay, write and key instead of every row's state) record, per
+// row, alpha (per value head), khat (per key head) and the write delta with
+// M_t = alpha M_p + khat delta^T (per value head), and no snapshot.  A logged
+// tree row whose parent is not the row just done rebuilds the parent's state:
+// the stream's state reloaded, then the parent's path replayed from the log
+// kept in LDS with the very operations that first produced it.  The commit
+// replays the kept path the same way, so it reaches, bit for bit, the state a
+// recorded window holds for that row.
+//
 // Every row of every mode runs this same code in the same order, so a window's
 // rows equal one-row steps bit for bit and a tree's paths equal chains (the
 // pages require window rows to equal one-row steps bit for bit: page
@@ -80,12 +91,14 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     float *act = smem;                                              // [mr][nch] conv+SiLU, then q^, k^
     float4 *wl = reinterpret_cast<float4 *>(act + mr * nch);        // [nch] conv weights
     uint16_t *raw = reinterpret_cast<uint16_t *>(wl + nch);         // [3 + mr][nch] raw bf16 rows
-    float *galpha = reinterpret_cast<float *>(raw + (3 + mr) * nch);  // [mr][vpw]
+    float *dlog = reinterpret_cast<float *>(raw + (3 + mr) * nch);  // [mr][vpw][dv] writes (logged)
+    float *galpha = dlog + (A.logged ? mr * A.vpw * A.dv : 0);      // [mr][vpw]
     float *gbeta = galpha + mr * A.vpw;                             // [mr][vpw]
     int *anc = reinterpret_cast<int *>(gbeta + mr * A.vpw);         // [mr][4]
     int *order = anc + mr * 4;                                      // [mr] processing order
     int *sub = order + mr;                                          // [mr] subtree sizes, then next free slot
-    int *bad = sub + mr;
+    int *pmask = sub + mr;                                          // [mr] strict ancestors, a bit each
+    int *bad = pmask + mr;
 
     // ---- this wave's tile of the state
     const int waves_per_head = A.dv / 64;
@@ -145,6 +158,10 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
             }
         } else {
             for (int i = 0; i < len; ++i) order[i] = i;
+        }
+        for (int i = 0; i < len; ++i) {
+            const int p = anc[i * 4];
+            pmask[i] = p >= 0 ? (pmask[p] | (1 << p)) : 0;
         }
     }
 
@@ -238,7 +255,7 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     }
     // ---- tail snapshots: the tail after row t is (x_{t-2}, x_{t-1}, x_t);
     // q/k channels are shared by the key head's workgroups, group 0 records them
-    if (A.mode != MODE_STEP) {
+    if (A.mode != MODE_STEP && !A.logged) {
         const int c_first = (g == 0) ? 0 : (2 * DK) / 8;
         const int cw = cpr - c_first;
         for (int idx = tid; idx < len * 3 * cw; idx += nthr) {
@@ -250,7 +267,7 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
             *reinterpret_cast<uint4 *>(A.tail_snap + ((size_t)(r0 + t) * 3 + j) * C + gc) =
                 *reinterpret_cast<const uint4 *>(raw + src_row * nch + lc);
         }
-    } else {
+    } else if (A.mode == MODE_STEP) {
         // one-row step: the new tail replaces the old one in place.  The old
         // tail is staged in LDS, and with one workgroup per key head in this
         // mode no other workgroup reads these channels.
@@ -288,6 +305,22 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     }
     lds_barrier();
 
+    // ---- the log's decays (this workgroup's value heads) and keys (the key
+    // head's workgroup group 0)
+    if (A.logged) {
+        for (int idx = tid; idx < len * A.vpw; idx += nthr) {
+            const int t = idx / A.vpw;
+            A.log_alpha[(size_t)(r0 + t) * A.hv + h0 + (idx - t * A.vpw)] = galpha[idx];
+        }
+        if (g == 0) {
+            for (int idx = tid; idx < len * (DK / 4); idx += nthr) {
+                const int t = idx / (DK / 4), i4 = idx - t * (DK / 4);
+                *reinterpret_cast<float4 *>(A.log_key + ((size_t)(r0 + t) * A.hk + kh) * DK + 4 * i4) =
+                    *reinterpret_cast<const float4 *>(act + t * nch + DK + 4 * i4);
+            }
+        }
+    }
+
     // ---- the recurrence, row after row, on the tile held in registers
     int prev = -1;
     for (int k = 0; k < len; ++k) {
@@ -295,12 +328,36 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
         const int p = anc[t * 4];
         if (p != prev) {
             // a tree row whose parent is not the row just done: reload the
-            // parent's state (the stream's own state for p == -1).  These
-            // are the addresses this lane itself stored.
-            const float *src = p < 0 ? st_in_head
-                                     : A.state_snap + ((size_t)(r0 + p) * A.hv + h) * head_elems + lane_off;
+            // parent's state (the stream's own state for p == -1).  Recorded:
+            // the parent's snapshot, at the addresses this lane itself stored.
+            // Logged: the stream's state, then the parent's path replayed.
+            const float *src = (p < 0 || A.logged)
+                                   ? st_in_head
+                                   : A.state_snap + ((size_t)(r0 + p) * A.hv + h) * head_elems + lane_off;
 #pragma unroll
             for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(src + (size_t)i * A.dv);
+            if (A.logged && p >= 0) {
+                const int path = pmask[p] | (1 << p);
+                for (int j = 0; j <= p; ++j) {
+                    if (!((path >> j) & 1)) continue;
+                    const float *kr = act + j * nch + DK + grp * R;
+                    const float aj = galpha[j * A.vpw + jl];
+                    const float4 dj = *reinterpret_cast<const float4 *>(dlog + (j * A.vpw + jl) * A.dv + col);
+#pragma unroll
+                    for (int i = 0; i < R; i += 4) {
+                        const float4 kv = *reinterpret_cast<const float4 *>(kr + i);
+                        const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float4 &me = m[i + e];
+                            me.x = fmaf(kk[e], dj.x, aj * me.x);
+                            me.y = fmaf(kk[e], dj.y, aj * me.y);
+                            me.z = fmaf(kk[e], dj.z, aj * me.z);
+                            me.w = fmaf(kk[e], dj.w, aj * me.w);
+                        }
+                    }
+                }
+            }
         }
         const float *qrow = act + t * nch + grp * R;
         const float *krow = act + t * nch + DK + grp * R;
@@ -361,6 +418,16 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
         const int row = r0 + t;
         if (grp == 0)
             *reinterpret_cast<float4 *>(A.out + ((size_t)row * A.hv + h) * A.dv + col) = o;
+        if (A.logged) {
+            // the write: to the log, and to LDS for a later replay by this
+            // wave (every lane group holds the same delta)
+            if (grp == 0) {
+                *reinterpret_cast<float4 *>(A.log_delta + ((size_t)row * A.hv + h) * A.dv + col) = d;
+                *reinterpret_cast<float4 *>(dlog + (t * A.vpw + jl) * A.dv + col) = d;
+            }
+            prev = t;
+            continue;
+        }
         float *dst = (A.mode == MODE_STEP)
                          ? A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off
                          : A.state_snap + ((size_t)row * A.hv + h) * head_elems + lane_off;
@@ -391,6 +458,94 @@ __global__ void __launch_bounds__(256) commit_kernel(const CommitArgs A)
     for (size_t i = first; i < A.tail_elems / 8; i += nthr) tdst[i] = tsrc[i];
 }
 
+// Commit by replay: the kept path of each stream (its accepted row and that
+// row's ancestors, root first) is replayed onto the stream's state from the
+// log, and the path's last three raw rows (continuing into the old tail)
+// become its conv tail.  One workgroup per (stream, value head); the
+// workgroups of a stream share the tail's channel groups out.  Each state
+// element takes the path's rows in order with the row kernel's operations,
+// so the result is the recorded state of the accepted row, bit for bit.
+__global__ void __launch_bounds__(256) replay_kernel(const ReplayArgs A)
+{
+    __shared__ int path[kMaxWindowRows];
+    __shared__ int plen;
+    __shared__ float pal[kMaxWindowRows];
+    __shared__ __align__(16) float pkey[kMaxWindowRows * 128];
+    __shared__ __align__(16) float pdel[kMaxWindowRows * 128];
+    const int tid = threadIdx.x;
+    const int s = blockIdx.x / A.hv, h = blockIdx.x - s * A.hv;
+    const int acc = A.accept[s];
+    if (acc < 0) return;
+    const int r0 = A.row_start[s], r1 = A.row_start[s + 1];
+    if (r0 < 0 || r1 < r0 || r1 > A.total_rows || r1 - r0 > A.max_rows || acc < r0 || acc >= r1) return;
+    if (tid == 0) {
+        // the path from the kept row up to the root, then reversed; a parent
+        // outside [-1, row) refuses the stream
+        int n = 0, ok = 1;
+        for (int i = acc - r0; i >= 0;) {
+            const int p = A.parent ? A.parent[r0 + i] : i - 1;
+            if (p < -1 || p >= i || n == kMaxWindowRows) {
+                ok = 0;
+                break;
+            }
+            path[n++] = i;
+            i = p;
+        }
+        for (int a = 0, b = n - 1; a < b; ++a, --b) {
+            const int t = path[a];
+            path[a] = path[b];
+            path[b] = t;
+        }
+        plen = ok ? n : 0;
+    }
+    __syncthreads();
+    const int n = plen;
+    if (n == 0) return;
+    const int dk = A.dk, dv = A.dv, kh = h / (A.hv / A.hk);
+    for (int idx = tid; idx < n * dk; idx += 256) {
+        const int q = idx / dk;
+        pkey[idx] = A.log_key[((size_t)(r0 + path[q]) * A.hk + kh) * dk + (idx - q * dk)];
+    }
+    for (int idx = tid; idx < n * dv; idx += 256) {
+        const int q = idx / dv;
+        pdel[idx] = A.log_delta[((size_t)(r0 + path[q]) * A.hv + h) * dv + (idx - q * dv)];
+    }
+    if (tid < n) pal[tid] = A.log_alpha[(size_t)(r0 + path[tid]) * A.hv + h];
+    __syncthreads();
+
+    float4 *st = reinterpret_cast<float4 *>(A.state + ((size_t)s * A.hv + h) * dk * dv);
+    const int c4n = dv / 4;
+    for (int e = tid; e < dk * c4n; e += 256) {
+        const int i = e / c4n, c = (e - i * c4n) * 4;
+        float4 m = st[e];
+        for (int q = 0; q < n; ++q) {
+            const float k = pkey[q * dk + i], a = pal[q];
+            const float4 d = *reinterpret_cast<const float4 *>(pdel + q * dv + c);
+            m.x = fmaf(k, d.x, a * m.x);
+            m.y = fmaf(k, d.y, a * m.y);
+            m.z = fmaf(k, d.z, a * m.z);
+            m.w = fmaf(k, d.w, a * m.w);
+        }
+        st[e] = m;
+    }
+
+    // the tail: new row j is path row n - 3 + j, or old tail row n + j before
+    // the path; one thread reads a channel group's three rows before writing
+    const int C = A.C, units = C / 8;
+    uint16_t *tl = A.tail + (size_t)s * 3 * C;
+    const uint16_t *src0 = n >= 3 ? A.qkv + (size_t)(r0 + path[n - 3]) * C : tl + (size_t)n * C;
+    const uint16_t *src1 = n >= 2 ? A.qkv + (size_t)(r0 + path[n - 2]) * C : tl + (size_t)(n + 1) * C;
+    const uint16_t *src2 = A.qkv + (size_t)(r0 + path[n - 1]) * C;
+    for (int u = h * 256 + tid; u < units; u += A.hv * 256) {
+        const uint4 x0 = *reinterpret_cast<const uint4 *>(src0 + 8 * u);
+        const uint4 x1 = *reinterpret_cast<const uint4 *>(src1 + 8 * u);
+        const uint4 x2 = *reinterpret_cast<const uint4 *>(src2 + 8 * u);
+        *reinterpret_cast<uint4 *>(tl + 8 * u) = x0;
+        *reinterpret_cast<uint4 *>(tl + (size_t)C + 8 * u) = x1;
+        *reinterpret_cast<uint4 *>(tl + (size_t)2 * C + 8 * u) = x2;
+    }
+}
+
 }  // namespace
 
 int rows_block_threads(const RowsArgs &A) { return 64 * A.vpw * (A.dv / 64); }
@@ -402,8 +557,9 @@ size_t rows_lds_bytes(const RowsArgs &A)
     return sizeof(float) * mr * nch                  // act
            + sizeof(float) * 4 * nch                 // conv weights
            + sizeof(uint16_t) * (3 + mr) * nch       // raw rows
+           + (A.logged ? sizeof(float) * mr * A.vpw * A.dv : 0)   // logged writes
            + sizeof(float) * 2 * mr * A.vpw          // gates
-           + sizeof(int) * (6 * mr + 1);             // ancestors, order, subtree sizes, flag
+           + sizeof(int) * (7 * mr + 1);             // ancestors, order, subtree sizes, ancestor masks, flag
 }
 
 namespace {
@@ -437,6 +593,12 @@ hipError_t launch_commit(const CommitArgs &A, hipStream_t stream)
 {
     const dim3 grid(48, (unsigned)A.n_streams);
     hipLaunchKernelGGL(commit_kernel, grid, dim3(256), 0, stream, A);
+    return hipGetLastError();
+}
+
+hipError_t launch_replay(const ReplayArgs &A, hipStream_t stream)
+{
+    hipLaunchKernelGGL(replay_kernel, dim3((unsigned)A.n_streams * A.hv), dim3(256), 0, stream, A);
     return hipGetLastError();
 }
 

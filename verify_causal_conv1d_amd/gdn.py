@@ -24,8 +24,8 @@ MAX_WINDOW_ROWS = 16
 
 EXPORTED = (
     "gdn_status_name", "gdn_last_error", "gdn_channels", "gdn_conv_step", "gdn_recur_window",
-    "gdn_recur_tree", "gdn_commit", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
-    "gdn_check_layout",
+    "gdn_recur_tree", "gdn_commit", "gdn_recur_log", "gdn_commit_replay",
+    "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_check_layout",
 )
 
 
@@ -66,13 +66,16 @@ def lib():
             L.gdn_recur_window.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
             L.gdn_recur_tree.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
             L.gdn_commit.argtypes = [P, i32, i32, P, P, P, P, P, P]
+            L.gdn_recur_log.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P]
+            L.gdn_commit_replay.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
             L.gdn_prefill_workspace_bytes.restype = C.c_size_t
             L.gdn_prefill_workspace_bytes.argtypes = [P, i32, i32]
             L.gdn_prefill_chunked.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P,
                                               C.c_size_t, P]
             L.gdn_check_layout.argtypes = [i32, i32, i32, P, P]
             for name in ("gdn_conv_step", "gdn_recur_window", "gdn_recur_tree", "gdn_commit",
-                         "gdn_prefill_chunked", "gdn_check_layout"):
+                         "gdn_recur_log", "gdn_commit_replay", "gdn_prefill_chunked",
+                         "gdn_check_layout"):
                 getattr(L, name).restype = C.c_int
             _lib = L
     return _lib
@@ -184,6 +187,46 @@ def commit(shape, accept_row, tail_snap, state_snap, conv_tail, state):
     _check(lib().gdn_commit(C.byref(sh), accept_row.shape[0], state_snap.shape[0], _ptr(accept_row),
                             _ptr(tail_snap), _ptr(state_snap), _ptr(conv_tail), _ptr(state),
                             _stream(state)), "gdn_commit")
+
+
+def recur_log(shape, params, row_start, qkv, a, b, conv_tail, state, out, log_alpha, log_delta,
+              log_key, max_rows=MAX_WINDOW_ROWS, parent=None):
+    """Verify windows (parent None) or trees that log every row's decay
+    ``log_alpha`` [R][hv], write ``log_delta`` [R][hv][dv] and key ``log_key``
+    [R][hk][dk] (fp32) instead of recording its state and tail."""
+    n = row_start.shape[0] - 1
+    total = qkv.shape[0]
+    for t, dt, nm in ((row_start, torch.int32, "row_start"), (qkv, torch.bfloat16, "qkv"),
+                      (a, torch.bfloat16, "a"), (b, torch.bfloat16, "b"),
+                      (conv_tail, torch.bfloat16, "conv_tail"), (state, torch.float32, "state"),
+                      (out, torch.float32, "out"), (log_alpha, torch.float32, "log_alpha"),
+                      (log_delta, torch.float32, "log_delta"), (log_key, torch.float32, "log_key")):
+        _dev(t, dt, nm)
+    if parent is not None:
+        _dev(parent, torch.int32, "parent")
+    sh = _shape(shape)
+    _check(lib().gdn_recur_log(C.byref(sh), C.byref(params._c), n, total, int(max_rows),
+                               _ptr(row_start), _ptr(parent), _ptr(qkv), _ptr(a), _ptr(b),
+                               _ptr(conv_tail), _ptr(state), _ptr(out), _ptr(log_alpha),
+                               _ptr(log_delta), _ptr(log_key), _stream(qkv)), "gdn_recur_log")
+
+
+def commit_replay(shape, row_start, accept_row, qkv, log_alpha, log_delta, log_key, conv_tail, state,
+                  max_rows=MAX_WINDOW_ROWS, parent=None):
+    """Each stream's kept path (accepted packed row, -1 = keep) replayed from
+    the log onto its state; the path's last raw rows become its conv tail."""
+    for t, dt, nm in ((row_start, torch.int32, "row_start"), (accept_row, torch.int32, "accept_row"),
+                      (qkv, torch.bfloat16, "qkv"), (log_alpha, torch.float32, "log_alpha"),
+                      (log_delta, torch.float32, "log_delta"), (log_key, torch.float32, "log_key"),
+                      (conv_tail, torch.bfloat16, "conv_tail"), (state, torch.float32, "state")):
+        _dev(t, dt, nm)
+    if parent is not None:
+        _dev(parent, torch.int32, "parent")
+    sh = _shape(shape)
+    _check(lib().gdn_commit_replay(C.byref(sh), accept_row.shape[0], qkv.shape[0], int(max_rows),
+                                   _ptr(row_start), _ptr(parent), _ptr(accept_row), _ptr(qkv),
+                                   _ptr(log_alpha), _ptr(log_delta), _ptr(log_key), _ptr(conv_tail),
+                                   _ptr(state), _stream(state)), "gdn_commit_replay")
 
 
 def prefill_workspace_bytes(shape: Shape, n_seqs: int, total_rows: int) -> int:
