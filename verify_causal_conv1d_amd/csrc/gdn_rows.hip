@@ -461,23 +461,34 @@ __global__ void __launch_bounds__(256) commit_kernel(const CommitArgs A)
 // Commit by replay: the kept path of each stream (its accepted row and that
 // row's ancestors, root first) is replayed onto the stream's state from the
 // log, and the path's last three raw rows (continuing into the old tail)
-// become its conv tail.  One workgroup per (stream, value head); the
-// workgroups of a stream share the tail's channel groups out.  Each state
-// element takes the path's rows in order with the row kernel's operations,
-// so the result is the recorded state of the accepted row, bit for bit.
+// become its conv tail.  One workgroup per (stream, value head); thread
+// (c4, rg) keeps state rows [rg*RPT, rg*RPT + RPT) x columns [4 c4, 4 c4 + 4)
+// in registers while the path's rows go by, reading each row's decay, write
+// and key from LDS.  Each state element takes the path's rows in order with
+// the row kernel's operations, so the result is the recorded state of the
+// accepted row, bit for bit.  The workgroups of a stream share the tail's
+// channel groups out.
+template <int DK, int DV>
 __global__ void __launch_bounds__(256) replay_kernel(const ReplayArgs A)
 {
+    constexpr int C4 = DV / 4;              // column groups of 4
+    constexpr int RPT = DK * C4 / 256;      // state rows a thread keeps
     __shared__ int path[kMaxWindowRows];
     __shared__ int plen;
     __shared__ float pal[kMaxWindowRows];
-    __shared__ __align__(16) float pkey[kMaxWindowRows * 128];
-    __shared__ __align__(16) float pdel[kMaxWindowRows * 128];
+    __shared__ __align__(16) float pkey[kMaxWindowRows * DK];
+    __shared__ __align__(16) float pdel[kMaxWindowRows * DV];
     const int tid = threadIdx.x;
     const int s = blockIdx.x / A.hv, h = blockIdx.x - s * A.hv;
     const int acc = A.accept[s];
     if (acc < 0) return;
     const int r0 = A.row_start[s], r1 = A.row_start[s + 1];
     if (r0 < 0 || r1 < r0 || r1 > A.total_rows || r1 - r0 > A.max_rows || acc < r0 || acc >= r1) return;
+    const int c4 = tid % C4, i0 = (tid / C4) * RPT;
+    float4 *st = reinterpret_cast<float4 *>(A.state + ((size_t)s * A.hv + h) * DK * DV);
+    float4 m[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) m[r] = st[(i0 + r) * C4 + c4];   // in flight while the path is found
     if (tid == 0) {
         // the path from the kept row up to the root, then reversed; a parent
         // outside [-1, row) refuses the stream
@@ -501,33 +512,39 @@ __global__ void __launch_bounds__(256) replay_kernel(const ReplayArgs A)
     __syncthreads();
     const int n = plen;
     if (n == 0) return;
-    const int dk = A.dk, dv = A.dv, kh = h / (A.hv / A.hk);
-    for (int idx = tid; idx < n * dk; idx += 256) {
-        const int q = idx / dk;
-        pkey[idx] = A.log_key[((size_t)(r0 + path[q]) * A.hk + kh) * dk + (idx - q * dk)];
+    const int kh = h / (A.hv / A.hk);
+    for (int idx = tid; idx < n * (DK / 4); idx += 256) {
+        const int q = idx / (DK / 4), i4 = idx - q * (DK / 4);
+        reinterpret_cast<float4 *>(pkey)[idx] =
+            reinterpret_cast<const float4 *>(A.log_key + ((size_t)(r0 + path[q]) * A.hk + kh) * DK)[i4];
     }
-    for (int idx = tid; idx < n * dv; idx += 256) {
-        const int q = idx / dv;
-        pdel[idx] = A.log_delta[((size_t)(r0 + path[q]) * A.hv + h) * dv + (idx - q * dv)];
+    for (int idx = tid; idx < n * C4; idx += 256) {
+        const int q = idx / C4, j4 = idx - q * C4;
+        reinterpret_cast<float4 *>(pdel)[idx] =
+            reinterpret_cast<const float4 *>(A.log_delta + ((size_t)(r0 + path[q]) * A.hv + h) * DV)[j4];
     }
     if (tid < n) pal[tid] = A.log_alpha[(size_t)(r0 + path[tid]) * A.hv + h];
     __syncthreads();
 
-    float4 *st = reinterpret_cast<float4 *>(A.state + ((size_t)s * A.hv + h) * dk * dv);
-    const int c4n = dv / 4;
-    for (int e = tid; e < dk * c4n; e += 256) {
-        const int i = e / c4n, c = (e - i * c4n) * 4;
-        float4 m = st[e];
-        for (int q = 0; q < n; ++q) {
-            const float k = pkey[q * dk + i], a = pal[q];
-            const float4 d = *reinterpret_cast<const float4 *>(pdel + q * dv + c);
-            m.x = fmaf(k, d.x, a * m.x);
-            m.y = fmaf(k, d.y, a * m.y);
-            m.z = fmaf(k, d.z, a * m.z);
-            m.w = fmaf(k, d.w, a * m.w);
+    for (int q = 0; q < n; ++q) {
+        const float a = pal[q];
+        const float4 d = reinterpret_cast<const float4 *>(pdel + q * DV)[c4];
+        float k[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; r += 4) {
+            const float4 kv = *reinterpret_cast<const float4 *>(pkey + q * DK + i0 + r);
+            k[r] = kv.x; k[r + 1] = kv.y; k[r + 2] = kv.z; k[r + 3] = kv.w;
         }
-        st[e] = m;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            m[r].x = fmaf(k[r], d.x, a * m[r].x);
+            m[r].y = fmaf(k[r], d.y, a * m[r].y);
+            m[r].z = fmaf(k[r], d.z, a * m[r].z);
+            m[r].w = fmaf(k[r], d.w, a * m[r].w);
+        }
     }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) st[(i0 + r) * C4 + c4] = m[r];
 
     // the tail: new row j is path row n - 3 + j, or old tail row n + j before
     // the path; one thread reads a channel group's three rows before writing
@@ -598,7 +615,15 @@ hipError_t launch_commit(const CommitArgs &A, hipStream_t stream)
 
 hipError_t launch_replay(const ReplayArgs &A, hipStream_t stream)
 {
-    hipLaunchKernelGGL(replay_kernel, dim3((unsigned)A.n_streams * A.hv), dim3(256), 0, stream, A);
+    const dim3 grid((unsigned)A.n_streams * A.hv);
+    if (A.dk == 128 && A.dv == 128)
+        hipLaunchKernelGGL((replay_kernel<128, 128>), grid, dim3(256), 0, stream, A);
+    else if (A.dk == 128)
+        hipLaunchKernelGGL((replay_kernel<128, 64>), grid, dim3(256), 0, stream, A);
+    else if (A.dv == 128)
+        hipLaunchKernelGGL((replay_kernel<64, 128>), grid, dim3(256), 0, stream, A);
+    else
+        hipLaunchKernelGGL((replay_kernel<64, 64>), grid, dim3(256), 0, stream, A);
     return hipGetLastError();
 }
 
