@@ -58,16 +58,18 @@ constexpr int NTILE = D / 16;   // 16-column state tiles of a head
 // A chunk-head block of sweep operands (bf16), every sub-array in lane order
 // [..][64 lanes][values]; lane l = (l16, g4) = (l & 15, l >> 4), and
 // accumulator register i of a 16x16 block holds row 4 g4 + i, column l16.
-//   WQ [w 4][kb 8][l][8]        e < 4:  W[16w + l16][16kb + 4g4 + e]
-//                               e >= 4: Q'[16w + l16][16kb + 4g4 + e - 4]
+//   W  [w 4][kb 8][l][4]        W[16w + l16][16kb + 4g4 + e]
+//   Q  [w 4][kb 8][l][4]        Q'[16w + l16][16kb + 4g4 + e]
 //        the A operands of k-step (kb, i) for output rows 16w..16w+15 of
-//        W M0 and Q' M0; step (kb, i) reads state rows 16kb + 4g4 + i
+//        W M0 and Q' M0; step (kb, i) reads state rows 16kb + 4g4 + i.
+//        Apart, so that each is written in whole lines (the two are formed
+//        at different times)
 //   KT [w 4][b 2][mp 2][l][e]   = K~[16m + 4g4 + i][32w + 16b + l16],
 //        m = 2mp + e/4, i = e%4, K~ = e^{gamma_L - gamma} k^
 //   UA [tile 8][w 4][l][4]      = U~[16w + 4g4 + i][16tile + l16]   (accumulator layout)
 // Rows past the chunk's end are zero in every array.  The chunk's P U~ goes
 // straight to the output rows (fp32), where the sweep adds Q' M0.
-constexpr int kOffWQ = 0, kOffKT = 16384, kOffUA = 24576;
+constexpr int kOffW = 0, kOffQ = 8192, kOffKT = 16384, kOffUA = 24576;
 constexpr int kBlockElems = 32768;
 // Word 3 of a raw buffer resource on gfx9-family chips (gfx950 included):
 // 32-bit data format, no swizzle; accesses past num_records are dropped.
@@ -132,12 +134,20 @@ __device__ bool chunk_at(const Ctx &X, int cid, int &p, int &c, int &s0, int &s1
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(uint16_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+__device__ __forceinline__ uint2 ld8(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
 __device__ __forceinline__ bf8v as_bf8(uint4 v) { return __builtin_bit_cast(bf8v, v); }
 
 // bf16 value e (0..7) of a 16-byte vector, as fp32
 __device__ __forceinline__ float bfe(const uint4 &u, int e)
 {
     const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+}
+
+// bf16 value e (0..3) of an 8-byte vector, as fp32
+__device__ __forceinline__ float bfe2(const uint2 &u, int e)
+{
+    const uint32_t w = (e >> 1) == 0 ? u.x : u.y;
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
 }
 
@@ -367,7 +377,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-            *reinterpret_cast<uint2 *>(blk + kOffWQ + ((mt * 8 + 2 * wave + hb) * 64 + lane) * 8 + 4) =
+            *reinterpret_cast<uint2 *>(blk + kOffQ + ((mt * 8 + 2 * wave + hb) * 64 + lane) * 4) =
                 *reinterpret_cast<const uint2 *>(Qs + (16 * mt + l16) * KSB + 16 * (2 * wave + hb) + 4 * g4);
     lds_barrier();   // every read of the staged rows done: -A and P may overwrite them
 
@@ -523,14 +533,14 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     // memory, so the parking store's registers are not forwarded, and passes
     // the lane's offset through, so that the parking addresses are not kept
     // alive through the solve for reuse here.
-    int qoff = kOffWQ + lane * 8 + 4;
+    int qoff = kOffQ + lane * 4;
     asm volatile("" : "+v"(qoff) : : "memory");
     uint2 qv[2][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-            qv[hb][mt] = *reinterpret_cast<const uint2 *>(blk + qoff + (mt * 8 + 2 * wave + hb) * 512);
+            qv[hb][mt] = *reinterpret_cast<const uint2 *>(blk + qoff + (mt * 8 + 2 * wave + hb) * 256);
 
     // ---- the products, wave w on key column blocks kb = 2w + hb and value
     // tiles 2w + hb (hb = 0, 1), with the permuted k order throughout:
@@ -568,7 +578,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
                 wpair[h2] = w;
                 upair[h2] = u;
                 // wt: lane holds W[16 mt + l16][16 kbk + 4 g4 + i]; u: U~[16 mt + 4 g4 + i][16 kbk + l16]
-                *reinterpret_cast<uint2 *>(blk + kOffWQ + ((mt * 8 + kbk) * 64 + lane) * 8) =
+                *reinterpret_cast<uint2 *>(blk + kOffW + ((mt * 8 + kbk) * 64 + lane) * 4) =
                     make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
                 *reinterpret_cast<uint2 *>(blk + kOffUA + ((kbk * 4 + mt) * 64 + lane) * 4) =
                     make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
@@ -603,7 +613,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             const float q[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xffff0000u),
                                 __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xffff0000u)};
             const float e = eg[t];
-            *reinterpret_cast<uint2 *>(blk + kOffWQ + ((mt * 8 + kbk) * 64 + lane) * 8 + 4) =
+            *reinterpret_cast<uint2 *>(blk + kOffQ + ((mt * 8 + kbk) * 64 + lane) * 4) =
                 make_uint2(pack2(fmaf(e, q[0], -pw[0]), fmaf(e, q[1], -pw[1])),
                            pack2(fmaf(e, q[2], -pw[2]), fmaf(e, q[3], -pw[3])));
             // pu: lane holds (P U~)[16 mt + 4 g4 + i][16 kbk + l16]
@@ -683,7 +693,8 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 
     const size_t cstride = (size_t)hv * kBlockElems;
     const uint16_t *bp = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
-    const uint16_t *pWQ = bp + kOffWQ + ((size_t)wave * 8 * 64 + lane) * 8;
+    const uint16_t *pW = bp + kOffW + ((size_t)wave * 8 * 64 + lane) * 4;
+    const uint16_t *pQ = bp + kOffQ + ((size_t)wave * 8 * 64 + lane) * 4;
     const uint16_t *pKT = bp + kOffKT + ((size_t)wave * 4 * 64 + lane) * 8;
     const uint16_t *pUA = bp + kOffUA + ((size_t)(tile * 4 + wave) * 64 + lane) * 4;
     const float *pel = X.el + (size_t)cid0 * hv + h;
@@ -700,15 +711,19 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
     for (int i = 0; i < 4; ++i) ooff[i] = (int)(((size_t)(16 * wave + 4 * g4 + i) * orow + (size_t)h * D + col) * 4);
 
-    uint4 wq[8], kt[4];
+    uint2 ww[8], wq[8];
+    uint4 kt[4];
     uint2 ua;
     float eL;
     f4v oin;
     // first chunk's operands, requested in the order the loop requests the
-    // next chunk's (wq; ua, oin; kt, eL), so the memory-counter waits at the
+    // next chunk's (W, Q'; ua, oin; kt, eL), so the memory-counter waits at the
     // loop head see one request order on both of its entries
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) wq[kb] = ld16(pWQ + kb * 512);
+    for (int kb = 0; kb < 8; ++kb) {
+        ww[kb] = ld8(pW + kb * 256);
+        wq[kb] = ld8(pQ + kb * 256);
+    }
     __builtin_amdgcn_sched_barrier(0);
     ua = *reinterpret_cast<const uint2 *>(pUA);
     {
@@ -739,8 +754,8 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
             const f4v mv = lds4(Ms + g4 * kMsG + l16 * kMsN + 4 * kb);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                aU = mfma_f32(bfe(wq[kb], i), mv[i], aU);
-                aO = mfma_f32(bfe(wq[kb], 4 + i), mv[i], aO);
+                aU = mfma_f32(bfe2(ww[kb], i), mv[i], aU);
+                aO = mfma_f32(bfe2(wq[kb], i), mv[i], aO);
             }
         }
         // O = P U~ + Q' M0 for rows 16 wave + 4 g4 + i, stored before the next
@@ -754,7 +769,10 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) wq[kb] = ld16(pWQ + nx + kb * 512);
+        for (int kb = 0; kb < 8; ++kb) {
+            ww[kb] = ld8(pW + nx + kb * 256);
+            wq[kb] = ld8(pQ + nx + kb * 256);
+        }
 
         // U = U~ - W M0 for the same rows, shared through Us
         f4v U;

@@ -182,23 +182,21 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
              base += B * nthr, wbase += BW * nthr, gbase += nthr) {
             uint4 v[B];
             float4 w[BW];
+            // loads from clamped indices, unconditionally (the values past
+            // the end are not stored): no branch around the register arrays
 #pragma unroll
             for (int k = 0; k < B; ++k) {
-                const int idx = base + k * nthr + tid;
-                if (idx < nchunks) {
-                    const int rr = idx / cpr;
-                    const int lc = (idx - rr * cpr) * 8;
-                    const int gc = global_channel(A, DK, kh, h0, lc);
-                    const uint16_t *src = rr < 3 ? tail + (size_t)rr * C + gc : rows + (size_t)(rr - 3) * C + gc;
-                    v[k] = *reinterpret_cast<const uint4 *>(src);
-                }
+                const int idx = min(base + k * nthr + tid, nchunks - 1);
+                const int rr = idx / cpr;
+                const int lc = (idx - rr * cpr) * 8;
+                const int gc = global_channel(A, DK, kh, h0, lc);
+                const uint16_t *src = rr < 3 ? tail + (size_t)rr * C + gc : rows + (size_t)(rr - 3) * C + gc;
+                v[k] = *reinterpret_cast<const uint4 *>(src);
             }
 #pragma unroll
             for (int k = 0; k < BW; ++k) {
-                const int ch = wbase + k * nthr + tid;
-                if (ch < nch)
-                    w[k] = *reinterpret_cast<const float4 *>(A.conv_w +
-                                                             (size_t)global_channel(A, DK, kh, h0, ch) * 4);
+                const int ch = min(wbase + k * nthr + tid, nch - 1);
+                w[k] = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)global_channel(A, DK, kh, h0, ch) * 4);
             }
             const int gi = gbase + tid;
             float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
