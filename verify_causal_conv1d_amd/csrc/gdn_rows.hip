@@ -101,9 +101,13 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     int *bad = pmask + mr;
 
     // ---- this wave's tile of the state
+    // Waves past the row loop's (vpw value heads of dv/64 waves each) only
+    // help with the prologue; their tile index is clamped to a real one, so
+    // their state loads (never used) read addresses other waves read too.
     const int waves_per_head = A.dv / 64;
-    const int jl = wave / waves_per_head;       // local value head
-    const int tile = wave - jl * waves_per_head;
+    const bool row_wave = wave < A.vpw * waves_per_head;
+    const int jl = min(wave / waves_per_head, A.vpw - 1);   // local value head
+    const int tile = row_wave ? wave - jl * waves_per_head : 0;
     const int h = h0 + jl;
     const int c4 = lane & 15, grp = lane >> 4;
     const int col = tile * 64 + c4 * 4;
@@ -318,6 +322,8 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
             }
         }
     }
+
+    if (!row_wave) return;   // no barrier below
 
     // ---- the recurrence, row after row, on the tile held in registers
     int prev = -1;
@@ -563,7 +569,15 @@ __global__ void __launch_bounds__(256) replay_kernel(const ReplayArgs A)
 
 }  // namespace
 
-int rows_block_threads(const RowsArgs &A) { return 64 * A.vpw * (A.dv / 64); }
+// The row loop needs 64 * vpw * dv/64 threads.  When the launch has no more
+// workgroups than the chip has CUs (256), each gets 512: the extra waves take
+// part in the prologue (staging, conv, norms) and then leave.
+int rows_block_threads(const RowsArgs &A)
+{
+    const long long wgs = (long long)A.n_streams * A.hk * (A.r / A.vpw);
+    const int need = 64 * A.vpw * (A.dv / 64);
+    return wgs <= 256 ? 512 : need;
+}
 
 size_t rows_lds_bytes(const RowsArgs &A)
 {
