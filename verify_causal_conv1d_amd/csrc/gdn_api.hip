@@ -55,17 +55,18 @@ int check_params(const gdn_params *p)
     } while (0)
 
 // Value heads per workgroup: the largest divisor of r whose workgroup stays
-// within 8 waves (512 threads).  LIBGDN_HEADS_PER_BLOCK overrides it (a
-// tuning knob; it must divide r and fit the limit).
+// within 16 waves (1024 threads; a wave holds 32 state columns of a head).
+// LIBGDN_HEADS_PER_BLOCK overrides it (a tuning knob; it must divide r and
+// fit the limit).
 int heads_per_block(int r, int dv)
 {
-    const int waves_per_head = dv / 64;
+    const int waves_per_head = dv / 32;
     int best = 1;
     for (int v = 1; v <= r; ++v)
-        if (r % v == 0 && v * waves_per_head <= 8) best = v;
+        if (r % v == 0 && v * waves_per_head <= 16) best = v;
     if (const char *e = getenv("LIBGDN_HEADS_PER_BLOCK")) {
         const int v = atoi(e);
-        if (v >= 1 && r % v == 0 && v * waves_per_head <= 8) best = v;
+        if (v >= 1 && r % v == 0 && v * waves_per_head <= 16) best = v;
     }
     return best;
 }
@@ -200,7 +201,7 @@ int gdn_conv_step(const gdn_shape *shape, const gdn_params *params, int32_t n_st
     if (rc) return rc;
     if (n_streams < 0) return fail(GDN_EINVAL, "n_streams %d is negative", n_streams);
     const int r = shape->hv / shape->hk;
-    if (r * (shape->dv / 64) > 8)
+    if (r * (shape->dv / 32) > 16)
         return fail(GDN_EUNSUPPORTED, "one-row steps need (hv/hk) * dv <= 512 (got %d * %d)", r, shape->dv);
     if (n_streams == 0) {
         g_err[0] = '\0';

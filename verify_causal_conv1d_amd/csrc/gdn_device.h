@@ -65,6 +65,15 @@ __device__ __forceinline__ float sum_row16(float x)
     return x;
 }
 
+// Sum over the eight 8-lane groups of the wave (lanes l, l^8, ..., l^56);
+// every lane gets the same bits.  row_ror:8 pairs each lane with lane ^ 8
+// inside its 16-lane row, then permlane16_swap and permlane32_swap as above.
+__device__ __forceinline__ float sum_rows8(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    return sum_rows4(x);
+}
+
 // Sum over all 64 lanes (butterfly, the same bits in every lane).
 __device__ __forceinline__ float sum_wave(float x)
 {

@@ -10,16 +10,19 @@
 //             along the row's own branch) + SiLU, from LDS; gates per (row,
 //             value head); per row an L2 norm of q and of k (q also times
 //             dk^-1/2).  Tail snapshots are 16-byte copies out of the staged rows.
-//   rows      each wave owns 64 columns of one value head's state M = S^T
-//             ([dk][dv], dv contiguous).  Lane (c, g) = (lane & 15, lane >> 4)
-//             keeps rows [g*dk/4, (g+1)*dk/4) x columns [4c, 4c+4) of the
+//   rows      each wave owns 32 columns of one value head's state M = S^T
+//             ([dk][dv], dv contiguous).  Lane (c, g) = (lane & 7, lane >> 3)
+//             keeps rows [g*dk/8, (g+1)*dk/8) x columns [4c, 4c+4) of the
 //             tile in VGPRs for the whole window, so the state crosses HBM
 //             once on the way in; the per-row snapshot is written with
-//             dwordx4 stores that form full 256-byte row segments.
+//             dwordx4 stores that form full 128-byte row segments.
 //             The two dk-sums (M^T k and M^T q) are per-lane partials over the
-//             lane's rows, then a butterfly over the four 16-lane rows with the
-//             gfx950 lane-swap instructions.  No barrier inside the row loop,
-//             and no global load except a tree row's parent-state reload.
+//             lane's rows, then a butterfly over the eight 8-lane groups: a
+//             DPP row rotate, then the gfx950 lane-swap instructions.  No
+//             barrier inside the row loop, and no global load except a tree
+//             row's parent-state reload.  Narrow tiles spread the row loop's
+//             fp32 work (four operations per state element and row) over
+//             twice the waves of 64-column ones.
 //
 // Logged windows and trees (page "perf(qwen3_5 cuda): deliver the first token
 // before drafting", commit note on tree-shaped verify windows: a verify logs
@@ -54,9 +57,9 @@ __device__ __forceinline__ int global_channel(const RowsArgs &A, int dk, int kh,
 }
 
 template <int DK>
-__global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
+__global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 {
-    constexpr int R = DK / 4;  // state rows held by one lane
+    constexpr int R = DK / 8;  // state rows held by one lane
     extern __shared__ float smem[];
 
     const int tid = threadIdx.x;
@@ -101,16 +104,16 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
     int *bad = pmask + mr;
 
     // ---- this wave's tile of the state
-    // Waves past the row loop's (vpw value heads of dv/64 waves each) only
+    // Waves past the row loop's (vpw value heads of dv/32 waves each) only
     // help with the prologue; their tile index is clamped to a real one, so
     // their state loads (never used) read addresses other waves read too.
-    const int waves_per_head = A.dv / 64;
+    const int waves_per_head = A.dv / 32;
     const bool row_wave = wave < A.vpw * waves_per_head;
     const int jl = min(wave / waves_per_head, A.vpw - 1);   // local value head
     const int tile = row_wave ? wave - jl * waves_per_head : 0;
     const int h = h0 + jl;
-    const int c4 = lane & 15, grp = lane >> 4;
-    const int col = tile * 64 + c4 * 4;
+    const int c4 = lane & 7, grp = lane >> 3;
+    const int col = tile * 32 + c4 * 4;
     const size_t head_elems = (size_t)DK * A.dv;
     const size_t lane_off = (size_t)(grp * R) * A.dv + col;
     const float *st_in_head = A.state_in + ((size_t)s * A.hv + h) * head_elems + lane_off;
@@ -380,10 +383,10 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
                 u.w = fmaf(m[i + e].w, kk[e], u.w);
             }
         }
-        u.x = sum_rows4(u.x);
-        u.y = sum_rows4(u.y);
-        u.z = sum_rows4(u.z);
-        u.w = sum_rows4(u.w);
+        u.x = sum_rows8(u.x);
+        u.y = sum_rows8(u.y);
+        u.z = sum_rows8(u.z);
+        u.w = sum_rows8(u.w);
 
         // delta = beta (v - alpha u);  M <- alpha M + k delta^T;  o = M^T q
         const float al = galpha[t * A.vpw + jl];
@@ -414,10 +417,10 @@ __global__ void __launch_bounds__(512) rows_kernel(const RowsArgs A)
                 o.w = fmaf(me.w, qq[e], o.w);
             }
         }
-        o.x = sum_rows4(o.x);
-        o.y = sum_rows4(o.y);
-        o.z = sum_rows4(o.z);
-        o.w = sum_rows4(o.w);
+        o.x = sum_rows8(o.x);
+        o.y = sum_rows8(o.y);
+        o.z = sum_rows8(o.z);
+        o.w = sum_rows8(o.w);
 
         const int row = r0 + t;
         if (grp == 0)
@@ -569,14 +572,14 @@ __global__ void __launch_bounds__(256) replay_kernel(const ReplayArgs A)
 
 }  // namespace
 
-// The row loop needs 64 * vpw * dv/64 threads.  When the launch has no more
-// workgroups than the chip has CUs (256), each gets 512: the extra waves take
-// part in the prologue (staging, conv, norms) and then leave.
+// The row loop needs 64 * vpw * dv/32 threads.  When the launch has no more
+// workgroups than the chip has CUs (256), each gets at least 512: the extra
+// waves take part in the prologue (staging, conv, norms) and then leave.
 int rows_block_threads(const RowsArgs &A)
 {
     const long long wgs = (long long)A.n_streams * A.hk * (A.r / A.vpw);
-    const int need = 64 * A.vpw * (A.dv / 64);
-    return wgs <= 256 ? 512 : need;
+    const int need = 64 * A.vpw * (A.dv / 32);
+    return wgs <= 256 ? max(need, 512) : need;
 }
 
 size_t rows_lds_bytes(const RowsArgs &A)
