@@ -1,6 +1,7 @@
 """HIP-graph capture of the launch-bound calls (one-row steps, a 2B-like
-verify window): captured launches replayed several times give, bit for bit,
-what the same calls give run eagerly.  Every count the kernels need is read on
+verify window, a logged verify round with its commit by replay, a prompt
+pass): captured launches replayed several times give, bit for bit, what the
+same calls give run eagerly.  Every count the kernels need is read on
 the device, so one captured graph serves any window layout of the same sizes
 (captured forwards: page "perf(qwen3_5 cuda): deliver the first token before
 drafting", commit note on captured forwards and device-read counts)."""
@@ -88,3 +89,90 @@ def test_captured_window_equals_eager_window_for_new_layouts():
         assert torch.equal(out_g[:length], out_e[:length]), f"window of {length}: outputs differ"
         assert torch.equal(ss_g[:length], ss_e[:length]), f"window of {length}: snapshots differ"
         assert torch.equal(ts_g[:length], ts_e[:length]), f"window of {length}: tail snapshots differ"
+
+
+def test_captured_logged_verify_round_equals_eager():
+    """A logged verify pass followed by the commit by replay, captured as one
+    graph: every replay (with new accepted rows written into the same device
+    buffer between replays) equals the eager calls bit for bit."""
+    shape = gi.Shape(hk=2, hv=6, dk=128, dv=128)
+    lengths = [16, 7, 12]
+    b = gi.make_batch(shape, lengths, seed=42)
+    announce(f"graph capture: logged verify {lengths} + commit by replay")
+    d = device_batch(b)
+    R = b.rows
+    rs = b.row_start.tolist()
+
+    def bufs():
+        return (torch.empty((R, shape.hv, shape.dv), device="cuda"),
+                torch.empty((R, shape.hv), device="cuda"),
+                torch.empty((R, shape.hv, shape.dv), device="cuda"),
+                torch.empty((R, shape.hk, shape.dk), device="cuda"))
+
+    out_g, la_g, ld_g, lk_g = bufs()
+    out_e, la_e, ld_e, lk_e = bufs()
+    accept = torch.tensor([rs[1] - 1, rs[1] + 3, -1], dtype=torch.int32, device="cuda")
+    tail0, state0 = d["tail"].clone(), d["state"].clone()
+    tail_g, state_g = tail0.clone(), state0.clone()
+
+    def round_(tail, state, out, la, ld, lk):
+        gdn.recur_log(shape, d["params"], d["row_start"], d["qkv"], d["a"], d["b"], tail, state, out, la, ld,
+                      lk, max_rows=16)
+        gdn.commit_replay(shape, d["row_start"], accept, d["qkv"], la, ld, lk, tail, state, max_rows=16)
+
+    round_(tail0.clone(), state0.clone(), out_g, la_g, ld_g, lk_g)   # first-call set-up, outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        round_(tail_g, state_g, out_g, la_g, ld_g, lk_g)
+    torch.cuda.synchronize()
+    tail_e, state_e = tail0.clone(), state0.clone()
+    for rep, acc in enumerate(([rs[1] - 1, rs[1] + 3, -1], [rs[0] + 5, -1, rs[3] - 1], [rs[0], rs[2] - 1, rs[2]])):
+        accept.copy_(torch.tensor(acc, dtype=torch.int32))
+        g.replay()
+        torch.cuda.synchronize()
+        round_(tail_e, state_e, out_e, la_e, ld_e, lk_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep}: o differs"
+        assert torch.equal(ld_g, ld_e) and torch.equal(lk_g, lk_e) and torch.equal(la_g, la_e), f"replay {rep}: log"
+        assert torch.equal(state_g, state_e), f"replay {rep}: states differ"
+        assert torch.equal(tail_g, tail_e), f"replay {rep}: tails differ"
+
+
+def test_captured_prompt_pass_equals_eager():
+    """The chunked prompt pass (two launches, no host work between them)
+    captured and replayed several times, each replay from the same initial
+    state, equals the eager pass bit for bit."""
+    shape = gi.Shape(hk=2, hv=6, dk=128, dv=128)
+    lengths = [200, 64, 3, 130]
+    b = gi.make_batch(shape, lengths, seed=43)
+    announce(f"graph capture: prompt pass {lengths}")
+    d = device_batch(b)
+    ws = torch.empty(gdn.prefill_workspace_bytes(shape, b.n, b.rows), dtype=torch.uint8, device="cuda")
+    out_g = torch.empty((b.rows, shape.hv, shape.dv), device="cuda")
+    out_e = torch.empty_like(out_g)
+    tail0, state0 = d["tail"].clone(), d["state"].clone()
+    tail_g, state_g = tail0.clone(), state0.clone()
+
+    def pass_(tail, state, out):
+        gdn.prefill_chunked(shape, d["params"], d["row_start"], d["qkv"], d["a"], d["b"], tail, state, out, ws,
+                            max_len=max(lengths))
+
+    pass_(tail0.clone(), state0.clone(), out_g)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pass_(tail_g, state_g, out_g)
+    torch.cuda.synchronize()
+    tail_e, state_e = tail0.clone(), state0.clone()
+    pass_(tail_e, state_e, out_e)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        tail_g.copy_(tail0)
+        state_g.copy_(state0)
+        out_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep}: o differs"
+        assert torch.equal(state_g, state_e), f"replay {rep}: states differ"
+        assert torch.equal(tail_g, tail_e), f"replay {rep}: tails differ"
