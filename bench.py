@@ -207,6 +207,7 @@ def main():
     avg_ms = sum(kernel_ms) / len(kernel_ms)
     med_ms = kernel_ms[len(kernel_ms) // 2]
 
+    cold_ms = cold_timed(torch, dev, step) if not args.graph else None
     bytes_per_launch = window_bytes(shape, n, R, logged=args.log)
     achieved_gbs = bytes_per_launch / (avg_ms * 1e-3) / 1e9
     ms_per_step = wall * 1e3 / args.steps
@@ -260,6 +261,7 @@ def main():
         "hbm_gbs": round(achieved_gbs, 1),
         "kernel_ms_avg": round(avg_ms, 5),
         "kernel_ms_median": round(med_ms, 5),
+        "kernel_ms_cold_median": None if cold_ms is None else round(cold_ms, 5),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
@@ -336,6 +338,35 @@ def copy_calibration(torch, dev):
     del src, dst
 
 
+def cold_timed(torch, dev, step, calls=10):
+    """Median event time of single calls, each after a 512 MB scratch write
+    that evicts the 256 MB last-level cache (the write is outside the events)."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ms = []
+    for _ in range(calls):
+        scratch.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms.append(s.elapsed_time(e))
+    del scratch
+    ms.sort()
+    return ms[len(ms) // 2]
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def timed(torch, dev, step, steps, warmup):
     """Warm-up, then per-launch events on torch's current stream (where libgdn
     launches) and the wall clock of the whole timed region."""
@@ -375,6 +406,7 @@ def bench_prefill(args, torch, gdn, gi, dev):
     if args.copy_calibration:
         copy_calibration(torch, dev)
     wall, avg_ms, med_ms = timed(torch, dev, step, args.steps, args.warmup)
+    cold_ms = cold_timed(torch, dev, step)
     f_bf16, f_fp32 = prefill_flops(shape, lengths)
     ideal_s = f_bf16 / (MFMA_BF16_PEAK_TFS * 1e12) + f_fp32 / (MFMA_FP32_PEAK_TFS * 1e12)
     fp32_equiv = f_fp32 + f_bf16 * MFMA_FP32_PEAK_TFS / MFMA_BF16_PEAK_TFS
@@ -395,6 +427,7 @@ def bench_prefill(args, torch, gdn, gi, dev):
                              "conv_width": 4},
                    "prompts": lengths, "rows": b.rows, "seed": kw["seed"]},
         "pass_ms_avg": round(avg_ms, 5), "pass_ms_median": round(med_ms, 5),
+        "pass_ms_cold_median": round(cold_ms, 5),
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFS,
             "unit": "TFLOP/s", "frac": round(ideal_s / (avg_ms * 1e-3), 4),
@@ -428,7 +461,7 @@ def cpu_baseline_prefill(b, budget_s):
         el += time.perf_counter() - t0
         rows += n
         n *= 2
-    return {"value": round(rows / el, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
+    return {"value": round(rows / el, 2), "unit": "tokens/s", "cores": oracle.max_threads(), "cpu": cpu_model(),
             "kind": "oracle", "sample": f"recurrent prompt passes of 64, 128, ... rows ({rows} rows in all), "
                                         f"fp64, {el:.1f} s wall"}
 
@@ -458,7 +491,7 @@ def cpu_baseline(b, tree, budget_s, logged=False):
         el = time.perf_counter() - t0
         if el >= budget_s or calls >= 10000:
             break
-    return {"value": round(b.rows * calls / el, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
+    return {"value": round(b.rows * calls / el, 2), "unit": "tokens/s", "cores": oracle.max_threads(), "cpu": cpu_model(),
             "kind": "oracle",
             "sample": f"{calls} whole calls of the same workload ({b.rows} rows each), fp64, "
                       f"{el:.1f} s wall"}
