@@ -438,12 +438,13 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         float *dst = (A.mode == MODE_STEP)
                          ? A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off
                          : A.state_snap + ((size_t)row * A.hv + h) * head_elems + lane_off;
-        // snapshots are streamed out (non-temporal): nothing in this launch
-        // rereads them except a tree's parent reload
+        // ordinary (cached) stores: in back-to-back launches they measured
+        // slightly ahead of non-temporal ones (a tree's parent reload finds
+        // the snapshot in the cache)
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const f4v val = {m[i].x, m[i].y, m[i].z, m[i].w};
-            __builtin_nontemporal_store(val, reinterpret_cast<f4v *>(dst + (size_t)i * A.dv));
+            *reinterpret_cast<f4v *>(dst + (size_t)i * A.dv) = val;
         }
         prev = t;
     }
