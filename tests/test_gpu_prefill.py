@@ -77,6 +77,19 @@ def test_prefill_2b_layer():
     check(b, out, tail, state)
 
 
+@pytest.mark.parametrize("hk,hv", [(2, 4), (1, 4), (2, 12)])
+def test_prefill_value_heads_per_key_head(hk, hv):
+    """Two and four value heads a key head (the per-chunk kernel then takes
+    two value heads a workgroup) and six (three a workgroup, two workgroups a
+    key head)."""
+    shape = gi.Shape(hk=hk, hv=hv, dk=128, dv=128)
+    lengths = [70, 5, 130]
+    b = gi.make_batch(shape, lengths, seed=35 + hv)
+    announce(f"prefill hk={hk} hv={hv} {lengths}")
+    out, tail, state = run_prefill(b)
+    check(b, out, tail, state)
+
+
 def test_prefill_with_empty_prompt():
     lengths = [70, 0, 33]
     b = gi.make_batch(SMALL_27B_HEADS, lengths, seed=34)

@@ -749,9 +749,16 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 
         // rows [16 wave, 16 wave + 16) of W M0 and Q' M0, over all 128 state rows
         f4v aU = {0.f, 0.f, 0.f, 0.f}, aO = {0.f, 0.f, 0.f, 0.f};
+        // the wave's B operands of all eight k-steps, read from LDS together
+        // before the products (read one k-step at a time, each wait stalls the
+        // matrix core)
+        f4v mvs[8];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) mvs[kb] = lds4(Ms + g4 * kMsG + l16 * kMsN + 4 * kb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            const f4v mv = lds4(Ms + g4 * kMsG + l16 * kMsN + 4 * kb);
+            const f4v mv = mvs[kb];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 aU = mfma_f32(bfe2(ww[kb], i), mv[i], aU);
@@ -793,9 +800,14 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         // M <- e^{gamma_L} M + K~^T U on this wave's rows, then into Ms
 #pragma unroll
         for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
+        // U's four k-steps from LDS together, as for M0 above
+        f4v uvs[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) uvs[m] = lds4(Us + g4 * kUsG + l16 * kUsN + 4 * m);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const f4v uv = lds4(Us + g4 * kUsG + l16 * kUsN + 4 * m);
+            const f4v uv = uvs[m];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
