@@ -240,6 +240,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(b, tree, args.cpu_seconds, logged=args.log)
 
+    # the instantiation that runs: dk = 128, logged or recording
+    row_kernel = f"rows_kernel<{shape.dk}, {'true' if args.log else 'false'}>"
     line = {
         "metric": "GDN layer tokens/s and achieved HBM GB/s at 16 streams x 16-row verify",
         "value": round(tokens_per_s, 1),
@@ -268,8 +270,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(f"rows_kernel<128>/{args.workload}" + ("_log" if args.log else "")),
-            "kernel": "rows_kernel<128>",
+            "traffic": measured_traffic(f"{row_kernel}/{args.workload}" + ("_log" if args.log else "")),
+            "kernel": row_kernel,
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "cpu_baseline": cpu,

@@ -71,6 +71,27 @@ int heads_per_block(int r, int dv)
     return best;
 }
 
+// Workgroups of a verify pass.  A launch with few streams would leave most
+// CUs idle and put every row's snapshot stores of a key head through one CU:
+// then each value head gets its own workgroups, cs of them sharing its dv/32
+// column tiles, as many as keep the launch within the chip's 256 CUs.  The
+// per-lane arithmetic is the same for every split, so results do not depend
+// on it.  Otherwise the widest workgroups heads_per_block allows.
+void split_columns(gdn::RowsArgs &A, int n_streams)
+{
+    const int tiles = A.dv / 32;
+    A.vpw = heads_per_block(A.r, A.dv);
+    A.cs = 1;
+    if (getenv("LIBGDN_HEADS_PER_BLOCK")) return;
+    for (int cs = tiles; cs >= 2; cs /= 2) {
+        if (tiles % cs == 0 && (long long)n_streams * A.hv * cs <= 256) {
+            A.vpw = 1;
+            A.cs = cs;
+            return;
+        }
+    }
+}
+
 gdn::RowsArgs rows_args(const gdn_shape *s, const gdn_params *p)
 {
     gdn::RowsArgs A = {};
@@ -80,6 +101,8 @@ gdn::RowsArgs rows_args(const gdn_shape *s, const gdn_params *p)
     A.dv = s->dv;
     A.C = 2 * s->hk * s->dk + s->hv * s->dv;
     A.r = s->hv / s->hk;
+    A.vpw = 1;
+    A.cs = 1;
     A.conv_w = p->conv_w;
     A.a_log = p->a_log;
     A.dt_bias = p->dt_bias;
@@ -141,7 +164,7 @@ int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
         REQUIRE_PTR(state_snap);
     }
     gdn::RowsArgs A = rows_args(shape, params);
-    A.vpw = heads_per_block(A.r, A.dv);
+    split_columns(A, n_streams);
     A.n_streams = n_streams;
     A.total_rows = total_rows;
     A.max_rows = max_rows;
@@ -160,7 +183,7 @@ int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
     A.log_alpha = po.log_alpha;
     A.log_delta = po.log_delta;
     A.log_key = po.log_key;
-    if ((long long)n_streams * A.hk * (A.r / A.vpw) > 0x7fffffffLL)
+    if ((long long)n_streams * A.hk * (A.r / A.vpw) * A.cs > 0x7fffffffLL)
         return fail(GDN_EUNSUPPORTED, "too many streams for one launch");
     if (gdn::rows_lds_bytes(A) > gdn::kRowsMaxLds)
         return fail(GDN_EUNSUPPORTED, "window needs %zu bytes of LDS", gdn::rows_lds_bytes(A));
@@ -214,6 +237,7 @@ int gdn_conv_step(const gdn_shape *shape, const gdn_params *params, int32_t n_st
     REQUIRE_PTR(out);
     gdn::RowsArgs A = rows_args(shape, params);
     A.vpw = A.r;  // one workgroup per key head: it alone reads and rewrites those tail channels
+    A.cs = 1;
     A.n_streams = n_streams;
     A.total_rows = n_streams;
     A.max_rows = 1;

@@ -84,6 +84,11 @@ __device__ __forceinline__ float sum_wave(float x)
     return sum_rows4(x);
 }
 
+// Wait until every vector memory operation of the wave has completed
+// (s_waitcnt vmcnt(0), expcnt and lgkmcnt left alone).  A real waitcnt
+// instruction, which the compiler's own wait insertion takes into account.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for
 // every outstanding global load and store of the thread (its fence covers
 // global memory), which would hold each barrier on loads and stores in flight.

@@ -18,6 +18,7 @@ struct RowsArgs {
     int32_t hk, hv, dk, dv, C;
     int32_t r;          // value heads per key head
     int32_t vpw;        // value heads handled by one workgroup (divides r)
+    int32_t cs;         // workgroups sharing a value head's dv/32 column tiles (1 unless vpw == 1)
     int32_t n_streams, total_rows, max_rows;
     int32_t mode;
     const int32_t *row_start;  // [n+1] (unused in MODE_STEP)

@@ -1,7 +1,8 @@
 // Row kernels of libgdn: one-row steps, verify windows and verify trees of the
 // gated-delta-rule mixer, plus the commit copy.  gfx950 (CDNA4), wave64.
 //
-// One workgroup serves one stream and `vpw` value heads of one key head.
+// One workgroup serves one stream and `vpw` value heads of one key head; in a
+// launch too small to fill the chip, a share of one value head's column tiles.
 //
 //   prologue  the raw bf16 rows of the window and the stream's tail (only the
 //             workgroup's channels) and the conv weights are staged in LDS
@@ -56,9 +57,11 @@ __device__ __forceinline__ int global_channel(const RowsArgs &A, int dk, int kh,
     return 2 * A.hk * dk + h0 * A.dv + (ch - 2 * dk);
 }
 
-template <int DK>
+template <int DK, bool LOG>
 __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 {
+    // LOG: a logged window or tree (LOG), a template argument so that the
+    // recording stores in the row loop carry no branch
     constexpr int R = DK / 8;  // state rows held by one lane
     extern __shared__ float smem[];
 
@@ -68,6 +71,8 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     const int wave = tid >> 6;
     const int groups = A.r / A.vpw;
     int bid = blockIdx.x;
+    const int part = bid % A.cs;   // which share of the head's column tiles
+    bid /= A.cs;
     const int g = bid % groups;
     bid /= groups;
     const int kh = bid % A.hk;
@@ -95,7 +100,7 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     float4 *wl = reinterpret_cast<float4 *>(act + mr * nch);        // [nch] conv weights
     uint16_t *raw = reinterpret_cast<uint16_t *>(wl + nch);         // [3 + mr][nch] raw bf16 rows
     float *dlog = reinterpret_cast<float *>(raw + (3 + mr) * nch);  // [mr][vpw][dv] writes (logged)
-    float *galpha = dlog + (A.logged ? mr * A.vpw * A.dv : 0);      // [mr][vpw]
+    float *galpha = dlog + (LOG ? mr * A.vpw * A.dv : 0);      // [mr][vpw]
     float *gbeta = galpha + mr * A.vpw;                             // [mr][vpw]
     int *anc = reinterpret_cast<int *>(gbeta + mr * A.vpw);         // [mr][4]
     int *order = anc + mr * 4;                                      // [mr] processing order
@@ -104,13 +109,17 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     int *bad = pmask + mr;
 
     // ---- this wave's tile of the state
-    // Waves past the row loop's (vpw value heads of dv/32 waves each) only
-    // help with the prologue; their tile index is clamped to a real one, so
-    // their state loads (never used) read addresses other waves read too.
-    const int waves_per_head = A.dv / 32;
-    const bool row_wave = wave < A.vpw * waves_per_head;
-    const int jl = min(wave / waves_per_head, A.vpw - 1);   // local value head
-    const int tile = row_wave ? wave - jl * waves_per_head : 0;
+    // The workgroup holds tiles [part * tpw, (part + 1) * tpw) of each of its
+    // value heads (cs workgroups share a head's dv / 32 tiles when a launch
+    // is too small to fill the chip otherwise; every lane's arithmetic is the
+    // same either way).  Waves past the row loop's (vpw value heads of tpw
+    // waves each) only help with the prologue; their tile index is clamped to
+    // a real one, so their state loads (never used) read addresses other
+    // waves read too.
+    const int tpw = A.dv / 32 / A.cs;
+    const bool row_wave = wave < A.vpw * tpw;
+    const int jl = min(wave / tpw, A.vpw - 1);   // local value head
+    const int tile = part * tpw + (row_wave ? wave - jl * tpw : 0);
     const int h = h0 + jl;
     const int c4 = lane & 7, grp = lane >> 3;
     const int col = tile * 32 + c4 * 4;
@@ -259,8 +268,9 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         }
     }
     // ---- tail snapshots: the tail after row t is (x_{t-2}, x_{t-1}, x_t);
-    // q/k channels are shared by the key head's workgroups, group 0 records them
-    if (A.mode != MODE_STEP && !A.logged) {
+    // q/k channels are shared by the key head's workgroups, group 0 records
+    // them; of the workgroups that share a head's columns, the first records
+    if (A.mode != MODE_STEP && !LOG && part == 0) {
         const int c_first = (g == 0) ? 0 : (2 * DK) / 8;
         const int cw = cpr - c_first;
         for (int idx = tid; idx < len * 3 * cw; idx += nthr) {
@@ -312,7 +322,7 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 
     // ---- the log's decays (this workgroup's value heads) and keys (the key
     // head's workgroup group 0)
-    if (A.logged) {
+    if (LOG && part == 0) {
         for (int idx = tid; idx < len * A.vpw; idx += nthr) {
             const int t = idx / A.vpw;
             A.log_alpha[(size_t)(r0 + t) * A.hv + h0 + (idx - t * A.vpw)] = galpha[idx];
@@ -328,22 +338,42 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 
     if (!row_wave) return;   // no barrier below
 
-    // ---- the recurrence, row after row, on the tile held in registers
+    // The state tile has arrived before the loop starts.  The memory counter
+    // also counts stores: left to the compiler, the waits for the tile's loads
+    // would sit at the loop's merge point and hold every row until the last
+    // row's snapshot stores had completed.
+    wait_vmem();
+
+    // ---- the recurrence, row after row, on the tile held in registers.  A
+    // tree reads each row's index and parent from LDS one row ahead; a chain
+    // has them in closed form (row k, parent k - 1).
+    const bool tree_order = A.mode == MODE_TREE;
     int prev = -1;
+    int t = tree_order ? order[0] : 0;
+    int p = tree_order ? anc[t * 4] : -1;
     for (int k = 0; k < len; ++k) {
-        const int t = order[k];
-        const int p = anc[t * 4];
+        const int kn = min(k + 1, len - 1);
+        const int t_next = tree_order ? order[kn] : kn;
+        const int p_next = tree_order ? anc[t_next * 4] : kn - 1;
         if (p != prev) {
             // a tree row whose parent is not the row just done: reload the
             // parent's state (the stream's own state for p == -1).  Recorded:
             // the parent's snapshot, at the addresses this lane itself stored.
             // Logged: the stream's state, then the parent's path replayed.
-            const float *src = (p < 0 || A.logged)
+            const float *src = (p < 0 || LOG)
                                    ? st_in_head
                                    : A.state_snap + ((size_t)(r0 + p) * A.hv + h) * head_elems + lane_off;
+            // the address is formed anew here: kept from the first load of the
+            // tile, its 16 row addresses would be held (and spilled) through
+            // the prologue
+            asm volatile("" : "+v"(src));
 #pragma unroll
             for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(src + (size_t)i * A.dv);
-            if (A.logged && p >= 0) {
+            // the loads complete inside the reload, so that rows without one
+            // do not wait: a replay uses every loaded row at once, otherwise
+            // an explicit wait
+            if (!LOG || p < 0) wait_vmem();
+            if (LOG && p >= 0) {
                 const int path = pmask[p] | (1 << p);
                 for (int j = 0; j <= p; ++j) {
                     if (!((path >> j) & 1)) continue;
@@ -397,6 +427,15 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         d.y = be * (vv.y - al * u.y);
         d.z = be * (vv.z - al * u.z);
         d.w = be * (vv.w - al * u.w);
+        // the recorded state (a snapshot, or the stream's state in place for a
+        // step) leaves with ordinary (cached) stores, each state row as soon
+        // as it is updated, so the stores issue among the row's arithmetic
+        // (non-temporal stores measured slower back to back, and a tree's
+        // parent reload finds the snapshot in the cache)
+        const int row = r0 + t;
+        float *dst = (A.mode == MODE_STEP)
+                         ? A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off
+                         : A.state_snap + ((size_t)row * A.hv + h) * head_elems + lane_off;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < R; i += 4) {
@@ -415,6 +454,10 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
                 o.y = fmaf(me.y, qq[e], o.y);
                 o.z = fmaf(me.z, qq[e], o.z);
                 o.w = fmaf(me.w, qq[e], o.w);
+                if (!LOG) {
+                    const f4v val = {me.x, me.y, me.z, me.w};
+                    *reinterpret_cast<f4v *>(dst + (size_t)(i + e) * A.dv) = val;
+                }
             }
         }
         o.x = sum_rows8(o.x);
@@ -422,31 +465,19 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         o.z = sum_rows8(o.z);
         o.w = sum_rows8(o.w);
 
-        const int row = r0 + t;
         if (grp == 0)
             *reinterpret_cast<float4 *>(A.out + ((size_t)row * A.hv + h) * A.dv + col) = o;
-        if (A.logged) {
+        if (LOG) {
             // the write: to the log, and to LDS for a later replay by this
             // wave (every lane group holds the same delta)
             if (grp == 0) {
                 *reinterpret_cast<float4 *>(A.log_delta + ((size_t)row * A.hv + h) * A.dv + col) = d;
                 *reinterpret_cast<float4 *>(dlog + (t * A.vpw + jl) * A.dv + col) = d;
             }
-            prev = t;
-            continue;
-        }
-        float *dst = (A.mode == MODE_STEP)
-                         ? A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off
-                         : A.state_snap + ((size_t)row * A.hv + h) * head_elems + lane_off;
-        // ordinary (cached) stores: in back-to-back launches they measured
-        // slightly ahead of non-temporal ones (a tree's parent reload finds
-        // the snapshot in the cache)
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const f4v val = {m[i].x, m[i].y, m[i].z, m[i].w};
-            *reinterpret_cast<f4v *>(dst + (size_t)i * A.dv) = val;
         }
         prev = t;
+        t = t_next;
+        p = p_next;
     }
 }
 
@@ -573,13 +604,13 @@ __global__ void __launch_bounds__(256) replay_kernel(const ReplayArgs A)
 
 }  // namespace
 
-// The row loop needs 64 * vpw * dv/32 threads.  When the launch has no more
+// The row loop needs 64 * vpw * dv/32/cs threads.  When the launch has no more
 // workgroups than the chip has CUs (256), each gets at least 512: the extra
 // waves take part in the prologue (staging, conv, norms) and then leave.
 int rows_block_threads(const RowsArgs &A)
 {
-    const long long wgs = (long long)A.n_streams * A.hk * (A.r / A.vpw);
-    const int need = 64 * A.vpw * (A.dv / 32);
+    const long long wgs = (long long)A.n_streams * A.hk * (A.r / A.vpw) * A.cs;
+    const int need = 64 * A.vpw * (A.dv / 32 / A.cs);
     return wgs <= 256 ? max(need, 512) : need;
 }
 
@@ -597,29 +628,29 @@ size_t rows_lds_bytes(const RowsArgs &A)
 
 namespace {
 // Dynamic LDS above the 64 KiB default has to be allowed per kernel once.
-template <int DK>
-hipError_t allow_lds()
+template <int DK, bool LOG>
+hipError_t launch_rows_as(const RowsArgs &A, dim3 grid, dim3 block, size_t lds, hipStream_t stream)
 {
-    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&rows_kernel<DK>),
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&rows_kernel<DK, LOG>),
                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
                                                     (int)kRowsMaxLds);
-    return e;
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((rows_kernel<DK, LOG>), grid, block, lds, stream, A);
+    return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_rows(const RowsArgs &A, hipStream_t stream)
 {
-    const dim3 grid((unsigned)A.n_streams * A.hk * (A.r / A.vpw));
+    const dim3 grid((unsigned)A.n_streams * A.hk * (A.r / A.vpw) * A.cs);
     const dim3 block(rows_block_threads(A));
     const size_t lds = rows_lds_bytes(A);
     if (lds > kRowsMaxLds) return hipErrorInvalidValue;
-    const hipError_t e = (A.dk == 128) ? allow_lds<128>() : allow_lds<64>();
-    if (e != hipSuccess) return e;
     if (A.dk == 128)
-        hipLaunchKernelGGL(rows_kernel<128>, grid, block, lds, stream, A);
-    else
-        hipLaunchKernelGGL(rows_kernel<64>, grid, block, lds, stream, A);
-    return hipGetLastError();
+        return A.logged ? launch_rows_as<128, true>(A, grid, block, lds, stream)
+                        : launch_rows_as<128, false>(A, grid, block, lds, stream);
+    return A.logged ? launch_rows_as<64, true>(A, grid, block, lds, stream)
+                    : launch_rows_as<64, false>(A, grid, block, lds, stream);
 }
 
 hipError_t launch_commit(const CommitArgs &A, hipStream_t stream)
