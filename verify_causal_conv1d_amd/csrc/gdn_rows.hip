@@ -113,9 +113,8 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     // value heads (cs workgroups share a head's dv / 32 tiles when a launch
     // is too small to fill the chip otherwise; every lane's arithmetic is the
     // same either way).  Waves past the row loop's (vpw value heads of tpw
-    // waves each) only help with the prologue; their tile index is clamped to
-    // a real one, so their state loads (never used) read addresses other
-    // waves read too.
+    // waves each) only help with the prologue and record the tails; their
+    // tile index is clamped to a real one and they load no state.
     const int tpw = A.dv / 32 / A.cs;
     const bool row_wave = wave < A.vpw * tpw;
     const int jl = min(wave / tpw, A.vpw - 1);   // local value head
@@ -130,19 +129,31 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     // ---- parents and the three nearest ancestors of every row.  anc[t][0]
     // is the parent (whose state row t starts from); anc[t][d] is the source
     // of x_{t-d}: a local row >= 0, or -1, -2, -3 for tail rows 2, 1, 0.
-    if (tid == 0) *bad = 0;
-    if (tid < len) anc[tid * 4] = (A.mode == MODE_TREE) ? A.parent[r0 + tid] : tid - 1;
-    lds_barrier();
-    if (tid < len && (anc[tid * 4] < -1 || anc[tid * 4] >= tid)) *bad = 1;
-    lds_barrier();
-    if (*bad) return;
-    if (tid < len) {
-        int i = tid;
+    // A chain has them in closed form (t - 1, then t - d), with its row order
+    // and ancestor masks, written without a barrier; a tree's parents are
+    // checked and walked.
+    const bool tree = A.mode == MODE_TREE;
+    if (tree) {
+        if (tid == 0) *bad = 0;
+        if (tid < len) anc[tid * 4] = A.parent[r0 + tid];
+        lds_barrier();
+        if (tid < len && (anc[tid * 4] < -1 || anc[tid * 4] >= tid)) *bad = 1;
+        lds_barrier();
+        if (*bad) return;
+        if (tid < len) {
+            int i = tid;
 #pragma unroll
-        for (int d = 1; d <= 3; ++d) {
-            i = (i >= 0) ? anc[i * 4] : i - 1;
-            anc[tid * 4 + d] = i;
+            for (int d = 1; d <= 3; ++d) {
+                i = (i >= 0) ? anc[i * 4] : i - 1;
+                anc[tid * 4 + d] = i;
+            }
         }
+    } else if (tid < len) {
+        anc[tid * 4] = tid - 1;
+#pragma unroll
+        for (int d = 1; d <= 3; ++d) anc[tid * 4 + d] = tid - d;
+        order[tid] = tid;
+        pmask[tid] = (1 << tid) - 1;
     }
     // Processing order.  A chain runs in row order.  A tree runs in depth-
     // first preorder (children by increasing index): every row still follows
@@ -150,8 +161,8 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     // leaf, so the parent state is re-read from its snapshot (leaves - 1)
     // times instead of once for every row whose parent is not the row
     // before it.  Each row's arithmetic is the same in any order.
-    if (tid == 0) {
-        if (A.mode == MODE_TREE) {
+    if (tree && tid == 0) {
+        {
             // subtree sizes (parents have smaller indices than children) ...
             for (int i = 0; i < len; ++i) sub[i] = 1;
             for (int i = len - 1; i > 0; --i)
@@ -172,8 +183,6 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
                 order[pos] = i;
                 sub[i] = pos + 1;   // from now on: this row's next free slot
             }
-        } else {
-            for (int i = 0; i < len; ++i) order[i] = i;
         }
         for (int i = 0; i < len; ++i) {
             const int p = anc[i * 4];
@@ -246,10 +255,13 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         }
     }
 
-    // ---- the state tile: its loads stay in flight through the prologue
+    // ---- the state tile (row waves only): its loads stay in flight through
+    // the prologue
     float4 m[R];
+    if (row_wave) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
+        for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
+    }
     lds_barrier();
 
     // ---- conv + SiLU of every (row, channel), from the staged rows; a thread
@@ -269,11 +281,15 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     }
     // ---- tail snapshots: the tail after row t is (x_{t-2}, x_{t-1}, x_t);
     // q/k channels are shared by the key head's workgroups, group 0 records
-    // them; of the workgroups that share a head's columns, the first records
-    if (A.mode != MODE_STEP && !LOG && part == 0) {
+    // them; of the workgroups that share a head's columns, the first records.
+    // With helper waves these leave after the norms, from the helpers alone.
+    const bool record_tails = A.mode != MODE_STEP && !LOG && part == 0;
+    const int row_threads = 64 * A.vpw * tpw;
+    const bool late_tails = nthr > row_threads;
+    auto tail_snaps = [&](int first, int stride) {
         const int c_first = (g == 0) ? 0 : (2 * DK) / 8;
         const int cw = cpr - c_first;
-        for (int idx = tid; idx < len * 3 * cw; idx += nthr) {
+        for (int idx = first; idx < len * 3 * cw; idx += stride) {
             const int tj = idx / cw;
             const int lc = (c_first + idx - tj * cw) * 8;
             const int t = tj / 3, j = tj - t * 3;
@@ -282,6 +298,9 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
             *reinterpret_cast<uint4 *>(A.tail_snap + ((size_t)(r0 + t) * 3 + j) * C + gc) =
                 *reinterpret_cast<const uint4 *>(raw + src_row * nch + lc);
         }
+    };
+    if (record_tails && !late_tails) {
+        tail_snaps(tid, nthr);
     } else if (A.mode == MODE_STEP) {
         // one-row step: the new tail replaces the old one in place.  The old
         // tail is staged in LDS, and with one workgroup per key head in this
@@ -336,7 +355,10 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         }
     }
 
-    if (!row_wave) return;   // no barrier below
+    if (!row_wave) {   // no barrier below
+        if (record_tails && late_tails) tail_snaps(tid - row_threads, nthr - row_threads);
+        return;
+    }
 
     // The state tile has arrived before the loop starts.  The memory counter
     // also counts stores: left to the compiler, the waits for the tile's loads
