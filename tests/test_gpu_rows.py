@@ -168,6 +168,36 @@ def test_packed_equals_solo_bitwise():
         assert np.array_equal(bits16(st), bits16(tsnap[rows]))
 
 
+@pytest.mark.parametrize("name", ["window2b", "verify27b"])
+def test_workgroup_split_is_bitwise_invariant(name, monkeypatch):
+    """A small launch gives each value head several workgroups (each a share
+    of its column tiles); LIBGDN_HEADS_PER_BLOCK forces the plain one-workgroup-
+    per-head layout.  Both must give the same bits, recorded and logged."""
+    shape, lengths, kw = gi.workload(name)
+    b = gi.make_batch(shape, lengths[:1], **kw)   # one stream: the launch that splits
+    d = device_batch(b)
+    announce(f"workgroup split {name} lengths={lengths[:1]}")
+    runs = []
+    for env in (None, "1"):
+        if env is None:
+            monkeypatch.delenv("LIBGDN_HEADS_PER_BLOCK", raising=False)
+        else:
+            monkeypatch.setenv("LIBGDN_HEADS_PER_BLOCK", env)
+        out, tsnap, ssnap = run_window(b, d=d)
+        o_l = torch.full_like(out, float("nan"))
+        la = torch.full((b.rows, shape.hv), float("nan"), device="cuda")
+        ld = torch.full((b.rows, shape.hv, shape.dv), float("nan"), device="cuda")
+        lk = torch.full((b.rows, shape.hk, shape.dk), float("nan"), device="cuda")
+        gdn.recur_log(shape, d["params"], d["row_start"], d["qkv"], d["a"], d["b"], d["tail"], d["state"],
+                      o_l, la, ld, lk)
+        torch.cuda.synchronize()
+        runs.append((out, tsnap, ssnap, o_l, la, ld, lk))
+    for x, y in zip(*runs):
+        bx = bits16(x) if x.dtype == torch.bfloat16 else bits32(x)
+        by = bits16(y) if y.dtype == torch.bfloat16 else bits32(y)
+        assert np.array_equal(bx, by)
+
+
 def test_empty_streams_and_zero_rows():
     shape = gi.QWEN_27B
     b = gi.make_batch(shape, [3, 0, 16, 0, 1], seed=5)
