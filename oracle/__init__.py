@@ -15,3 +15,4 @@ from .gdn_oracle import (  # noqa: F401
     OracleShape, lib, gates, conv_silu, raw_recurrence, window, tree, prefill, commit,
     replay, commit_replay, max_threads,
 )
+from . import inproj  # noqa: F401  (the affine 4-bit in-projection, numpy fp64)

@@ -17,7 +17,8 @@ standard deviation ``s``):
 * ``A_log`` ~ U(0, 2.7) fp32 ``[hv]`` (the "long memory" variant draws
   U(-7, -4), which keeps the per-row decay near 1);
 * ``dt_bias`` ~ N(0, 0.1) fp32 ``[hv]``;
-* recurrent state ~ N(0, 0.05), fp32, ``[n][hv][dk][dv]``.
+* recurrent state ~ N(0, 0.05), fp32, ``[n][hv][dk][dv]``;
+* the in-projection's hidden rows, codes, scales and biases (``make_inproj``).
 """
 from __future__ import annotations
 
@@ -194,6 +195,86 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """The raw 16-bit patterns of a bf16 tensor, as uint16 (a copy)."""
     assert t.dtype == torch.bfloat16
     return t.contiguous().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+# ---- the affine 4-bit in-projection before the mixer: hidden rows x -> the
+# mixer's packed rows qkv and its gate inputs a and b.  Weights come in MLX's
+# affine 4-bit form: per output feature n and group g of ``group`` consecutive
+# inputs, a bf16 scale and a bf16 bias, and a 4-bit code per weight, eight codes
+# a 32-bit word (code j of a word in bits [4j, 4j + 4), word w of a row holding
+# inputs 8w .. 8w + 7).  Output features are ordered [qkv (C) | a (hv) | b (hv)].
+HIDDEN_2B = 2048     # synthetic hidden sizes of the 2B-like and 27B-like layers
+HIDDEN_27B = 5120
+
+
+@dataclass
+class Inproj:
+    shape: Shape
+    hidden: int
+    group: int
+    x: torch.Tensor        # bf16 [R][hidden]
+    wq: torch.Tensor       # int32 [N][hidden/8]: the packed codes' 32-bit patterns
+    scales: torch.Tensor   # bf16 [N][hidden/group]
+    biases: torch.Tensor   # bf16 [N][hidden/group]
+
+    @property
+    def rows(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def features(self) -> int:
+        return inproj_features(self.shape)
+
+
+def inproj_features(shape: Shape) -> int:
+    """Output features of the in-projection: C + 2 hv."""
+    return shape.channels + 2 * shape.hv
+
+
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes [N][K] (values 0..15) into int32 words [N][K/8]."""
+    c = codes.astype(np.uint32).reshape(codes.shape[0], -1, 8)
+    words = np.zeros(c.shape[:2], np.uint32)
+    for j in range(8):
+        words |= c[:, :, j] << np.uint32(4 * j)
+    return words.view(np.int32)
+
+
+def make_inproj(shape: Shape, rows: int, hidden: int, group: int, seed: int) -> Inproj:
+    """Draw one in-projection call: x ~ N(0, 1); codes uniform in 0..15; per
+    group a scale exp(N(0, 0.2)) / (4.6 sqrt(hidden)) and a bias of about
+    -7.5 scales (so that the weights are centred, with a standard deviation
+    near 1 / sqrt(hidden) and outputs near N(0, 1))."""
+    gen = torch.Generator().manual_seed(int(seed))
+    n = inproj_features(shape)
+    ng = hidden // group
+    x = _normal(gen, (rows, hidden), 1.0, torch.bfloat16)
+    codes = torch.randint(0, 16, (n, hidden), generator=gen).numpy()
+    scale = torch.exp(_normal(gen, (n, ng), 0.2)) / (4.6 * hidden ** 0.5)
+    bias = -7.5 * scale * (1.0 + _normal(gen, (n, ng), 0.1))
+    return Inproj(shape=shape, hidden=hidden, group=group, x=x,
+                  wq=torch.from_numpy(pack_codes(codes)),
+                  scales=scale.to(torch.bfloat16), biases=bias.to(torch.bfloat16))
+
+
+def inproj_workload(name: str, seed: Optional[int] = None):
+    """The in-projection's workloads, by name: (shape, rows, hidden, group, seed).
+
+    * ``inproj_decode27b``  16 rows (one decode row of 16 streams), 27B-like layer
+    * ``inproj_verify27b``  256 rows (16 streams x 16-row windows), 27B-like layer
+    * ``inproj_prefill27b`` 8,306 rows (the four prompts of the prompt pass)
+    * ``inproj_window2b``   16 rows, 2B-like layer
+    """
+    table = {
+        "inproj_decode27b": (QWEN_27B, 16, HIDDEN_27B),
+        "inproj_verify27b": (QWEN_27B, 256, HIDDEN_27B),
+        "inproj_prefill27b": (QWEN_27B, 8306, HIDDEN_27B),
+        "inproj_window2b": (QWEN_2B, 16, HIDDEN_2B),
+    }
+    shape, rows, hidden = table[name]
+    if seed is None:
+        seed = 1234 + 10 + list(table).index(name)
+    return shape, rows, hidden, 64, seed
 
 
 # Named workloads.  Each returns (shape, lengths, extra keyword arguments).
