@@ -223,6 +223,29 @@ int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_
                         size_t workspace_bytes, void *stream);
 
 /*
+ * The in-projection before the mixer: its packed rows qkv and gate inputs a,
+ * b from hidden rows x, y = x W^T, with W in affine 4-bit form (the
+ * projections of the MLX affine 4-bit checkpoint run through affine-4
+ * kernels: page "perf(qwen3_5 cuda): deliver the first token before
+ * drafting", note on that checkpoint; the format read as MLX's affine
+ * quantisation).  Output features are [qkv (C) | a (hv) | b (hv)], C =
+ * 2*hk*dk + hv*dv; weight w[n][k] = scales[n][k/group] * q[n][k] +
+ * biases[n][k/group].
+ *   x      [rows][hidden] bf16, device, 16-byte aligned
+ *   wq     [C + 2 hv][hidden/8] packed codes, device, 16-byte aligned: code j
+ *          of word w (bits 4j..4j+3) is q[n][8w + j]
+ *   scales, biases [C + 2 hv][hidden/group] bf16, device
+ *   qkv    [rows][C] bf16 out (16-byte aligned); a, b [rows][hv] bf16 out
+ * hidden must be a multiple of 128 and group_size 32, 64 or 128
+ * (GDN_EUNSUPPORTED otherwise).  Weights are rounded to bf16 before the
+ * matrix-core products, which accumulate in fp32; outputs are rounded to
+ * bf16.  rows == 0 does nothing.
+ */
+int gdn_inproj_affine4(const gdn_shape *shape, int32_t rows, int32_t hidden, int32_t group_size,
+                       const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                       const uint16_t *biases, uint16_t *qkv, uint16_t *a, uint16_t *b, void *stream);
+
+/*
  * Host-side check of a window or tree layout (HOST copies of row_start and,
  * for trees, parent; parent may be NULL for chains).  Returns GDN_OK or
  * GDN_EINVAL with gdn_last_error() naming the first broken rule.

@@ -28,7 +28,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -177,6 +177,24 @@ def test_prefill_refusals(L):
     assert call(wsb=1) == gdn.GDN_EWORKSPACE
     assert call(ws=None) == gdn.GDN_EWORKSPACE
     assert call(ws=P_ODD) == gdn.GDN_EINVAL
+
+
+def test_inproj_refusals(L):
+    sh = _shape()
+
+    def call(rows=16, hidden=5120, group=64, x=P16, wq=P16, sc=P16, qkv=P16, a=P16, shape=sh):
+        return L.gdn_inproj_affine4(C.byref(shape), rows, hidden, group, x, wq, sc, P16, qkv, a, P16, None)
+    assert call(rows=-1) == gdn.GDN_EINVAL
+    assert call(hidden=5000) == gdn.GDN_EUNSUPPORTED and "hidden" in L.gdn_last_error().decode()
+    assert call(hidden=0) == gdn.GDN_EUNSUPPORTED
+    assert call(group=16) == gdn.GDN_EUNSUPPORTED and "group" in L.gdn_last_error().decode()
+    assert call(x=None) == gdn.GDN_EINVAL and "x" in L.gdn_last_error().decode()
+    assert call(wq=P_ODD) == gdn.GDN_EINVAL and "wq" in L.gdn_last_error().decode()
+    assert call(sc=None) == gdn.GDN_EINVAL
+    assert call(qkv=None) == gdn.GDN_EINVAL
+    assert call(a=None) == gdn.GDN_EINVAL
+    assert call(rows=0, x=None, wq=None, sc=None, qkv=None, a=None) == gdn.GDN_OK
+    assert call(shape=_shape(hv=47)) == gdn.GDN_EINVAL
 
 
 def test_prefill_workspace_bytes(L):

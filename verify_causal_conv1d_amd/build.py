@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_rows.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.hip", "gdn_rows.hip", "gdn_prefill.hip", "gdn_inproj.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

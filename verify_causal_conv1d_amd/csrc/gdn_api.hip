@@ -7,6 +7,7 @@
 
 #include "../../include/libgdn.h"
 #include "gdn_internal.h"
+#include "gdn_inproj.h"
 #include "gdn_prefill.h"
 
 namespace {
@@ -422,6 +423,45 @@ int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_
     P.out = out;
     P.workspace = workspace;
     return launched(gdn::launch_prefill(P, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_inproj_affine4(const gdn_shape *shape, int32_t rows, int32_t hidden, int32_t group_size,
+                       const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                       const uint16_t *biases, uint16_t *qkv, uint16_t *a, uint16_t *b, void *stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (rows < 0) return fail(GDN_EINVAL, "rows %d is negative", rows);
+    if (hidden <= 0 || hidden % 128 != 0)
+        return fail(GDN_EUNSUPPORTED, "hidden %d: a positive multiple of 128 is needed", hidden);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(GDN_EUNSUPPORTED, "group_size %d: 32, 64 or 128 is supported", group_size);
+    const long long features = 2LL * shape->hk * shape->dk + (long long)shape->hv * shape->dv + 2LL * shape->hv;
+    if ((long long)rows * hidden > 0x7fffffffLL || features * (hidden / 8) > 0x7fffffffLL)
+        return fail(GDN_EUNSUPPORTED, "projection too large for one call");
+    if (rows == 0) {
+        g_err[0] = '\0';
+        return GDN_OK;
+    }
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(wq);
+    if (!scales || !biases) return fail(GDN_EINVAL, "scales or biases is NULL");
+    REQUIRE_PTR(qkv);
+    if (!a || !b) return fail(GDN_EINVAL, "a or b is NULL");
+    gdn::InprojArgs A = {};
+    A.rows = rows;
+    A.hidden = hidden;
+    A.group = group_size;
+    A.channels = 2 * shape->hk * shape->dk + shape->hv * shape->dv;
+    A.hv = shape->hv;
+    A.x = x;
+    A.wq = wq;
+    A.scales = scales;
+    A.biases = biases;
+    A.qkv = qkv;
+    A.a = a;
+    A.b = b;
+    return launched(gdn::launch_inproj(A, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_check_layout(int32_t n_streams, int32_t total_rows, int32_t max_rows,

@@ -26,6 +26,7 @@ EXPORTED = (
     "gdn_status_name", "gdn_last_error", "gdn_channels", "gdn_conv_step", "gdn_recur_window",
     "gdn_recur_tree", "gdn_commit", "gdn_recur_log", "gdn_commit_replay",
     "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_check_layout",
+    "gdn_inproj_affine4",
 )
 
 
@@ -73,9 +74,10 @@ def lib():
             L.gdn_prefill_chunked.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P,
                                               C.c_size_t, P]
             L.gdn_check_layout.argtypes = [i32, i32, i32, P, P]
+            L.gdn_inproj_affine4.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P, P]
             for name in ("gdn_conv_step", "gdn_recur_window", "gdn_recur_tree", "gdn_commit",
                          "gdn_recur_log", "gdn_commit_replay", "gdn_prefill_chunked",
-                         "gdn_check_layout"):
+                         "gdn_check_layout", "gdn_inproj_affine4"):
                 getattr(L, name).restype = C.c_int
             _lib = L
     return _lib
@@ -248,6 +250,20 @@ def prefill_chunked(shape, params, seq_start, qkv, a, b, conv_tail, state, out, 
                                      _ptr(a), _ptr(b), _ptr(conv_tail), _ptr(state), _ptr(out),
                                      _ptr(workspace), workspace.numel(), _stream(qkv)),
            "gdn_prefill_chunked")
+
+
+def inproj_affine4(shape, x, wq, scales, biases, qkv, a, b, group: int):
+    """The affine 4-bit in-projection: qkv, a, b (bf16, written) from hidden
+    rows x (bf16 [R][hidden]), packed codes wq (int32 [C + 2 hv][hidden/8]) and
+    bf16 scales and biases ([C + 2 hv][hidden/group])."""
+    for t, dt, nm in ((x, torch.bfloat16, "x"), (wq, torch.int32, "wq"), (scales, torch.bfloat16, "scales"),
+                      (biases, torch.bfloat16, "biases"), (qkv, torch.bfloat16, "qkv"),
+                      (a, torch.bfloat16, "a"), (b, torch.bfloat16, "b")):
+        _dev(t, dt, nm)
+    sh = _shape(shape)
+    _check(lib().gdn_inproj_affine4(C.byref(sh), x.shape[0], x.shape[1], int(group), _ptr(x), _ptr(wq),
+                                    _ptr(scales), _ptr(biases), _ptr(qkv), _ptr(a), _ptr(b), _stream(x)),
+           "gdn_inproj_affine4")
 
 
 def check_layout(row_start, max_rows: int, total_rows: int, parent=None):
