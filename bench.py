@@ -109,7 +109,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify27b",
-                    choices=["verify27b", "tree27b", "ragged27b", "window2b", "step", "prefill27b"])
+                    choices=["verify27b", "tree27b", "ragged27b", "window2b", "step", "prefill27b",
+                             "inproj_decode27b", "inproj_verify27b", "inproj_prefill27b", "inproj_window2b"])
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of the calls (launch-bound workloads)")
     ap.add_argument("--log", action="store_true",
@@ -141,6 +142,8 @@ def main():
 
     if args.workload == "prefill27b":
         return bench_prefill(args, torch, gdn, gi, dev)
+    if args.workload.startswith("inproj_"):
+        return bench_inproj(args, torch, gdn, gi, dev)
     if args.workload == "step":
         return bench_step(args, torch, gdn, gi, dev)
 
@@ -442,6 +445,92 @@ def bench_prefill(args, torch, gdn, gi, dev):
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def inproj_work(shape, rows, hidden, group):
+    """Algorithmic bytes and bf16 matrix flops of one in-projection call: x in,
+    packed codes and bf16 scales and biases in, qkv, a, b out (bf16); two
+    flops a weight and row."""
+    n = shape.channels + 2 * shape.hv
+    nbytes = rows * hidden * 2 + n * hidden // 2 + n * (hidden // group) * 4 + rows * n * 2
+    return nbytes, 2 * rows * n * hidden
+
+
+def bench_inproj(args, torch, gdn, gi, dev):
+    """One step = one gdn_inproj_affine4 call (hidden rows -> qkv, a, b)."""
+    shape, rows, hidden, group, seed = gi.inproj_workload(args.workload)
+    t = gi.make_inproj(shape, rows, hidden, group, seed)
+    x = t.x.to(dev)
+    # the weights are repacked once, as at load time (not timed)
+    wq, sc, bi = gdn.inproj_pack(shape, t.wq.to(dev), t.scales.to(dev), t.biases.to(dev), group)
+    qkv = torch.empty((rows, shape.channels), dtype=torch.bfloat16, device=dev)
+    a = torch.empty((rows, shape.hv), dtype=torch.bfloat16, device=dev)
+    b = torch.empty((rows, shape.hv), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        gdn.inproj_affine4(shape, x, wq, sc, bi, qkv, a, b, group)
+
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    wall, avg_ms, med_ms = timed(torch, dev, step, args.steps, args.warmup)
+    cold_ms = cold_timed(torch, dev, step)
+    nbytes, flops = inproj_work(shape, rows, hidden, group)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFS * 1e12)
+    kernel = "inproj_small_kernel" if rows <= 32 else "inproj_large_kernel"
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / (avg_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(t_hbm / (avg_ms * 1e-3), 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / (avg_ms * 1e-3) / 1e12, 2),
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(t_mfma / (avg_ms * 1e-3), 4)}
+    roof.update({"traffic": measured_traffic(f"{kernel}/{args.workload}", "gdn_inproj.hip"), "kernel": kernel,
+                 "algorithmic_bytes_per_launch": nbytes, "flops_bf16_per_launch": flops})
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_inproj(t, args.cpu_seconds)
+    line = {
+        "metric": "GDN in-projection rows/s (affine 4-bit weights -> qkv, a, b)",
+        "value": round(rows * args.steps / wall, 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (4-bit affine weights, fp32 accumulation)", "data": "synthetic",
+        "config": {"workload": f"{rows} rows of hidden {hidden} -> qkv, a, b of the "
+                               f"{'27B' if shape.hv == 48 else '2B'}-like layer, group {group}",
+                   "rows": rows, "hidden": hidden, "features": shape.channels + 2 * shape.hv,
+                   "group": group, "seed": seed},
+        "kernel_ms_avg": round(avg_ms, 5), "kernel_ms_median": round(med_ms, 5),
+        "kernel_ms_cold_median": None if cold_ms is None else round(cold_ms, 5),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_inproj(t, budget_s):
+    """The oracle's fp64 projection on a bounded sample: the first 1, 2, 4, ...
+    rows of the same call, until about budget_s seconds."""
+    import oracle
+    from verify_causal_conv1d_amd import inputs as gi
+    xb = gi.bf16_bits(t.x)
+    wq, sb, bb = t.wq.numpy(), gi.bf16_bits(t.scales), gi.bf16_bits(t.biases)
+    rows, el, n = 0, 0.0, 1
+    while el < budget_s and n <= t.rows:
+        t0 = time.perf_counter()
+        oracle.inproj.project(xb[:n], wq, sb, bb, t.group)
+        el += time.perf_counter() - t0
+        rows += n
+        n *= 2
+    try:   # the BLAS threads numpy's product ran on
+        from threadpoolctl import threadpool_info
+        cores = max(i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas")
+    except (ImportError, ValueError):
+        cores = 1
+    return {"value": round(rows / el, 2), "unit": "rows/s", "cores": cores, "cpu": cpu_model(),
+            "kind": "oracle", "sample": f"the first 1, 2, 4, ... rows of the call ({rows} rows in all, "
+                                        f"weights dequantised each time), numpy fp64, {el:.1f} s wall"}
 
 
 def cpu_baseline_prefill(b, budget_s):

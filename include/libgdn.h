@@ -229,21 +229,37 @@ int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_
  * kernels: page "perf(qwen3_5 cuda): deliver the first token before
  * drafting", note on that checkpoint; the format read as MLX's affine
  * quantisation).  Output features are [qkv (C) | a (hv) | b (hv)], C =
- * 2*hk*dk + hv*dv; weight w[n][k] = scales[n][k/group] * q[n][k] +
- * biases[n][k/group].
+ * 2*hk*dk + hv*dv; weight w[n][k] = scale[n][k/group] * q[n][k] +
+ * bias[n][k/group].  Weights are repacked once (at load) into a tiled layout
+ * for these kernels: gdn_inproj_pack_affine4.
+ *
+ * gdn_inproj_padded_features: NP = 16 * ceil((C + 2 hv) / 16), or -1 for a
+ * bad shape.
+ *
+ * gdn_inproj_pack_affine4: MLX layout in, tiled layout out (device arrays,
+ * 16-byte aligned, all on `stream`):
+ *   wq     [C + 2 hv][hidden/8] packed codes: code j of word w (bits
+ *          4j..4j+3) is q[n][8w + j]
+ *   scales, biases [C + 2 hv][hidden/group] bf16
+ *   wq_tiled [NP * hidden / 8] words; scales_tiled, biases_tiled
+ *          [NP * hidden / group] bf16 (the padded features get zeros)
+ *
+ * gdn_inproj_affine4:
  *   x      [rows][hidden] bf16, device, 16-byte aligned
- *   wq     [C + 2 hv][hidden/8] packed codes, device, 16-byte aligned: code j
- *          of word w (bits 4j..4j+3) is q[n][8w + j]
- *   scales, biases [C + 2 hv][hidden/group] bf16, device
+ *   wq_tiled, scales_tiled, biases_tiled from gdn_inproj_pack_affine4
  *   qkv    [rows][C] bf16 out (16-byte aligned); a, b [rows][hv] bf16 out
  * hidden must be a multiple of 128 and group_size 32, 64 or 128
  * (GDN_EUNSUPPORTED otherwise).  Weights are rounded to bf16 before the
  * matrix-core products, which accumulate in fp32; outputs are rounded to
  * bf16.  rows == 0 does nothing.
  */
+int32_t gdn_inproj_padded_features(const gdn_shape *shape);
+int gdn_inproj_pack_affine4(const gdn_shape *shape, int32_t hidden, int32_t group_size, const uint32_t *wq,
+                            const uint16_t *scales, const uint16_t *biases, uint32_t *wq_tiled,
+                            uint16_t *scales_tiled, uint16_t *biases_tiled, void *stream);
 int gdn_inproj_affine4(const gdn_shape *shape, int32_t rows, int32_t hidden, int32_t group_size,
-                       const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
-                       const uint16_t *biases, uint16_t *qkv, uint16_t *a, uint16_t *b, void *stream);
+                       const uint16_t *x, const uint32_t *wq_tiled, const uint16_t *scales_tiled,
+                       const uint16_t *biases_tiled, uint16_t *qkv, uint16_t *a, uint16_t *b, void *stream);
 
 /*
  * Host-side check of a window or tree layout (HOST copies of row_start and,

@@ -196,6 +196,18 @@ def test_inproj_refusals(L):
     assert call(rows=0, x=None, wq=None, sc=None, qkv=None, a=None) == gdn.GDN_OK
     assert call(shape=_shape(hv=47)) == gdn.GDN_EINVAL
 
+    def pack(hidden=5120, group=64, wq=P16, wt=P16, st=P16):
+        return L.gdn_inproj_pack_affine4(C.byref(sh), hidden, group, wq, P16, P16, wt, st, P16, None)
+    assert pack(hidden=100) == gdn.GDN_EUNSUPPORTED
+    assert pack(group=256) == gdn.GDN_EUNSUPPORTED
+    assert pack(wq=None) == gdn.GDN_EINVAL
+    assert pack(wt=P_ODD) == gdn.GDN_EINVAL and "wq_tiled" in L.gdn_last_error().decode()
+    assert pack(st=None) == gdn.GDN_EINVAL
+    # features padded to a multiple of 16: 10240 + 96 at the 27B-like layer, 512 + 8 -> 528
+    assert L.gdn_inproj_padded_features(C.byref(sh)) == 10336
+    assert L.gdn_inproj_padded_features(C.byref(_shape(hk=2, hv=4, dk=64, dv=64))) == 528
+    assert L.gdn_inproj_padded_features(C.byref(_shape(hv=47))) == -1
+
 
 def test_prefill_workspace_bytes(L):
     sh = _shape()

@@ -30,7 +30,8 @@ def run(t: gi.Inproj):
     qkv = torch.full((t.rows, sh.channels), nan, dtype=torch.bfloat16, device=dev)
     a = torch.full((t.rows, sh.hv), nan, dtype=torch.bfloat16, device=dev)
     b = torch.full((t.rows, sh.hv), nan, dtype=torch.bfloat16, device=dev)
-    gdn.inproj_affine4(sh, t.x.to(dev), t.wq.to(dev), t.scales.to(dev), t.biases.to(dev), qkv, a, b, t.group)
+    wt, st, bt = gdn.inproj_pack(sh, t.wq.to(dev), t.scales.to(dev), t.biases.to(dev), t.group)
+    gdn.inproj_affine4(sh, t.x.to(dev), wt, st, bt, qkv, a, b, t.group)
     torch.cuda.synchronize()
     return torch.cat([qkv, a, b], dim=1).float().cpu().numpy().astype(np.float64)
 
@@ -107,7 +108,8 @@ def test_inproj_feeds_the_mixer():
     qkv = torch.empty((12, shape.channels), dtype=torch.bfloat16, device=dev)
     a = torch.empty((12, shape.hv), dtype=torch.bfloat16, device=dev)
     bb = torch.empty((12, shape.hv), dtype=torch.bfloat16, device=dev)
-    gdn.inproj_affine4(shape, t.x.to(dev), t.wq.to(dev), t.scales.to(dev), t.biases.to(dev), qkv, a, bb, 64)
+    wt, st, bt = gdn.inproj_pack(shape, t.wq.to(dev), t.scales.to(dev), t.biases.to(dev), 64)
+    gdn.inproj_affine4(shape, t.x.to(dev), wt, st, bt, qkv, a, bb, 64)
     params = gdn.LayerParams.from_host(b.params, dev)
     out = torch.empty((12, shape.hv, shape.dv), device=dev)
     ts = torch.empty((12, 3, shape.channels), dtype=torch.bfloat16, device=dev)

@@ -436,7 +436,7 @@ int gdn_inproj_affine4(const gdn_shape *shape, int32_t rows, int32_t hidden, int
         return fail(GDN_EUNSUPPORTED, "hidden %d: a positive multiple of 128 is needed", hidden);
     if (group_size != 32 && group_size != 64 && group_size != 128)
         return fail(GDN_EUNSUPPORTED, "group_size %d: 32, 64 or 128 is supported", group_size);
-    const long long features = 2LL * shape->hk * shape->dk + (long long)shape->hv * shape->dv + 2LL * shape->hv;
+    const long long features = gdn_inproj_padded_features(shape);
     if ((long long)rows * hidden > 0x7fffffffLL || features * (hidden / 8) > 0x7fffffffLL)
         return fail(GDN_EUNSUPPORTED, "projection too large for one call");
     if (rows == 0) {
@@ -462,6 +462,44 @@ int gdn_inproj_affine4(const gdn_shape *shape, int32_t rows, int32_t hidden, int
     A.a = a;
     A.b = b;
     return launched(gdn::launch_inproj(A, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_inproj_padded_features(const gdn_shape *shape)
+{
+    if (check_shape(shape)) return -1;
+    const int features = 2 * shape->hk * shape->dk + shape->hv * shape->dv + 2 * shape->hv;
+    return 16 * ((features + 15) / 16);
+}
+
+int gdn_inproj_pack_affine4(const gdn_shape *shape, int32_t hidden, int32_t group_size, const uint32_t *wq,
+                            const uint16_t *scales, const uint16_t *biases, uint32_t *wq_tiled,
+                            uint16_t *scales_tiled, uint16_t *biases_tiled, void *stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (hidden <= 0 || hidden % 128 != 0)
+        return fail(GDN_EUNSUPPORTED, "hidden %d: a positive multiple of 128 is needed", hidden);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(GDN_EUNSUPPORTED, "group_size %d: 32, 64 or 128 is supported", group_size);
+    const long long np = gdn_inproj_padded_features(shape);
+    if (np * (hidden / 8) > 0x7fffffffLL) return fail(GDN_EUNSUPPORTED, "projection too large for one call");
+    REQUIRE_PTR(wq);
+    if (!scales || !biases) return fail(GDN_EINVAL, "scales or biases is NULL");
+    REQUIRE_PTR(wq_tiled);
+    if (!scales_tiled || !biases_tiled) return fail(GDN_EINVAL, "scales_tiled or biases_tiled is NULL");
+    gdn::InprojPackArgs P = {};
+    P.hidden = hidden;
+    P.group = group_size;
+    P.channels = 2 * shape->hk * shape->dk + shape->hv * shape->dv;
+    P.hv = shape->hv;
+    P.blocks = (int)(np / 16);
+    P.wq = wq;
+    P.scales = scales;
+    P.biases = biases;
+    P.wq_tiled = wq_tiled;
+    P.scales_tiled = scales_tiled;
+    P.biases_tiled = biases_tiled;
+    return launched(gdn::launch_inproj_pack(P, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_check_layout(int32_t n_streams, int32_t total_rows, int32_t max_rows,

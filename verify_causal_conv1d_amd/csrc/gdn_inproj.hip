@@ -9,19 +9,29 @@
 // even) right before it enters v_mfma_f32_16x16x32_bf16, as MLX's own matrix
 // kernels do; products accumulate in fp32 and the outputs are rounded to bf16.
 //
-// Inputs go in chunks of 128.  Within a chunk, lane (l16, g4) of a wave owns
-// inputs [32 g4, 32 g4 + 32): four consecutive code words, one 16-byte load,
-// and in k-step s (0..3) it supplies inputs 32 g4 + 8 s .. + 8 of both
-// operands (A: row l16 of x, B: feature l16 of W), so that every input meets
-// its weight once.  Its 32 inputs lie in one group (group sizes 32, 64, 128),
-// so one scale and one bias serve the lane for the chunk.
+// The small kernel takes inputs in chunks of 128.  Within a chunk, lane
+// (l16, g4) of a wave owns inputs [32 g4, 32 g4 + 32): four consecutive code
+// words, one 16-byte load, and in k-step s (0..3) it supplies inputs
+// 32 g4 + 8 s .. + 8 of both operands (A: row l16 of x, B: feature l16 of W),
+// so that every input meets its weight once.  Those 32 inputs lie in one
+// group (group sizes 32, 64, 128): one scale and one bias serve the lane for
+// the chunk.  The large kernel expands weights the same way, 32 inputs of one
+// feature a thread, into LDS.
 //
-//   small  (rows <= 32): a workgroup is 16 features x 16 or 32 rows; its four
-//          waves take every fourth chunk and add their partial sums in LDS.
-//   large  a workgroup is 64 features x 128 rows, wave w the features
-//          [16 w, 16 w + 16) of all 128 rows (8 accumulators); the chunk of x
-//          is staged in LDS for the four waves, and the output tile leaves
-//          through LDS in whole 128-byte rows where it lies inside qkv.
+//   small  (rows <= 32): a workgroup is 16 features x 16 or 32 rows; its 8
+//          waves split the inputs.
+//   large  a workgroup is 128 features x 128 rows on 32 x 32 matrix-core
+//          blocks; the chunk of x and the chunk of weights (expanded once)
+//          are staged in LDS for its four waves, and the output tile leaves
+//          through LDS in whole rows where it lies inside qkv.
+//
+// Weights come in a tiled layout, repacked once from MLX's by
+// gdn_inproj_pack_affine4: features in blocks of 16 (the last padded with
+// zero codes, scales and biases), per block and 128-input chunk one 1 KB piece
+// [lane = 16 g4 + l16][4 words] holding words 16 c + 4 g4 .. + 3 of feature
+// 16 block + l16, and scales and biases as [block][group][16].  So a wave's
+// code words of a chunk are one contiguous 1 KB read, and 16 features' scales
+// one 32-byte read.
 #include "gdn_device.h"
 #include "gdn_inproj.h"
 
@@ -42,9 +52,15 @@ __device__ __forceinline__ f4v mfma16x16x32(uint4 a, uint4 b, f4v c)
 // rounded to bf16, as a B operand in input order.
 __device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float b)
 {
+    // even codes in the bytes of lo, odd codes in the bytes of hi: each code
+    // then converts with one byte-to-float instruction
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
     float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = fmaf(s, (float)((w >> (4 * j)) & 15u), b);
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = fmaf(s, (float)((lo >> (8 * j)) & 0xFFu), b);
+        v[2 * j + 1] = fmaf(s, (float)((hi >> (8 * j)) & 0xFFu), b);
+    }
     return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
 }
 
@@ -66,19 +82,25 @@ __device__ __forceinline__ void put(const InprojArgs &A, int r, int n, float y)
 }
 
 // ---------------------------------------------------------------- small
+// A workgroup is 16 features x 16 MS rows; its 8 waves take every 8th chunk
+// (each wave's next chunk in flight while one computes) and add their partial
+// sums in LDS in a fixed order.  A wave's code words of a chunk are one
+// contiguous 1 KB block of the tiled layout.
 template <int MS>
-__global__ void __launch_bounds__(256) inproj_small_kernel(const InprojArgs A)
+__global__ void __launch_bounds__(512) inproj_small_kernel(const InprojArgs A)
 {
-    __shared__ f4v red[4][MS][64];
+    constexpr int W = 8;
+    __shared__ f4v red[W][MS][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int features = A.channels + 2 * A.hv;
-    const int kw = A.hidden / 8, ng = A.hidden / A.group;
-    const int n = blockIdx.x * 16 + l16;
-    const int nl = min(n, features - 1);
+    const int nck = A.hidden / kChunk, ng = A.hidden / A.group;
+    const int nb = blockIdx.x;
     const int r0 = blockIdx.y * 16 * MS;
-    const uint32_t *wrow = A.wq + (size_t)nl * kw + 4 * g4;
+    const uint32_t *wblk = A.wq + (size_t)nb * nck * 256 + 4 * lane;
+    const uint16_t *sblk = A.scales + (size_t)nb * ng * 16 + l16;
+    const uint16_t *bblk = A.biases + (size_t)nb * ng * 16 + l16;
     const uint16_t *xrow[MS];
 #pragma unroll
     for (int m = 0; m < MS; ++m) xrow[m] = A.x + (size_t)min(r0 + 16 * m + l16, A.rows - 1) * A.hidden + 32 * g4;
@@ -86,140 +108,269 @@ __global__ void __launch_bounds__(256) inproj_small_kernel(const InprojArgs A)
     f4v acc[MS];
 #pragma unroll
     for (int m = 0; m < MS; ++m) acc[m] = f4v{0.f, 0.f, 0.f, 0.f};
-    for (int c = wave; c < A.hidden / kChunk; c += 4) {
+    uint4 wv, xv[MS][4];
+    float s, b;
+    auto fetch = [&](int c) {
         const int k0 = c * kChunk;
-        const uint4 wv = ld16g(wrow + k0 / 8);
+        wv = ld16g(wblk + (size_t)c * 256);
         const int g = (k0 + 32 * g4) / A.group;
-        const float s = bf16f(A.scales[(size_t)nl * ng + g]);
-        const float b = bf16f(A.biases[(size_t)nl * ng + g]);
-        uint4 xv[MS][4];
+        s = bf16f(sblk[g * 16]);
+        b = bf16f(bblk[g * 16]);
 #pragma unroll
         for (int m = 0; m < MS; ++m)
 #pragma unroll
             for (int st = 0; st < 4; ++st) xv[m][st] = ld16g(xrow[m] + k0 + 8 * st);
+    };
+    // each chunk's loads are issued while the one before computes (the last
+    // chunk loads its own again: no branch around the loads)
+    if (wave < nck) fetch(wave);
+    for (int c = wave; c < nck; c += W) {
+        const uint4 wc = wv;
+        const float sc = s, bc = b;
+        uint4 xc[MS][4];
+#pragma unroll
+        for (int m = 0; m < MS; ++m)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) xc[m][st] = xv[m][st];
+        fetch(c + W < nck ? c + W : c);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const uint4 bw = dequant8(word(wv, st), s, b);
+            const uint4 bw = dequant8(word(wc, st), sc, bc);
 #pragma unroll
-            for (int m = 0; m < MS; ++m) acc[m] = mfma16x16x32(xv[m][st], bw, acc[m]);
+            for (int m = 0; m < MS; ++m) acc[m] = mfma16x16x32(xc[m][st], bw, acc[m]);
         }
     }
 #pragma unroll
     for (int m = 0; m < MS; ++m) red[wave][m][lane] = acc[m];
     __syncthreads();
-    if (wave != 0 || n >= features) return;
+    // wave m < MS adds the partial sums of row tile m (waves in order)
+    const int n = nb * 16 + l16;
+    if (wave >= MS || n >= features) return;
+    f4v y = red[0][wave][lane];
 #pragma unroll
-    for (int m = 0; m < MS; ++m) {
-        const f4v y = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
+    for (int w = 1; w < W; ++w) y += red[w][wave][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + 16 * m + 4 * g4 + i;
-            if (r < A.rows) put(A, r, n, y[i]);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 16 * wave + 4 * g4 + i;
+        if (r < A.rows) put(A, r, n, y[i]);
     }
 }
 
 // ---------------------------------------------------------------- large
+// A workgroup computes 128 rows x 128 features, waves (wr, wf) = (w >> 1,
+// w & 1) the 64 x 64 block at rows 64 wr, features 64 wf, as 2 x 2
+// v_mfma_f32_32x32x16_bf16 accumulators.  Inputs go in chunks of 64: the
+// workgroup stages the chunk of x (128 x 64) and expands the chunk of weights
+// (128 x 64, thread t the 32 inputs 32 (t & 1) .. of feature t >> 1: four
+// code words, one scale and bias) into LDS once, for all four waves; chunk
+// c + 1's loads are in flight while chunk c computes (two LDS buffers).
 constexpr int kRows = 128;             // rows of a workgroup
-constexpr int kXPitch = kChunk + 8;    // bf16 pitch of the staged x rows (272 B: rows 4 banks apart)
-constexpr int kYPitch = 64 + 8;        // bf16 pitch of the output tile
+constexpr int kFeat = 128;             // features of a workgroup
+constexpr int kKC = 64;                // inputs a chunk
+constexpr int kPitch = kKC + 8;        // bf16 pitch of the staged rows (144 B)
+constexpr int kTile = 128 * kPitch;    // one staged 128 x 64 tile (x or weights)
+constexpr int kYPitch = kFeat + 8;     // bf16 pitch of the output tile
+constexpr size_t kLargeLds = 4 * kTile * sizeof(uint16_t);   // x and weights, two buffers each: 72 KB
+
+__device__ __forceinline__ f16v mfma32x32x16(uint4 a, uint4 b, f16v c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b), c,
+                                                  0, 0, 0);
+}
 
 __global__ void __launch_bounds__(256) inproj_large_kernel(const InprojArgs A)
 {
-    __shared__ __align__(16) uint16_t xs[kRows * kXPitch];
+    extern __shared__ __align__(16) uint16_t lds[];   // [2][x tile | weight tile]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, g4 = lane >> 4;
+    const int wr = wave >> 1, wf = wave & 1;
+    const int l32 = lane & 31, hh = lane >> 5;
     const int features = A.channels + 2 * A.hv;
-    const int kw = A.hidden / 8, ng = A.hidden / A.group;
-    const int n0 = blockIdx.x * 64;
-    const int n = n0 + 16 * wave + l16;
-    const int nl = min(n, features - 1);
+    const int ng = A.hidden / A.group, nck = A.hidden / kChunk;
+    const int n0 = blockIdx.x * kFeat;
     const int r0 = blockIdx.y * kRows;
-    const uint32_t *wrow = A.wq + (size_t)nl * kw + 4 * g4;
+    const int nchunks = A.hidden / kKC;
 
-    // staging: thread t moves 16-byte pieces t + 256 j (row p / 16, piece p % 16)
-    const uint16_t *xsrc[8];
+    // this thread's staging: x pieces t + 256 j (row p / 8, piece p % 8) and
+    // the weights of feature f = t / 2, inputs 32 (t & 1) .. + 32 of a chunk
+    const uint16_t *xsrc[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
         const int p = tid + 256 * j;
-        xsrc[j] = A.x + (size_t)min(r0 + (p >> 4), A.rows - 1) * A.hidden + 8 * (p & 15);
+        xsrc[j] = A.x + (size_t)min(r0 + (p >> 3), A.rows - 1) * A.hidden + 8 * (p & 7);
     }
-
-    f4v acc[8];
+    // weights: thread t expands feature f = 16 (t / 32) + t % 16, inputs
+    // 32 half .. + 32 of a 64-input chunk (half = t / 16 % 2): in the tiled
+    // layout the 32 threads of a 16-feature block read 512 contiguous bytes
+    const int half = (tid >> 4) & 1;
+    const int f = 16 * (tid >> 5) + (tid & 15);
+    const int nb = min(n0 / 16 + (tid >> 5), (features + 15) / 16 - 1);
+    const uint32_t *wsrc = A.wq + (size_t)nb * nck * 256 + ((tid & 31) << 2);
+    const uint16_t *ssrc = A.scales + (size_t)nb * ng * 16 + (tid & 15);
+    const uint16_t *bsrc = A.biases + (size_t)nb * ng * 16 + (tid & 15);
+    // a chunk's loads: its x pieces, this thread's code words, scale and bias
+    struct Loads {
+        uint4 x[4], w;
+        uint32_t sb;   // scale (low half) and bias (high half), bf16
+    };
+    auto fetch = [&](int c, Loads &L) {
+        const int k0 = c * kKC;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] = f4v{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < A.hidden / kChunk; ++c) {
-        const int k0 = c * kChunk;
-        uint4 xv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = ld16g(xsrc[j] + k0);
-        const uint4 wv = ld16g(wrow + k0 / 8);
-        const int g = (k0 + 32 * g4) / A.group;
-        const float s = bf16f(A.scales[(size_t)nl * ng + g]);
-        const float b = bf16f(A.biases[(size_t)nl * ng + g]);
-        lds_barrier();   // every wave is done with the previous chunk
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int p = tid + 256 * j;
-            *reinterpret_cast<uint4 *>(xs + (p >> 4) * kXPitch + 8 * (p & 15)) = xv[j];
-        }
-        lds_barrier();
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint4 bw = dequant8(word(wv, st), s, b);
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const uint4 av = *reinterpret_cast<const uint4 *>(xs + (16 * m + l16) * kXPitch + 32 * g4 + 8 * st);
-                acc[m] = mfma16x16x32(av, bw, acc[m]);
-            }
-        }
-    }
-
-    if (n0 + 64 <= A.channels) {
-        // inside qkv: the tile [128 rows][64 features] through LDS, then rows
-        // of 128 bytes (16-byte stores)
-        lds_barrier();
-        uint16_t *ys = xs;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ys[(16 * m + 4 * g4 + i) * kYPitch + 16 * wave + l16] = f2bf(acc[m][i]);
-        lds_barrier();
+        for (int j = 0; j < 4; ++j) L.x[j] = ld16g(xsrc[j] + k0);
+        // 128-input block c / 2, lanes 32 (c % 2) .. : this thread's word quad
+        L.w = ld16g(wsrc + (size_t)(c >> 1) * 256 + 128 * (c & 1));
+        const int g = (k0 + 32 * half) / A.group;
+        L.sb = (uint32_t)ssrc[g * 16] | ((uint32_t)bsrc[g * 16] << 16);
+    };
+    auto stage = [&](int buf, const Loads &L) {
+        uint16_t *xt = lds + buf * 2 * kTile, *wt = xt + kTile;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int p = tid + 256 * j;   // row p / 8, piece p % 8
-            const int r = r0 + (p >> 3);
+            const int p = tid + 256 * j;
+            *reinterpret_cast<uint4 *>(xt + (p >> 3) * kPitch + 8 * (p & 7)) = L.x[j];
+        }
+        const float s = __uint_as_float(L.sb << 16), b = __uint_as_float(L.sb & 0xffff0000u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(wt + f * kPitch + 32 * half + 8 * i) = dequant8(word(L.w, i), s, b);
+    };
+
+    f16v acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    // Chunk c computes from buffer c % 2 while chunk c + 2's loads are in
+    // flight and chunk c + 1's wait in registers; these go to the other
+    // buffer after the products, which every wave finished reading before
+    // the barrier that ended chunk c - 1.  (Past the end, the last chunk is
+    // loaded again: no branch around the loads.)
+    Loads next, after;
+    fetch(0, next);
+    stage(0, next);
+    fetch(min(1, nchunks - 1), next);
+    lds_barrier();
+    for (int c = 0; c < nchunks; ++c) {
+        fetch(min(c + 2, nchunks - 1), after);
+        const uint16_t *xt = lds + (c & 1) * 2 * kTile, *wt = xt + kTile;
+        const uint16_t *xa = xt + (64 * wr + l32) * kPitch + 8 * hh;
+        const uint16_t *wb = wt + (64 * wf + l32) * kPitch + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < kKC / 16; ++ks) {
+            const uint4 a0 = *reinterpret_cast<const uint4 *>(xa + 16 * ks);
+            const uint4 a1 = *reinterpret_cast<const uint4 *>(xa + 32 * kPitch + 16 * ks);
+            const uint4 b0 = *reinterpret_cast<const uint4 *>(wb + 16 * ks);
+            const uint4 b1 = *reinterpret_cast<const uint4 *>(wb + 32 * kPitch + 16 * ks);
+            acc[0][0] = mfma32x32x16(a0, b0, acc[0][0]);
+            acc[0][1] = mfma32x32x16(a0, b1, acc[0][1]);
+            acc[1][0] = mfma32x32x16(a1, b0, acc[1][0]);
+            acc[1][1] = mfma32x32x16(a1, b1, acc[1][1]);
+        }
+        stage((c + 1) & 1, next);
+        next = after;
+        lds_barrier();
+    }
+
+    // accumulator register e of lane (l32, hh) of block (i, j): row
+    // 64 wr + 32 i + 8 (e / 4) + 4 hh + e % 4, feature 64 wf + 32 j + l32
+    if (n0 + kFeat <= A.channels) {
+        // inside qkv: the tile through LDS (the buffer the last chunk computed
+        // from; every wave is past the barrier after it), then 16-byte stores
+        // of whole 256-byte row pieces
+        uint16_t *ys = lds + ((nchunks - 1) & 1) * 2 * kTile;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    ys[(64 * wr + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3)) * kYPitch + 64 * wf + 32 * j + l32] =
+                        f2bf(acc[i][j][e]);
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int p = tid + 256 * j;   // row p / 16, piece p % 16
+            const int r = r0 + (p >> 4);
             if (r < A.rows)
-                *reinterpret_cast<uint4 *>(A.qkv + (size_t)r * A.channels + n0 + 8 * (p & 7)) =
-                    *reinterpret_cast<const uint4 *>(ys + (p >> 3) * kYPitch + 8 * (p & 7));
+                *reinterpret_cast<uint4 *>(A.qkv + (size_t)r * A.channels + n0 + 8 * (p & 15)) =
+                    *reinterpret_cast<const uint4 *>(ys + (p >> 4) * kYPitch + 8 * (p & 15));
         }
         return;
     }
-    if (n >= features) return;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int j = 0; j < 2; ++j) {
+        const int n = n0 + 64 * wf + 32 * j + l32;
+        if (n >= features) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + 16 * m + 4 * g4 + i;
-            if (r < A.rows) put(A, r, n, acc[m][i]);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = r0 + 64 * wr + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
+                if (r < A.rows) put(A, r, n, acc[i][j][e]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------- repack
+// MLX layout -> tiled layout, one thread a word quad (and, for the first
+// K / group threads of a block row, its scales and biases).
+__global__ void __launch_bounds__(256) inproj_pack_kernel(const InprojPackArgs P)
+{
+    const int features = P.channels + 2 * P.hv;
+    const int nck = P.hidden / kChunk, kw = P.hidden / 8, ng = P.hidden / P.group;
+    const size_t quads = (size_t)P.blocks * nck * 64;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < quads) {
+        const int lane = (int)(i & 63);
+        const size_t bc = i >> 6;                      // block * nck + chunk
+        const int nb = (int)(bc / nck), c = (int)(bc - (size_t)nb * nck);
+        const int n = nb * 16 + (lane & 15), g4 = lane >> 4;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (n < features) {
+            const uint32_t *src = P.wq + (size_t)n * kw + 16 * c + 4 * g4;
+            v = make_uint4(src[0], src[1], src[2], src[3]);
         }
+        *reinterpret_cast<uint4 *>(P.wq_tiled + 4 * i) = v;
+    }
+    const size_t sbn = (size_t)P.blocks * ng * 16;
+    if (i < sbn) {
+        const int l16 = (int)(i & 15);
+        const size_t bg = i >> 4;                      // block * ng + group
+        const int nb = (int)(bg / ng), g = (int)(bg - (size_t)nb * ng);
+        const int n = nb * 16 + l16;
+        P.scales_tiled[i] = n < features ? P.scales[(size_t)n * ng + g] : (uint16_t)0;
+        P.biases_tiled[i] = n < features ? P.biases[(size_t)n * ng + g] : (uint16_t)0;
+    }
 }
 
 }  // namespace
+
+hipError_t launch_inproj_pack(const InprojPackArgs &P, hipStream_t stream)
+{
+    const size_t quads = (size_t)P.blocks * (P.hidden / kChunk) * 64;
+    const size_t sbn = (size_t)P.blocks * (P.hidden / P.group) * 16;
+    const size_t n = quads > sbn ? quads : sbn;
+    hipLaunchKernelGGL(inproj_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, P);
+    return hipGetLastError();
+}
 
 hipError_t launch_inproj(const InprojArgs &A, hipStream_t stream)
 {
     const int features = A.channels + 2 * A.hv;
     if (A.rows <= 16) {
-        hipLaunchKernelGGL(inproj_small_kernel<1>, dim3((features + 15) / 16, (A.rows + 15) / 16), dim3(256), 0,
+        hipLaunchKernelGGL(inproj_small_kernel<1>, dim3((features + 15) / 16, (A.rows + 15) / 16), dim3(512), 0,
                            stream, A);
     } else if (A.rows <= 32) {
-        hipLaunchKernelGGL(inproj_small_kernel<2>, dim3((features + 15) / 16, (A.rows + 31) / 32), dim3(256), 0,
+        hipLaunchKernelGGL(inproj_small_kernel<2>, dim3((features + 15) / 16, (A.rows + 31) / 32), dim3(512), 0,
                            stream, A);
     } else {
-        hipLaunchKernelGGL(inproj_large_kernel, dim3((features + 63) / 64, (A.rows + kRows - 1) / kRows), dim3(256),
-                           0, stream, A);
+        static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(inproj_large_kernel),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLargeLds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(inproj_large_kernel, dim3((features + kFeat - 1) / kFeat, (A.rows + kRows - 1) / kRows),
+                           dim3(256), kLargeLds, stream, A);
     }
     return hipGetLastError();
 }

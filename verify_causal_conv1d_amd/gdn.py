@@ -26,7 +26,7 @@ EXPORTED = (
     "gdn_status_name", "gdn_last_error", "gdn_channels", "gdn_conv_step", "gdn_recur_window",
     "gdn_recur_tree", "gdn_commit", "gdn_recur_log", "gdn_commit_replay",
     "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_check_layout",
-    "gdn_inproj_affine4",
+    "gdn_inproj_affine4", "gdn_inproj_pack_affine4", "gdn_inproj_padded_features",
 )
 
 
@@ -75,9 +75,12 @@ def lib():
                                               C.c_size_t, P]
             L.gdn_check_layout.argtypes = [i32, i32, i32, P, P]
             L.gdn_inproj_affine4.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P, P]
+            L.gdn_inproj_pack_affine4.argtypes = [P, i32, i32, P, P, P, P, P, P, P]
+            L.gdn_inproj_padded_features.restype = i32
+            L.gdn_inproj_padded_features.argtypes = [P]
             for name in ("gdn_conv_step", "gdn_recur_window", "gdn_recur_tree", "gdn_commit",
                          "gdn_recur_log", "gdn_commit_replay", "gdn_prefill_chunked",
-                         "gdn_check_layout", "gdn_inproj_affine4"):
+                         "gdn_check_layout", "gdn_inproj_affine4", "gdn_inproj_pack_affine4"):
                 getattr(L, name).restype = C.c_int
             _lib = L
     return _lib
@@ -252,10 +255,29 @@ def prefill_chunked(shape, params, seq_start, qkv, a, b, conv_tail, state, out, 
            "gdn_prefill_chunked")
 
 
+def inproj_pack(shape, wq, scales, biases, group: int):
+    """Repack affine 4-bit weights (MLX layout: codes int32 [C + 2 hv][hidden/8],
+    bf16 scales and biases [C + 2 hv][hidden/group]) into the tiled layout of
+    the in-projection kernels; returns (wq_tiled, scales_tiled, biases_tiled)."""
+    for t, dt, nm in ((wq, torch.int32, "wq"), (scales, torch.bfloat16, "scales"),
+                      (biases, torch.bfloat16, "biases")):
+        _dev(t, dt, nm)
+    sh = _shape(shape)
+    np_ = int(lib().gdn_inproj_padded_features(C.byref(sh)))
+    if np_ < 0:
+        raise ValueError("bad shape")
+    hidden = wq.shape[1] * 8
+    wt = torch.empty(np_ * hidden // 8, dtype=torch.int32, device=wq.device)
+    st = torch.empty(np_ * hidden // group, dtype=torch.bfloat16, device=wq.device)
+    bt = torch.empty_like(st)
+    _check(lib().gdn_inproj_pack_affine4(C.byref(sh), hidden, int(group), _ptr(wq), _ptr(scales), _ptr(biases),
+                                         _ptr(wt), _ptr(st), _ptr(bt), _stream(wq)), "gdn_inproj_pack_affine4")
+    return wt, st, bt
+
+
 def inproj_affine4(shape, x, wq, scales, biases, qkv, a, b, group: int):
     """The affine 4-bit in-projection: qkv, a, b (bf16, written) from hidden
-    rows x (bf16 [R][hidden]), packed codes wq (int32 [C + 2 hv][hidden/8]) and
-    bf16 scales and biases ([C + 2 hv][hidden/group])."""
+    rows x (bf16 [R][hidden]) and the tiled weights of ``inproj_pack``."""
     for t, dt, nm in ((x, torch.bfloat16, "x"), (wq, torch.int32, "wq"), (scales, torch.bfloat16, "scales"),
                       (biases, torch.bfloat16, "biases"), (qkv, torch.bfloat16, "qkv"),
                       (a, torch.bfloat16, "a"), (b, torch.bfloat16, "b")):
