@@ -82,40 +82,55 @@ __device__ __forceinline__ void put(const InprojArgs &A, int r, int n, float y)
 }
 
 // ---------------------------------------------------------------- small
-// A workgroup is 16 features x 16 MS rows; its 8 waves take every 8th chunk
-// (each wave's next chunk in flight while one computes) and add their partial
-// sums in LDS in a fixed order.  A wave's code words of a chunk are one
-// contiguous 1 KB block of the tiled layout.
-template <int MS>
+// A workgroup is NF blocks of 16 features x 16 MS rows; its 8 waves take
+// every 8th chunk (each wave's next chunk in flight while one computes) and
+// add their partial sums in LDS in a fixed order.  A wave's code words of a
+// chunk and block are one contiguous 1 KB piece of the tiled layout; its x
+// pieces serve all NF blocks (two blocks halve the reads of x, which every
+// workgroup reads whole).
+template <int MS, int NF>
 __global__ void __launch_bounds__(512) inproj_small_kernel(const InprojArgs A)
 {
     constexpr int W = 8;
-    __shared__ f4v red[W][MS][64];
+    __shared__ f4v red[W][NF * MS][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int features = A.channels + 2 * A.hv;
+    const int blocks = (features + 15) / 16;
     const int nck = A.hidden / kChunk, ng = A.hidden / A.group;
-    const int nb = blockIdx.x;
     const int r0 = blockIdx.y * 16 * MS;
-    const uint32_t *wblk = A.wq + (size_t)nb * nck * 256 + 4 * lane;
-    const uint16_t *sblk = A.scales + (size_t)nb * ng * 16 + l16;
-    const uint16_t *bblk = A.biases + (size_t)nb * ng * 16 + l16;
+    // (past the last block, a workgroup's second block repeats the last one
+    // and writes nothing)
+    const uint32_t *wblk[NF];
+    const uint16_t *sblk[NF], *bblk[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int nb = min((int)blockIdx.x * NF + f, blocks - 1);
+        wblk[f] = A.wq + (size_t)nb * nck * 256 + 4 * lane;
+        sblk[f] = A.scales + (size_t)nb * ng * 16 + l16;
+        bblk[f] = A.biases + (size_t)nb * ng * 16 + l16;
+    }
     const uint16_t *xrow[MS];
 #pragma unroll
     for (int m = 0; m < MS; ++m) xrow[m] = A.x + (size_t)min(r0 + 16 * m + l16, A.rows - 1) * A.hidden + 32 * g4;
 
-    f4v acc[MS];
+    f4v acc[NF][MS];
 #pragma unroll
-    for (int m = 0; m < MS; ++m) acc[m] = f4v{0.f, 0.f, 0.f, 0.f};
-    uint4 wv, xv[MS][4];
-    float s, b;
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int m = 0; m < MS; ++m) acc[f][m] = f4v{0.f, 0.f, 0.f, 0.f};
+    uint4 wv[NF], xv[MS][4];
+    float s[NF], b[NF];
     auto fetch = [&](int c) {
         const int k0 = c * kChunk;
-        wv = ld16g(wblk + (size_t)c * 256);
         const int g = (k0 + 32 * g4) / A.group;
-        s = bf16f(sblk[g * 16]);
-        b = bf16f(bblk[g * 16]);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            wv[f] = ld16g(wblk[f] + (size_t)c * 256);
+            s[f] = bf16f(sblk[f][g * 16]);
+            b[f] = bf16f(bblk[f][g * 16]);
+        }
 #pragma unroll
         for (int m = 0; m < MS; ++m)
 #pragma unroll
@@ -125,33 +140,45 @@ __global__ void __launch_bounds__(512) inproj_small_kernel(const InprojArgs A)
     // chunk loads its own again: no branch around the loads)
     if (wave < nck) fetch(wave);
     for (int c = wave; c < nck; c += W) {
-        const uint4 wc = wv;
-        const float sc = s, bc = b;
-        uint4 xc[MS][4];
+        uint4 wc[NF], xc[MS][4];
+        float sc[NF], bc[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            wc[f] = wv[f];
+            sc[f] = s[f];
+            bc[f] = b[f];
+        }
 #pragma unroll
         for (int m = 0; m < MS; ++m)
 #pragma unroll
             for (int st = 0; st < 4; ++st) xc[m][st] = xv[m][st];
         fetch(c + W < nck ? c + W : c);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint4 bw = dequant8(word(wc, st), sc, bc);
+        for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int m = 0; m < MS; ++m) acc[m] = mfma16x16x32(xc[m][st], bw, acc[m]);
-        }
+            for (int f = 0; f < NF; ++f) {
+                const uint4 bw = dequant8(word(wc[f], st), sc[f], bc[f]);
+#pragma unroll
+                for (int m = 0; m < MS; ++m) acc[f][m] = mfma16x16x32(xc[m][st], bw, acc[f][m]);
+            }
     }
 #pragma unroll
-    for (int m = 0; m < MS; ++m) red[wave][m][lane] = acc[m];
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int m = 0; m < MS; ++m) red[wave][f * MS + m][lane] = acc[f][m];
     __syncthreads();
-    // wave m < MS adds the partial sums of row tile m (waves in order)
+    // wave i < NF MS adds the partial sums of block i / MS, row tile i % MS
+    // (waves in order)
+    if (wave >= NF * MS) return;
+    const int nb = blockIdx.x * NF + wave / MS, m = wave % MS;
     const int n = nb * 16 + l16;
-    if (wave >= MS || n >= features) return;
+    if (nb >= blocks || n >= features) return;
     f4v y = red[0][wave][lane];
 #pragma unroll
     for (int w = 1; w < W; ++w) y += red[w][wave][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = r0 + 16 * wave + 4 * g4 + i;
+        const int r = r0 + 16 * m + 4 * g4 + i;
         if (r < A.rows) put(A, r, n, y[i]);
     }
 }
@@ -164,6 +191,11 @@ __global__ void __launch_bounds__(512) inproj_small_kernel(const InprojArgs A)
 // (128 x 64, thread t the 32 inputs 32 (t & 1) .. of feature t >> 1: four
 // code words, one scale and bias) into LDS once, for all four waves; chunk
 // c + 1's loads are in flight while chunk c computes (two LDS buffers).
+// With KS = 2 a workgroup has two such groups of four waves, each with its
+// own buffers and one half of the inputs; the second group's sums are added
+// to the first's through LDS at the end (in that order).  Two groups a
+// compute unit overlap one group's weight expansion and staging with the
+// other's products: it serves launches with at most one tile a compute unit.
 constexpr int kRows = 128;             // rows of a workgroup
 constexpr int kFeat = 128;             // features of a workgroup
 constexpr int kKC = 64;                // inputs a chunk
@@ -178,18 +210,23 @@ __device__ __forceinline__ f16v mfma32x32x16(uint4 a, uint4 b, f16v c)
                                                   0, 0, 0);
 }
 
-__global__ void __launch_bounds__(256) inproj_large_kernel(const InprojArgs A)
+template <int KS>
+__global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs A)
 {
-    extern __shared__ __align__(16) uint16_t lds[];   // [2][x tile | weight tile]
-    const int tid = threadIdx.x, lane = tid & 63;
+    extern __shared__ __align__(16) uint16_t lds_all[];   // [KS][2][x tile | weight tile]
+    // kh: this thread's group (input share); tid, lane, wave within it
+    const int kh = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
+    const int tid = threadIdx.x & 255, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint16_t *lds = lds_all + kh * 4 * kTile;
     const int wr = wave >> 1, wf = wave & 1;
     const int l32 = lane & 31, hh = lane >> 5;
     const int features = A.channels + 2 * A.hv;
     const int ng = A.hidden / A.group, nck = A.hidden / kChunk;
     const int n0 = blockIdx.x * kFeat;
     const int r0 = blockIdx.y * kRows;
-    const int nchunks = A.hidden / kKC;
+    const int nchunks = A.hidden / kKC / KS;   // chunks of a share
+    const int cbase = kh * nchunks;
 
     // this thread's staging: x pieces t + 256 j (row p / 8, piece p % 8) and
     // the weights of feature f = t / 2, inputs 32 (t & 1) .. + 32 of a chunk
@@ -213,7 +250,8 @@ __global__ void __launch_bounds__(256) inproj_large_kernel(const InprojArgs A)
         uint4 x[4], w;
         uint32_t sb;   // scale (low half) and bias (high half), bf16
     };
-    auto fetch = [&](int c, Loads &L) {
+    auto fetch = [&](int cs, Loads &L) {
+        const int c = cbase + cs;
         const int k0 = c * kKC;
 #pragma unroll
         for (int j = 0; j < 4; ++j) L.x[j] = ld16g(xsrc[j] + k0);
@@ -273,22 +311,50 @@ __global__ void __launch_bounds__(256) inproj_large_kernel(const InprojArgs A)
         lds_barrier();
     }
 
-    // accumulator register e of lane (l32, hh) of block (i, j): row
-    // 64 wr + 32 i + 8 (e / 4) + 4 hh + e % 4, feature 64 wf + 32 j + l32
-    if (n0 + kFeat <= A.channels) {
-        // inside qkv: the tile through LDS (the buffer the last chunk computed
-        // from; every wave is past the barrier after it), then 16-byte stores
-        // of whole 256-byte row pieces
-        uint16_t *ys = lds + ((nchunks - 1) & 1) * 2 * kTile;
+    if constexpr (KS == 2) {
+        // the second share's sums, [wave][i][j][e][lane] in fp32, through the
+        // second share's buffers (64 of its 72 KB; every wave is past the
+        // barrier after its last chunk)
+        float *part = reinterpret_cast<float *>(lds_all + 4 * kTile);
+        if (kh == 1) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    ys[(64 * wr + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3)) * kYPitch + 64 * wf + 32 * j + l32] =
-                        f2bf(acc[i][j][e]);
+                    for (int e = 0; e < 16; ++e) part[(((wave * 2 + i) * 2 + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+        }
         lds_barrier();
+        if (kh == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] += part[(((wave * 2 + i) * 2 + j) * 16 + e) * 64 + lane];
+        }
+    }
+
+    // accumulator register e of lane (l32, hh) of block (i, j): row
+    // 64 wr + 32 i + 8 (e / 4) + 4 hh + e % 4, feature 64 wf + 32 j + l32;
+    // the first share writes the tile
+    if (n0 + kFeat <= A.channels) {
+        // inside qkv: the tile through LDS (the first share's buffer the last
+        // chunk computed from; every wave is past the barrier after it), then
+        // 16-byte stores of whole 256-byte row pieces
+        uint16_t *ys = lds_all + ((nchunks - 1) & 1) * 2 * kTile;
+        if (kh == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        ys[(64 * wr + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3)) * kYPitch + 64 * wf + 32 * j + l32] =
+                            f2bf(acc[i][j][e]);
+        }
+        lds_barrier();
+        if (kh != 0) return;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int p = tid + 256 * j;   // row p / 16, piece p % 16
@@ -299,6 +365,7 @@ __global__ void __launch_bounds__(256) inproj_large_kernel(const InprojArgs A)
         }
         return;
     }
+    if (kh != 0) return;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int n = n0 + 64 * wf + 32 * j + l32;
@@ -345,6 +412,21 @@ __global__ void __launch_bounds__(256) inproj_pack_kernel(const InprojPackArgs P
     }
 }
 
+// Compute units of the current device (looked up once per device; a race
+// between threads writes the same value).
+int compute_units()
+{
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 }  // namespace
 
 hipError_t launch_inproj_pack(const InprojPackArgs &P, hipStream_t stream)
@@ -359,18 +441,35 @@ hipError_t launch_inproj_pack(const InprojPackArgs &P, hipStream_t stream)
 hipError_t launch_inproj(const InprojArgs &A, hipStream_t stream)
 {
     const int features = A.channels + 2 * A.hv;
-    if (A.rows <= 16) {
-        hipLaunchKernelGGL(inproj_small_kernel<1>, dim3((features + 15) / 16, (A.rows + 15) / 16), dim3(512), 0,
-                           stream, A);
-    } else if (A.rows <= 32) {
-        hipLaunchKernelGGL(inproj_small_kernel<2>, dim3((features + 15) / 16, (A.rows + 31) / 32), dim3(512), 0,
-                           stream, A);
+    if (A.rows <= 32) {
+        // two feature blocks a workgroup while that still leaves a workgroup
+        // for every compute unit
+        const int blocks = (features + 15) / 16;
+        const int nf = blocks / 2 >= compute_units() ? 2 : 1;
+        const dim3 grid((blocks + nf - 1) / nf, A.rows <= 16 ? (A.rows + 15) / 16 : (A.rows + 31) / 32);
+        if (A.rows <= 16) {
+            if (nf == 2) hipLaunchKernelGGL((inproj_small_kernel<1, 2>), grid, dim3(512), 0, stream, A);
+            else hipLaunchKernelGGL((inproj_small_kernel<1, 1>), grid, dim3(512), 0, stream, A);
+        } else {
+            if (nf == 2) hipLaunchKernelGGL((inproj_small_kernel<2, 2>), grid, dim3(512), 0, stream, A);
+            else hipLaunchKernelGGL((inproj_small_kernel<2, 1>), grid, dim3(512), 0, stream, A);
+        }
     } else {
-        static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(inproj_large_kernel),
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLargeLds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(inproj_large_kernel, dim3((features + kFeat - 1) / kFeat, (A.rows + kRows - 1) / kRows),
-                           dim3(256), kLargeLds, stream, A);
+        static const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void *>(inproj_large_kernel<1>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLargeLds);
+        static const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(inproj_large_kernel<2>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         (int)(2 * kLargeLds));
+        const dim3 grid((features + kFeat - 1) / kFeat, (A.rows + kRows - 1) / kRows);
+        // two input shares a workgroup while the tiles leave a compute unit
+        // to each workgroup
+        if ((int)(grid.x * grid.y) <= compute_units()) {
+            if (e2 != hipSuccess) return e2;
+            hipLaunchKernelGGL((inproj_large_kernel<2>), grid, dim3(512), 2 * kLargeLds, stream, A);
+        } else {
+            if (e1 != hipSuccess) return e1;
+            hipLaunchKernelGGL((inproj_large_kernel<1>), grid, dim3(256), kLargeLds, stream, A);
+        }
     }
     return hipGetLastError();
 }
