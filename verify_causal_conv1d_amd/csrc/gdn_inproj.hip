@@ -246,9 +246,10 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
     const uint16_t *ssrc = A.scales + (size_t)nb * ng * 16 + (tid & 15);
     const uint16_t *bsrc = A.biases + (size_t)nb * ng * 16 + (tid & 15);
     // a chunk's loads: its x pieces, this thread's code words, scale and bias
+    // (kept as loaded: work on them here would wait for the loads)
     struct Loads {
         uint4 x[4], w;
-        uint32_t sb;   // scale (low half) and bias (high half), bf16
+        uint32_t s, b;   // bf16 scale and bias
     };
     auto fetch = [&](int cs, Loads &L) {
         const int c = cbase + cs;
@@ -258,7 +259,8 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
         // 128-input block c / 2, lanes 32 (c % 2) .. : this thread's word quad
         L.w = ld16g(wsrc + (size_t)(c >> 1) * 256 + 128 * (c & 1));
         const int g = (k0 + 32 * half) / A.group;
-        L.sb = (uint32_t)ssrc[g * 16] | ((uint32_t)bsrc[g * 16] << 16);
+        L.s = ssrc[g * 16];
+        L.b = bsrc[g * 16];
     };
     auto stage = [&](int buf, const Loads &L) {
         uint16_t *xt = lds + buf * 2 * kTile, *wt = xt + kTile;
@@ -267,7 +269,7 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
             const int p = tid + 256 * j;
             *reinterpret_cast<uint4 *>(xt + (p >> 3) * kPitch + 8 * (p & 7)) = L.x[j];
         }
-        const float s = __uint_as_float(L.sb << 16), b = __uint_as_float(L.sb & 0xffff0000u);
+        const float s = __uint_as_float(L.s << 16), b = __uint_as_float(L.b << 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             *reinterpret_cast<uint4 *>(wt + f * kPitch + 32 * half + 8 * i) = dequant8(word(L.w, i), s, b);
@@ -280,18 +282,20 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    // Chunk c computes from buffer c % 2 while chunk c + 2's loads are in
-    // flight and chunk c + 1's wait in registers; these go to the other
-    // buffer after the products, which every wave finished reading before
-    // the barrier that ended chunk c - 1.  (Past the end, the last chunk is
-    // loaded again: no branch around the loads.)
-    Loads next, after;
-    fetch(0, next);
-    stage(0, next);
-    fetch(min(1, nchunks - 1), next);
+    // Step c computes chunk c from buffer c % 2 while chunk c + 2's loads
+    // are in flight and chunk c + 1's wait in registers; these go to the
+    // other buffer after the products, which every wave finished reading
+    // before the barrier that ended step c - 1.  The two register sets trade
+    // roles from step to step (a copy from one to the other would wait for
+    // the loads in flight).  Past the end, the last chunk is loaded again:
+    // no branch around the loads.
+    Loads la, lb;
+    fetch(0, la);
+    stage(0, la);
+    fetch(min(1, nchunks - 1), la);
     lds_barrier();
-    for (int c = 0; c < nchunks; ++c) {
-        fetch(min(c + 2, nchunks - 1), after);
+    auto step = [&](int c, const Loads &cur, Loads &nxt) {
+        fetch(min(c + 2, nchunks - 1), nxt);
         const uint16_t *xt = lds + (c & 1) * 2 * kTile, *wt = xt + kTile;
         const uint16_t *xa = xt + (64 * wr + l32) * kPitch + 8 * hh;
         const uint16_t *wb = wt + (64 * wf + l32) * kPitch + 8 * hh;
@@ -306,10 +310,15 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
             acc[1][0] = mfma32x32x16(a1, b0, acc[1][0]);
             acc[1][1] = mfma32x32x16(a1, b1, acc[1][1]);
         }
-        stage((c + 1) & 1, next);
-        next = after;
+        stage((c + 1) & 1, cur);
         lds_barrier();
+    };
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        step(c, la, lb);
+        step(c + 1, lb, la);
     }
+    if (c < nchunks) step(c, la, lb);
 
     if constexpr (KS == 2) {
         // the second share's sums, [wave][i][j][e][lane] in fp32, through the
