@@ -55,7 +55,8 @@ def check(t: gi.Inproj, y_gpu: np.ndarray, rows=None):
 
 CASES = {
     # rows, hidden, group: the small kernel (1 and 2 row tiles), the large one
-    # (a partial row tile, the feature tile that crosses into a and b)
+    # (a partial row tile, the feature tile that crosses into a and b; two
+    # input shares while the tiles leave a compute unit each)
     "rows1-g32": (gi.SMALL, 1, 256, 32),
     "rows5-g64": (gi.SMALL, 5, 384, 64),
     "rows16-g128": (gi.SMALL, 16, 512, 128),
@@ -64,6 +65,11 @@ CASES = {
     "rows33-g64": (gi.SMALL, 33, 256, 64),
     "rows200-g128": (gi.SMALL, 200, 640, 128),
     "small27b-rows130": (gi.Shape(hk=2, hv=6, dk=128, dv=128), 130, 768, 64),
+    # the 27B-like layer's 81 feature tiles: 4 tiles of 128 rows (more tiles
+    # than compute units, one input share), then 256-row tiles (3, the last
+    # one ragged)
+    "27b-rows500-g64": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 500, 256, 64),
+    "27b-rows700-g32": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 700, 384, 32),
 }
 
 

@@ -53,14 +53,20 @@ __device__ __forceinline__ f4v mfma16x16x32(uint4 a, uint4 b, f4v c)
 __device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float b)
 {
     // even codes in the bytes of lo, odd codes in the bytes of hi: each code
-    // then converts with one byte-to-float instruction
+    // then converts with one byte-to-float instruction (written out: the
+    // compiler would extract each byte first)
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    float v[8];
+    float q[8], v[8];
+    asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(q[0]) : "v"(lo));
+    asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(q[2]) : "v"(lo));
+    asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(q[4]) : "v"(lo));
+    asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(q[6]) : "v"(lo));
+    asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(q[1]) : "v"(hi));
+    asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(q[3]) : "v"(hi));
+    asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(q[5]) : "v"(hi));
+    asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(q[7]) : "v"(hi));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = fmaf(s, (float)((lo >> (8 * j)) & 0xFFu), b);
-        v[2 * j + 1] = fmaf(s, (float)((hi >> (8 * j)) & 0xFFu), b);
-    }
+    for (int j = 0; j < 8; ++j) v[j] = fmaf(s, q[j], b);
     return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
 }
 
@@ -184,25 +190,35 @@ __global__ void __launch_bounds__(512) inproj_small_kernel(const InprojArgs A)
 }
 
 // ---------------------------------------------------------------- large
-// A workgroup computes 128 rows x 128 features, waves (wr, wf) = (w >> 1,
+// A workgroup computes 64 WR rows x 128 features; wave (wr, wf) = (w >> 1,
 // w & 1) the 64 x 64 block at rows 64 wr, features 64 wf, as 2 x 2
 // v_mfma_f32_32x32x16_bf16 accumulators.  Inputs go in chunks of 64: the
-// workgroup stages the chunk of x (128 x 64) and expands the chunk of weights
-// (128 x 64, thread t the 32 inputs 32 (t & 1) .. of feature t >> 1: four
-// code words, one scale and bias) into LDS once, for all four waves; chunk
-// c + 1's loads are in flight while chunk c computes (two LDS buffers).
-// With KS = 2 a workgroup has two such groups of four waves, each with its
-// own buffers and one half of the inputs; the second group's sums are added
-// to the first's through LDS at the end (in that order).  Two groups a
-// compute unit overlap one group's weight expansion and staging with the
-// other's products: it serves launches with at most one tile a compute unit.
-constexpr int kRows = 128;             // rows of a workgroup
+// workgroup stages the chunk of x (64 WR x 64) and expands the chunk of
+// weights (128 x 64: each thread 8 WPT inputs of one feature, WPT code words
+// and one scale and bias) into LDS once, for all its waves; chunk c + 1's
+// loads wait in registers and chunk c + 2's are in flight while chunk c
+// computes (two LDS buffers).  WR = 4 (256 rows) halves the expansion work
+// a product against WR = 2 and serves long launches.
+// With KS = 2 (and WR = 2) a workgroup has two such groups of four waves,
+// each with its own buffers and one half of the inputs; the second group's
+// sums are added to the first's through LDS at the end (in that order).  Two
+// groups a compute unit overlap one group's weight expansion and staging with
+// the other's products: it serves launches with at most one tile a compute
+// unit.
 constexpr int kFeat = 128;             // features of a workgroup
 constexpr int kKC = 64;                // inputs a chunk
 constexpr int kPitch = kKC + 8;        // bf16 pitch of the staged rows (144 B)
-constexpr int kTile = 128 * kPitch;    // one staged 128 x 64 tile (x or weights)
 constexpr int kYPitch = kFeat + 8;     // bf16 pitch of the output tile
-constexpr size_t kLargeLds = 4 * kTile * sizeof(uint16_t);   // x and weights, two buffers each: 72 KB
+
+template <int KS, int WR>
+struct LargeCfg {
+    static constexpr int rows = 64 * WR;                      // rows of a workgroup
+    static constexpr int nt = 128 * WR;                       // threads of a share
+    static constexpr int wpt = 8 / WR;                        // code words a thread a chunk
+    static constexpr int xt = rows * kPitch;                  // staged x (bf16)
+    static constexpr int buf = (rows + kFeat) * kPitch;       // one buffer: x and weights (bf16)
+    static constexpr size_t lds = (size_t)KS * 2 * buf * sizeof(uint16_t);
+};
 
 __device__ __forceinline__ f16v mfma32x32x16(uint4 a, uint4 b, f16v c)
 {
@@ -210,45 +226,51 @@ __device__ __forceinline__ f16v mfma32x32x16(uint4 a, uint4 b, f16v c)
                                                   0, 0, 0);
 }
 
-template <int KS>
-__global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs A)
+template <int KS, int WR>
+__global__ void __launch_bounds__(128 * WR * KS) inproj_large_kernel(const InprojArgs A)
 {
+    using C = LargeCfg<KS, WR>;
+    constexpr int NT = C::nt, WPT = C::wpt;
     extern __shared__ __align__(16) uint16_t lds_all[];   // [KS][2][x tile | weight tile]
     // kh: this thread's group (input share); tid, lane, wave within it
-    const int kh = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
-    const int tid = threadIdx.x & 255, lane = tid & 63;
+    const int kh = __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT);
+    const int tid = threadIdx.x % NT, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint16_t *lds = lds_all + kh * 4 * kTile;
+    uint16_t *lds = lds_all + kh * 2 * C::buf;
     const int wr = wave >> 1, wf = wave & 1;
     const int l32 = lane & 31, hh = lane >> 5;
     const int features = A.channels + 2 * A.hv;
     const int ng = A.hidden / A.group, nck = A.hidden / kChunk;
     const int n0 = blockIdx.x * kFeat;
-    const int r0 = blockIdx.y * kRows;
+    const int r0 = blockIdx.y * C::rows;
     const int nchunks = A.hidden / kKC / KS;   // chunks of a share
     const int cbase = kh * nchunks;
 
-    // this thread's staging: x pieces t + 256 j (row p / 8, piece p % 8) and
-    // the weights of feature f = t / 2, inputs 32 (t & 1) .. + 32 of a chunk
+    // this thread's staging: x pieces t + NT j (row p / 8, piece p % 8)
     const uint16_t *xsrc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int p = tid + 256 * j;
+        const int p = tid + NT * j;
         xsrc[j] = A.x + (size_t)min(r0 + (p >> 3), A.rows - 1) * A.hidden + 8 * (p & 7);
     }
-    // weights: thread t expands feature f = 16 (t / 32) + t % 16, inputs
-    // 32 half .. + 32 of a 64-input chunk (half = t / 16 % 2): in the tiled
-    // layout the 32 threads of a 16-feature block read 512 contiguous bytes
-    const int half = (tid >> 4) & 1;
-    const int f = 16 * (tid >> 5) + (tid & 15);
-    const int nb = min(n0 / 16 + (tid >> 5), (features + 15) / 16 - 1);
-    const uint32_t *wsrc = A.wq + (size_t)nb * nck * 256 + ((tid & 31) << 2);
-    const uint16_t *ssrc = A.scales + (size_t)nb * ng * 16 + (tid & 15);
-    const uint16_t *bsrc = A.biases + (size_t)nb * ng * 16 + (tid & 15);
+    // weights: 128 / WPT threads a 16-feature block; thread t of a block
+    // expands feature t % 16, inputs 8 WPT sub .. of a 64-input chunk (sub =
+    // t / 16).  In the tiled layout those words sit in slot t % 16 + 16 g4 of
+    // the chunk pair's 1 KB piece, g4 = 2 (c % 2) + input / 32, and the
+    // threads of a block read 512 contiguous bytes.
+    constexpr int TPB = 128 / WPT;
+    const int bt = tid % TPB, l16 = bt & 15, sub = bt >> 4;
+    const int f = 16 * (tid / TPB) + l16;
+    const int ko = 8 * WPT * sub;   // first input within the chunk
+    const int nb = min(n0 / 16 + tid / TPB, (features + 15) / 16 - 1);
+    const uint32_t *wsrc = A.wq + (size_t)nb * nck * 256 + 4 * (l16 + 16 * (ko >> 5)) + ((ko & 31) >> 3);
+    const uint16_t *ssrc = A.scales + (size_t)nb * ng * 16 + l16;
+    const uint16_t *bsrc = A.biases + (size_t)nb * ng * 16 + l16;
     // a chunk's loads: its x pieces, this thread's code words, scale and bias
     // (kept as loaded: work on them here would wait for the loads)
     struct Loads {
-        uint4 x[4], w;
+        uint4 x[4];
+        uint32_t w[WPT];
         uint32_t s, b;   // bf16 scale and bias
     };
     auto fetch = [&](int cs, Loads &L) {
@@ -256,23 +278,30 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
         const int k0 = c * kKC;
 #pragma unroll
         for (int j = 0; j < 4; ++j) L.x[j] = ld16g(xsrc[j] + k0);
-        // 128-input block c / 2, lanes 32 (c % 2) .. : this thread's word quad
-        L.w = ld16g(wsrc + (size_t)(c >> 1) * 256 + 128 * (c & 1));
-        const int g = (k0 + 32 * half) / A.group;
+        // chunk pair c / 2, slots 32 (c % 2) ..
+        const uint32_t *wc = wsrc + (size_t)(c >> 1) * 256 + 128 * (c & 1);
+        if constexpr (WPT == 4) {
+            const uint4 v = ld16g(wc);
+            L.w[0] = v.x; L.w[1] = v.y; L.w[2] = v.z; L.w[3] = v.w;
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2 *>(wc);
+            L.w[0] = v.x; L.w[1] = v.y;
+        }
+        const int g = (k0 + ko) / A.group;
         L.s = ssrc[g * 16];
         L.b = bsrc[g * 16];
     };
-    auto stage = [&](int buf, const Loads &L) {
-        uint16_t *xt = lds + buf * 2 * kTile, *wt = xt + kTile;
+    auto stage = [&](int bf, const Loads &L) {
+        uint16_t *xt = lds + bf * C::buf, *wt = xt + C::xt;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int p = tid + 256 * j;
+            const int p = tid + NT * j;
             *reinterpret_cast<uint4 *>(xt + (p >> 3) * kPitch + 8 * (p & 7)) = L.x[j];
         }
         const float s = __uint_as_float(L.s << 16), b = __uint_as_float(L.b << 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4 *>(wt + f * kPitch + 32 * half + 8 * i) = dequant8(word(L.w, i), s, b);
+        for (int i = 0; i < WPT; ++i)
+            *reinterpret_cast<uint4 *>(wt + f * kPitch + ko + 8 * i) = dequant8(L.w[i], s, b);
     };
 
     f16v acc[2][2];
@@ -296,7 +325,7 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
     lds_barrier();
     auto step = [&](int c, const Loads &cur, Loads &nxt) {
         fetch(min(c + 2, nchunks - 1), nxt);
-        const uint16_t *xt = lds + (c & 1) * 2 * kTile, *wt = xt + kTile;
+        const uint16_t *xt = lds + (c & 1) * C::buf, *wt = xt + C::xt;
         const uint16_t *xa = xt + (64 * wr + l32) * kPitch + 8 * hh;
         const uint16_t *wb = wt + (64 * wf + l32) * kPitch + 8 * hh;
 #pragma unroll
@@ -322,9 +351,10 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
 
     if constexpr (KS == 2) {
         // the second share's sums, [wave][i][j][e][lane] in fp32, through the
-        // second share's buffers (64 of its 72 KB; every wave is past the
-        // barrier after its last chunk)
-        float *part = reinterpret_cast<float *>(lds_all + 4 * kTile);
+        // second share's buffers (every wave is past the barrier after its
+        // last chunk)
+        static_assert(64 * 4 * 64 * sizeof(float) * (WR / 2) <= 2 * C::buf * sizeof(uint16_t), "partials");
+        float *part = reinterpret_cast<float *>(lds_all + 2 * C::buf);
         if (kh == 1) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -348,10 +378,11 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
     // 64 wr + 32 i + 8 (e / 4) + 4 hh + e % 4, feature 64 wf + 32 j + l32;
     // the first share writes the tile
     if (n0 + kFeat <= A.channels) {
-        // inside qkv: the tile through LDS (the first share's buffer the last
-        // chunk computed from; every wave is past the barrier after it), then
-        // 16-byte stores of whole 256-byte row pieces
-        uint16_t *ys = lds_all + ((nchunks - 1) & 1) * 2 * kTile;
+        // inside qkv: the tile through LDS (the first share's two buffers;
+        // every wave is past the barrier after the last chunk), then 16-byte
+        // stores of whole 256-byte row pieces
+        static_assert(C::rows * kYPitch <= 2 * C::buf, "output tile");
+        uint16_t *ys = lds_all;
         if (kh == 0) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -366,7 +397,7 @@ __global__ void __launch_bounds__(256 * KS) inproj_large_kernel(const InprojArgs
         if (kh != 0) return;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int p = tid + 256 * j;   // row p / 16, piece p % 16
+            const int p = tid + NT * j;   // row p / 16, piece p % 16
             const int r = r0 + (p >> 4);
             if (r < A.rows)
                 *reinterpret_cast<uint4 *>(A.qkv + (size_t)r * A.channels + n0 + 8 * (p & 15)) =
@@ -436,6 +467,18 @@ int compute_units()
     return cache[dev];
 }
 
+template <int KS, int WR>
+hipError_t launch_large(const InprojArgs &A, int ft, hipStream_t stream)
+{
+    using C = LargeCfg<KS, WR>;
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(inproj_large_kernel<KS, WR>),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((inproj_large_kernel<KS, WR>), dim3(ft, (A.rows + C::rows - 1) / C::rows), dim3(C::nt * KS),
+                       C::lds, stream, A);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_inproj_pack(const InprojPackArgs &P, hipStream_t stream)
@@ -464,21 +507,13 @@ hipError_t launch_inproj(const InprojArgs &A, hipStream_t stream)
             else hipLaunchKernelGGL((inproj_small_kernel<2, 1>), grid, dim3(512), 0, stream, A);
         }
     } else {
-        static const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void *>(inproj_large_kernel<1>),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLargeLds);
-        static const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(inproj_large_kernel<2>),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                         (int)(2 * kLargeLds));
-        const dim3 grid((features + kFeat - 1) / kFeat, (A.rows + kRows - 1) / kRows);
-        // two input shares a workgroup while the tiles leave a compute unit
-        // to each workgroup
-        if ((int)(grid.x * grid.y) <= compute_units()) {
-            if (e2 != hipSuccess) return e2;
-            hipLaunchKernelGGL((inproj_large_kernel<2>), grid, dim3(512), 2 * kLargeLds, stream, A);
-        } else {
-            if (e1 != hipSuccess) return e1;
-            hipLaunchKernelGGL((inproj_large_kernel<1>), grid, dim3(256), kLargeLds, stream, A);
-        }
+        // two input shares a workgroup while 128-row tiles leave a compute
+        // unit to each workgroup; 256-row tiles for long launches
+        const int ft = (features + kFeat - 1) / kFeat;
+        const int t128 = ft * ((A.rows + 127) / 128);
+        if (t128 <= compute_units()) return launch_large<2, 2>(A, ft, stream);
+        if (A.rows > 512) return launch_large<1, 4>(A, ft, stream);
+        return launch_large<1, 2>(A, ft, stream);
     }
     return hipGetLastError();
 }
