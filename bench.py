@@ -456,6 +456,21 @@ def inproj_work(shape, rows, hidden, group):
     return nbytes, 2 * rows * n * hidden
 
 
+def inproj_kernel_name(torch, dev, shape, rows):
+    """The kernel instantiation gdn_inproj_affine4 launches for ``rows`` (the
+    library picks it by tile count against the compute units), which names
+    its measured traffic."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    features = shape.channels + 2 * shape.hv
+    if rows <= 32:
+        blocks = (features + 15) // 16
+        return f"inproj_small_kernel<{1 if rows <= 16 else 2}, {2 if blocks // 2 >= cus else 1}>"
+    ft = (features + 127) // 128
+    if ft * ((rows + 127) // 128) <= cus:
+        return "inproj_large_kernel<2, 2>"
+    return "inproj_large_kernel<1, 4>" if rows > 512 else "inproj_large_kernel<1, 2>"
+
+
 def bench_inproj(args, torch, gdn, gi, dev):
     """One step = one gdn_inproj_affine4 call (hidden rows -> qkv, a, b)."""
     shape, rows, hidden, group, seed = gi.inproj_workload(args.workload)
@@ -477,7 +492,7 @@ def bench_inproj(args, torch, gdn, gi, dev):
     nbytes, flops = inproj_work(shape, rows, hidden, group)
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (MFMA_BF16_PEAK_TFS * 1e12)
-    kernel = "inproj_small_kernel" if rows <= 32 else "inproj_large_kernel"
+    kernel = inproj_kernel_name(torch, dev, shape, rows)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(nbytes / (avg_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(t_hbm / (avg_ms * 1e-3), 4)}
