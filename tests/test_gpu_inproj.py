@@ -70,6 +70,13 @@ CASES = {
     # one ragged)
     "27b-rows500-g64": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 500, 256, 64),
     "27b-rows700-g32": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 700, 384, 32),
+    # the smallest hidden size (one 128-input chunk): seven of the small
+    # kernel's eight waves without a chunk; one 64-input chunk a share; one
+    # pair of chunks for 128- and 256-row tiles
+    "rows3-h128-g128": (gi.SMALL, 3, 128, 128),
+    "rows40-h128-g64": (gi.SMALL, 40, 128, 64),
+    "27b-rows400-h128-g32": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 400, 128, 32),
+    "27b-rows600-h128-g128": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 600, 128, 128),
 }
 
 
