@@ -6,8 +6,10 @@
 // run through affine-4 kernels; the format is MLX's affine quantisation).
 //
 // Each weight is expanded to bf16 (s * q + b in fp32, rounded to nearest
-// even) right before it enters v_mfma_f32_16x16x32_bf16, as MLX's own matrix
-// kernels do; products accumulate in fp32 and the outputs are rounded to bf16.
+// even) right before it enters the matrix cores (v_mfma_f32_16x16x32_bf16
+// in the small kernel, v_mfma_f32_32x32x16_bf16 in the large one), as MLX's
+// own matrix kernels do; products accumulate in fp32 and the outputs are
+// rounded to bf16.
 //
 // The small kernel takes inputs in chunks of 128.  Within a chunk, lane
 // (l16, g4) of a wave owns inputs [32 g4, 32 g4 + 32): four consecutive code
@@ -15,15 +17,17 @@
 // 32 g4 + 8 s .. + 8 of both operands (A: row l16 of x, B: feature l16 of W),
 // so that every input meets its weight once.  Those 32 inputs lie in one
 // group (group sizes 32, 64, 128): one scale and one bias serve the lane for
-// the chunk.  The large kernel expands weights the same way, 32 inputs of one
-// feature a thread, into LDS.
+// the chunk.  The large kernel expands weights the same way, 16 or 32 inputs
+// of one feature (a pair or a quad of code words) a thread, into LDS.
 //
-//   small  (rows <= 32): a workgroup is 16 features x 16 or 32 rows; its 8
-//          waves split the inputs.
-//   large  a workgroup is 128 features x 128 rows on 32 x 32 matrix-core
-//          blocks; the chunk of x and the chunk of weights (expanded once)
-//          are staged in LDS for its four waves, and the output tile leaves
-//          through LDS in whole rows where it lies inside qkv.
+//   small  (rows <= 32): a workgroup is one or two blocks of 16 features x
+//          16 or 32 rows; its 8 waves split the inputs.
+//   large  a workgroup is 128 features x 128 or 256 rows on 32 x 32
+//          matrix-core blocks; the chunk of x and the chunk of weights
+//          (expanded once) are staged in LDS for its waves, and the output
+//          tile leaves through LDS in whole rows where it lies inside qkv.
+//          Launches with few tiles split the inputs between two groups of
+//          waves in each workgroup.
 //
 // Weights come in a tiled layout, repacked once from MLX's by
 // gdn_inproj_pack_affine4: features in blocks of 16 (the last padded with
