@@ -125,9 +125,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "libgdn's bench measures one GPU; --gpus must be 1 "
                                    "(the verify path shards by stream or key-head group with no "
-                                   "exchange, see the design notes)"}))
+                                   "exchange between GPUs)"}))
         sys.exit(2)
 
     import torch
