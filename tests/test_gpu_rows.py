@@ -89,6 +89,22 @@ def test_tree_matches_oracle_and_commit():
             assert np.array_equal(bits16(tail[s]), bits16(tsnap[r])), s
 
 
+def test_small_heads_windows_and_trees():
+    """dk = dv = 64 (the small layer's heads, their own instantiation of the
+    row kernel) beyond one row: ragged windows of up to 16 rows and draft
+    trees against the oracle (outputs, state snapshots, tail snapshots)."""
+    shape = gi.SMALL
+    lengths = [16, 1, 7, 12, 3, 16]
+    b = gi.make_batch(shape, lengths, seed=91)
+    announce(f"recur_window small heads lengths={lengths} seed=91")
+    out, tsnap, ssnap = run_window(b)
+    check_against_oracle(b, out, tsnap, ssnap)
+    bt = gi.make_batch(shape, lengths, seed=92, tree=True)
+    announce(f"recur_tree small heads lengths={lengths} seed=92")
+    out, tsnap, ssnap = run_window(bt, tree=True)
+    check_against_oracle(bt, out, tsnap, ssnap, tree=True)
+
+
 @pytest.mark.parametrize("name,n_streams", [("step", 1), ("window2b", 1), ("ragged27b", 3)])
 def test_window_rows_equal_one_row_steps_bitwise(name, n_streams):
     shape, lengths, kw = gi.workload(name)
