@@ -86,16 +86,22 @@ void gdn_oracle_gates(double a, double b, double a_log, double dt_bias,
 
 /* Causal depthwise conv of channels [c0, c0 + count) of one row: taps[j] is
  * the raw row x_{t-3+j} (taps[3] = the current row).  Writes the conv output
- * before (optional) and after SiLU, indexed from c0. */
+ * before (optional) and after SiLU, indexed from c0, and (optional) the
+ * magnitude of each output: the magnitude of the conv's terms, sum_j
+ * |w_j x_j|, times SiLU's gate sigmoid(y) (silu(y) = y sigmoid(y)). */
 static void conv_silu_range(const float *conv_w, const uint16_t *const taps[4], int c0, int count,
-                            double *pre, double *post)
+                            double *pre, double *post, double *mag)
 {
     for (int c = c0; c < c0 + count; ++c) {
-        double y = 0.0;
-        for (int j = 0; j < CONV_W; ++j)
-            y += (double)conv_w[(size_t)c * CONV_W + j] * bf16_value(taps[j][c]);
+        double y = 0.0, ymag = 0.0;
+        for (int j = 0; j < CONV_W; ++j) {
+            const double term = (double)conv_w[(size_t)c * CONV_W + j] * bf16_value(taps[j][c]);
+            y += term;
+            ymag += fabs(term);
+        }
         if (pre) pre[c - c0] = y;
         if (post) post[c - c0] = silu(y);
+        if (mag) mag[c - c0] = sigmoid(y) * ymag;
     }
 }
 
@@ -103,21 +109,25 @@ static void conv_silu_range(const float *conv_w, const uint16_t *const taps[4], 
 void gdn_oracle_conv_silu(int32_t C, const float *conv_w, const uint16_t *const taps[4],
                           double *pre, double *post)
 {
-    conv_silu_range(conv_w, taps, 0, C, pre, post);
+    conv_silu_range(conv_w, taps, 0, C, pre, post, NULL);
 }
 
 /* Everything value head h needs from one row: normalised q and k of its key
  * head, its v, and its gates.  Only the conv channels of those heads are
- * computed: q of key head kh, k of key head kh, v of value head h. */
+ * computed: q of key head kh, k of key head kh, v of value head h.  With mag
+ * (optional: [dk] q, [dk] k, [dv] v) also the magnitude of each (the conv's
+ * term magnitude through SiLU's gate, then the same normalisation scale). */
 static void head_inputs(const oracle_shape *s, const float *conv_w, const uint16_t *const taps[4],
                         int h, double a, double b, double a_log, double dt_bias,
-                        double *qhat, double *khat, double *v, double *alpha, double *beta)
+                        double *qhat, double *khat, double *v, double *alpha, double *beta,
+                        double *mag)
 {
     const int r = s->hv / s->hk;
     const int kh = h / r;
-    conv_silu_range(conv_w, taps, kh * s->dk, s->dk, NULL, qhat);
-    conv_silu_range(conv_w, taps, s->hk * s->dk + kh * s->dk, s->dk, NULL, khat);
-    conv_silu_range(conv_w, taps, 2 * s->hk * s->dk + h * s->dv, s->dv, NULL, v);
+    double *qm = mag, *km = mag ? mag + s->dk : NULL, *vm = mag ? mag + 2 * s->dk : NULL;
+    conv_silu_range(conv_w, taps, kh * s->dk, s->dk, NULL, qhat, qm);
+    conv_silu_range(conv_w, taps, s->hk * s->dk + kh * s->dk, s->dk, NULL, khat, km);
+    conv_silu_range(conv_w, taps, 2 * s->hk * s->dk + h * s->dv, s->dv, NULL, v, vm);
     double qq = 0.0, kk = 0.0;
     for (int i = 0; i < s->dk; ++i) {
         qq += qhat[i] * qhat[i];
@@ -128,6 +138,10 @@ static void head_inputs(const oracle_shape *s, const float *conv_w, const uint16
     for (int i = 0; i < s->dk; ++i) {
         qhat[i] = qhat[i] * qs;
         khat[i] = khat[i] * ks;
+        if (mag) {
+            qm[i] *= qs;
+            km[i] *= ks;
+        }
     }
     gdn_oracle_gates(a, b, a_log, dt_bias, alpha, beta);
 }
@@ -155,26 +169,78 @@ static void delta_step(int dk, int dv, const double *khat, const double *qhat,
     }
 }
 
+/* The magnitudes of one step, for error bounds that respect cancellation
+ * (a readout o_j = sum_i M_ij q_i, a write v_j - alpha (k^T M)_j or a conv
+ * output can be far smaller than the terms it adds up, and no finite-
+ * precision evaluation keeps a small relative error on such a value).  The
+ * step that starts from state M is carried out on magnitudes: |M| for the
+ * state, km, qm, vm for khat, qhat and v, every sum as the sum of its terms'
+ * magnitudes and every product as the product of magnitudes (alpha, beta >= 0):
+ *     U = |M|^T km,   A = alpha (|M| + beta km U^T) + beta km vm^T,   O = A^T qm,
+ * and the row's write delta = beta (v - alpha k^T M) has magnitude
+ * W = beta (vm + alpha U).  A ([dk][dv]) gets the new state's magnitudes, O
+ * (optional) the readout's, W (optional) the write's; U is scratch [dv].
+ * The magnitudes start from the state a row is given, not from magnitudes
+ * carried across rows: carried, alpha (I + beta km km^T) would grow them by
+ * up to alpha (1 + beta) a row, where the step itself, alpha (I - beta k
+ * k^T), never grows the state. */
+static void magnitude_step(int dk, int dv, const double *km, const double *qm, const double *vm,
+                           double alpha, double beta, const double *M, double *A, double *U,
+                           double *O, double *W)
+{
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += km[i] * fabs(M[(size_t)i * dv + j]);
+        U[j] = acc;
+        if (W) W[j] = beta * (vm[j] + alpha * acc);
+    }
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            A[(size_t)i * dv + j] = alpha * (fabs(M[(size_t)i * dv + j]) + beta * km[i] * U[j]) +
+                                    beta * km[i] * vm[j];
+    if (O)
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += A[(size_t)i * dv + j] * qm[i];
+            O[j] = acc;
+        }
+}
+
 /* The recurrence alone, on inputs given directly: T rows of alpha, beta,
  * khat [T][dk], qhat [T][dk] and v [T][dv], from M0 [dk][dv].  Writes the
  * final state and o [T][dv]; M_all [T][dk][dv] (optional) gets every row's
- * state. */
+ * state, o_mag [T][dv] (optional) each readout's magnitude (magnitude_step
+ * with |khat|, |qhat| and |v|). */
 void gdn_oracle_raw_recurrence(int32_t dk, int32_t dv, int32_t T, const double *alpha,
                                const double *beta, const double *khat, const double *qhat,
                                const double *v, const double *M0, double *M_out,
-                               double *o, double *M_all)
+                               double *o, double *M_all, double *o_mag)
 {
-    double *M = malloc(sizeof(double) * (size_t)dk * dv);
+    const size_t msz = (size_t)dk * dv;
+    double *M = malloc(sizeof(double) * msz);
     double *tmp = malloc(sizeof(double) * (size_t)dv);
-    memcpy(M, M0, sizeof(double) * (size_t)dk * dv);
+    double *A = o_mag ? malloc(sizeof(double) * msz) : NULL;
+    double *am = o_mag ? malloc(sizeof(double) * (size_t)(2 * dk + dv)) : NULL;
+    memcpy(M, M0, sizeof(double) * msz);
     for (int t = 0; t < T; ++t) {
-        delta_step(dk, dv, khat + (size_t)t * dk, qhat + (size_t)t * dk, v + (size_t)t * dv,
-                   alpha[t], beta[t], M, tmp, o + (size_t)t * dv);
-        if (M_all) memcpy(M_all + (size_t)t * dk * dv, M, sizeof(double) * (size_t)dk * dv);
+        const double *k = khat + (size_t)t * dk, *q = qhat + (size_t)t * dk, *vt = v + (size_t)t * dv;
+        if (A) {
+            for (int i = 0; i < dk; ++i) {
+                am[i] = fabs(k[i]);
+                am[dk + i] = fabs(q[i]);
+            }
+            for (int j = 0; j < dv; ++j) am[2 * dk + j] = fabs(vt[j]);
+            magnitude_step(dk, dv, am, am + dk, am + 2 * dk, alpha[t], beta[t], M, A, tmp,
+                           o_mag + (size_t)t * dv, NULL);
+        }
+        delta_step(dk, dv, k, q, vt, alpha[t], beta[t], M, tmp, o + (size_t)t * dv);
+        if (M_all) memcpy(M_all + (size_t)t * msz, M, sizeof(double) * msz);
     }
-    memcpy(M_out, M, sizeof(double) * (size_t)dk * dv);
+    memcpy(M_out, M, sizeof(double) * msz);
     free(M);
     free(tmp);
+    free(A);
+    free(am);
 }
 
 /*
@@ -205,6 +271,10 @@ typedef struct {
     double *log_alpha;             /* [rows][hv] or NULL: each row's decay        */
     double *log_delta;             /* [rows][hv][dv] or NULL: each row's write    */
     double *log_key;               /* [rows][hk][dk] or NULL: each row's khat     */
+    double *o_mag;                 /* [rows][hv][dv] or NULL: magnitude of each o */
+    double *log_delta_mag;         /* [rows][hv][dv] or NULL: ... of each write   */
+    float *snap_mag;               /* [rows][hv][dk][dv] or NULL: ... of each state */
+    double *final_mag;             /* [hv][dk][dv] or NULL: ... of the last state */
 } stream_job;
 
 /* Per-row tails of a stream (bf16 bits): node tails follow the parents. */
@@ -229,11 +299,14 @@ static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
     const int C = channels(s), dk = s->dk, dv = s->dv;
     const size_t msz = (size_t)dk * dv;
     const int is_tree = jb->parent != NULL;
+    const int mags = jb->o_mag || jb->log_delta_mag || jb->snap_mag || jb->final_mag;
     /* a chain needs only the running state; a tree keeps every node's */
     double *states = malloc(sizeof(double) * msz * (is_tree ? (size_t)jb->rows : 1));
     double *cur = malloc(sizeof(double) * msz);
+    double *amag = mags ? malloc(sizeof(double) * msz) : NULL;   /* the row's state magnitudes */
     double *qhat = malloc(sizeof(double) * dk), *khat = malloc(sizeof(double) * dk);
     double *v = malloc(sizeof(double) * dv), *tmp = malloc(sizeof(double) * dv);
+    double *inmag = malloc(sizeof(double) * (size_t)(2 * dk + dv));   /* q, k, v magnitudes */
     const double *M0 = jb->state0 + (size_t)h * msz;
     memcpy(cur, M0, sizeof(double) * msz);
     for (int i = 0; i < jb->rows; ++i) {
@@ -244,14 +317,18 @@ static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
         double alpha, beta;
         head_inputs(s, jb->conv_w, taps, h, bf16_value(jb->a[(size_t)i * s->hv + h]),
                     bf16_value(jb->b[(size_t)i * s->hv + h]), jb->a_log[h], jb->dt_bias[h],
-                    qhat, khat, v, &alpha, &beta);
-        delta_step(dk, dv, khat, qhat, v, alpha, beta, cur,
-                   tmp, jb->o + ((size_t)i * s->hv + h) * dv);
+                    qhat, khat, v, &alpha, &beta, mags ? inmag : NULL);
+        const size_t oo = ((size_t)i * s->hv + h) * dv;
+        if (mags)   /* from the state the row starts from, before the update */
+            magnitude_step(dk, dv, inmag + dk, inmag, inmag + 2 * dk, alpha, beta, cur, amag, tmp,
+                           jb->o_mag ? jb->o_mag + oo : NULL,
+                           jb->log_delta_mag ? jb->log_delta_mag + oo : NULL);
+        delta_step(dk, dv, khat, qhat, v, alpha, beta, cur, tmp, jb->o + oo);
         /* the log: tmp holds k^T M of the row's starting state */
         if (jb->log_alpha) jb->log_alpha[(size_t)i * s->hv + h] = alpha;
         if (jb->log_delta)
             for (int j = 0; j < dv; ++j)
-                jb->log_delta[((size_t)i * s->hv + h) * dv + j] = beta * (v[j] - alpha * tmp[j]);
+                jb->log_delta[oo + j] = beta * (v[j] - alpha * tmp[j]);
         if (jb->log_key && h % (s->hv / s->hk) == 0)   /* one value head per key head writes it */
             memcpy(jb->log_key + ((size_t)i * s->hk + h / (s->hv / s->hk)) * dk, khat,
                    sizeof(double) * dk);
@@ -260,10 +337,15 @@ static void stream_head(const stream_job *jb, const uint16_t *tails, int h)
         if (jb->snap64) memcpy(jb->snap64 + off, cur, sizeof(double) * msz);
         if (jb->snap32)
             for (size_t e = 0; e < msz; ++e) jb->snap32[off + e] = (float)cur[e];
+        if (jb->snap_mag)
+            for (size_t e = 0; e < msz; ++e) jb->snap_mag[off + e] = (float)amag[e];
     }
     if (jb->final_state && jb->rows > 0)
         memcpy(jb->final_state + (size_t)h * msz, cur, sizeof(double) * msz);
-    free(states); free(cur); free(qhat); free(khat); free(v); free(tmp);
+    if (jb->final_mag)
+        for (size_t e = 0; e < msz; ++e)
+            jb->final_mag[(size_t)h * msz + e] = jb->rows > 0 ? amag[e] : fabs(M0[e]);
+    free(states); free(cur); free(amag); free(qhat); free(khat); free(v); free(tmp); free(inmag);
 }
 
 static void finish_tails(const stream_job *jb, const uint16_t *tails)
@@ -316,14 +398,18 @@ static void fill_job(stream_job *jb, const oracle_shape *s, const float *conv_w,
  * [n][3][C] bf16 bits, state [n][hv][dk][dv] fp64.  Outputs (any may be NULL
  * but o): o [R][hv][dv] fp64, tail_snap [R][3][C], snap64 / snap32
  * [R][hv][dk][dv], and the log: log_alpha [R][hv], log_delta [R][hv][dv],
- * log_key [R][hk][dk].  Returns 0, or -1 on a malformed layout.
+ * log_key [R][hk][dk]; and the magnitudes (the step on magnitudes, see
+ * magnitude_step) of every o (o_mag [R][hv][dv]), every write (log_delta_mag
+ * [R][hv][dv]) and every row's state (snap_mag [R][hv][dk][dv], fp32).
+ * Returns 0, or -1 on a malformed layout.
  */
 int gdn_oracle_window(const oracle_shape *s, const float *conv_w, const float *a_log,
                       const float *dt_bias, int32_t n, const int32_t *row_start,
                       const int32_t *parent, const uint16_t *qkv, const uint16_t *a,
                       const uint16_t *b, const uint16_t *tail, const double *state,
                       double *o, uint16_t *tail_snap, double *snap64, float *snap32,
-                      double *log_alpha, double *log_delta, double *log_key)
+                      double *log_alpha, double *log_delta, double *log_key, double *o_mag,
+                      double *log_delta_mag, float *snap_mag)
 {
     if (s->hk <= 0 || s->hv <= 0 || s->hv % s->hk || s->dk <= 0 || s->dv <= 0 || n < 0)
         return -1;
@@ -346,6 +432,9 @@ int gdn_oracle_window(const oracle_shape *s, const float *conv_w, const float *a
         if (log_alpha) jobs[st].log_alpha = log_alpha + (size_t)r0 * s->hv;
         if (log_delta) jobs[st].log_delta = log_delta + (size_t)r0 * s->hv * s->dv;
         if (log_key) jobs[st].log_key = log_key + (size_t)r0 * s->hk * s->dk;
+        if (o_mag) jobs[st].o_mag = o_mag + (size_t)r0 * s->hv * s->dv;
+        if (log_delta_mag) jobs[st].log_delta_mag = log_delta_mag + (size_t)r0 * s->hv * s->dv;
+        if (snap_mag) jobs[st].snap_mag = snap_mag + (size_t)r0 * s->hv * msz;
     }
     run_streams(jobs, n, s->hv);
     free(jobs);
@@ -356,13 +445,16 @@ int gdn_oracle_window(const oracle_shape *s, const float *conv_w, const float *a
  * Prompt passes: each of the n prompts runs its rows as one chain from its
  * stream's state and tail, and its final state and tail replace them (in
  * place).  state is fp64 [n][hv][dk][dv] in/out, tail [n][3][C] bf16 bits
- * in/out, o [T][hv][dv] fp64.  A prompt of zero rows leaves its stream as it
- * was.
+ * in/out, o [T][hv][dv] fp64; optional magnitudes (see magnitude_step) of
+ * every o (o_mag [T][hv][dv]) and of each final state (final_mag
+ * [n][hv][dk][dv], |state| for an empty prompt).  A prompt of zero rows leaves
+ * its stream as it was.
  */
 int gdn_oracle_prefill(const oracle_shape *s, const float *conv_w, const float *a_log,
                        const float *dt_bias, int32_t n, const int32_t *seq_start,
                        const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
-                       uint16_t *tail, double *state, double *o)
+                       uint16_t *tail, double *state, double *o, double *o_mag,
+                       double *final_mag)
 {
     if (s->hk <= 0 || s->hv <= 0 || s->hv % s->hk || s->dk <= 0 || s->dv <= 0 || n < 0)
         return -1;
@@ -382,6 +474,8 @@ int gdn_oracle_prefill(const oracle_shape *s, const float *conv_w, const float *
         fill_job(&jobs[st], s, conv_w, a_log, dt_bias, seq_start, st, qkv, a, b, tail_in,
                  state_in);
         jobs[st].o = o + (size_t)seq_start[st] * s->hv * s->dv;
+        if (o_mag) jobs[st].o_mag = o_mag + (size_t)seq_start[st] * s->hv * s->dv;
+        if (final_mag) jobs[st].final_mag = final_mag + (size_t)st * ssz;
         jobs[st].final_state = state + (size_t)st * ssz;
         jobs[st].final_tail = tail + (size_t)st * TAIL * C;
     }

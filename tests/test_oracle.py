@@ -121,7 +121,7 @@ def test_silu_identities():
 # --------------------------------------------------------------------------- raw recurrence
 
 def _read_golden():
-    recs = {"in": [], "o": [], "M": []}
+    recs = {"in": [], "o": [], "M": [], "mag": []}
     M0 = None
     with open(os.path.join(GOLDEN, "raw_recurrence_worked.txt")) as fh:
         for line in fh:
@@ -142,12 +142,53 @@ def test_hand_worked_example():
     rows = np.array(recs["in"])
     alpha, beta = rows[:, 1], rows[:, 2]
     k, v, q = rows[:, 3:5], rows[:, 5:7], rows[:, 7:9]
-    M, o, M_all = oracle.raw_recurrence(alpha, beta, k, q, v, M0, keep_all=True)
+    M, o, M_all, mag = oracle.raw_recurrence(alpha, beta, k, q, v, M0, keep_all=True, mag=True)
     for t, rec in enumerate(recs["o"]):
         assert np.allclose(o[t], rec[1:], rtol=0, atol=1e-14), (t, o[t], rec)
     for t, rec in enumerate(recs["M"]):
         assert np.allclose(M_all[t].ravel(), rec[1:], rtol=0, atol=1e-14), (t, M_all[t], rec)
+    for t, rec in enumerate(recs["mag"]):
+        assert np.allclose(mag[t], rec[1:], rtol=0, atol=1e-14), (t, mag[t], rec)
     assert np.array_equal(M, M_all[-1])
+    assert len(recs["mag"]) == len(recs["o"]) == 4
+
+
+def test_readout_magnitude_bounds_and_equalities():
+    """The readout magnitude (the row's step carried out on magnitudes) is at least
+    |o_j|, equals it where no term has the other sign, scales with |q|, is
+    read from the state after the row's update, and counts the delta rule's
+    subtraction as a term (a write of what the state already holds changes
+    nothing, yet triples that row's magnitude)."""
+    rng = np.random.default_rng(5)
+    dk, dv, T = 6, 5, 7
+    M0 = rng.standard_normal((dk, dv))
+    k = rng.standard_normal((T, dk)); k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    alpha, beta = rng.uniform(0.2, 1.0, T), rng.uniform(0.0, 1.0, T)
+    _, o, _, mag = oracle.raw_recurrence(alpha, beta, k, q, v, M0, mag=True)
+    assert np.all(mag >= np.abs(o) * (1 - 1e-15))
+    assert np.any(mag > 1.5 * np.abs(o))            # random signs do cancel
+    _, o2, _, mag2 = oracle.raw_recurrence(alpha, beta, k, -3.0 * q, v, M0, mag=True)
+    assert np.allclose(o2, -3.0 * o, rtol=1e-14, atol=0) and np.allclose(mag2, 3.0 * mag, rtol=1e-14)
+    # one sign: no write (beta = 0), non-negative state and query
+    Mp, qp = np.abs(M0), np.abs(q)
+    _, o3, _, mag3 = oracle.raw_recurrence(alpha, np.zeros(T), k, qp, v, Mp, mag=True)
+    assert np.allclose(mag3, o3, rtol=1e-15, atol=0)
+    for i in range(dk):
+        e = np.zeros((1, dk)); e[0, i] = 1.0
+        # a unit write from the zero state with q = k = e_i: o = v, magnitude |v|
+        # (the state before the update would give 0)
+        _, o4, _, mag4 = oracle.raw_recurrence([1.0], [1.0], e, e, v[:1], np.zeros((dk, dv)), mag=True)
+        assert np.array_equal(o4[0], v[0]) and np.array_equal(mag4[0], np.abs(v[0]))
+        # writing back row i of the state (v = M0^T e_i, alpha = beta = 1):
+        # M is unchanged, and row i's magnitude is |M0_i| + |M0_i| (the
+        # subtracted readout) + |v| = 3 |M0_i|
+        _, o5, _, mag5 = oracle.raw_recurrence([1.0], [1.0], e, e, M0[i][None], M0, mag=True)
+        assert np.array_equal(o5[0], M0[i]) and np.allclose(mag5[0], 3 * np.abs(M0[i]), rtol=1e-15)
+        # and with alpha = 1/2: the old state and the subtracted term halve
+        _, _, _, mag6 = oracle.raw_recurrence([0.5], [1.0], e, e, M0[i][None], M0, mag=True)
+        assert np.allclose(mag6[0], 2 * np.abs(M0[i]), rtol=1e-15)
 
 
 def test_delta_write_exact_with_unit_axis_key():
@@ -450,13 +491,108 @@ def test_pure_decay_through_the_whole_path():
         assert np.allclose(res["o"][t], res["o"][0] * 0.5 ** t, rtol=1e-14, atol=1e-18)
 
 
+def _signed_inputs(shape, lengths, seed, q_sign, k_sign, v_sign):
+    """Conv weights that pass the current row through (tap 3 = 1, so no conv
+    output cancels) and raw rows whose q, k and v channels have the given
+    signs, which SiLU keeps in qhat, khat and v; the initial state is made
+    non-negative."""
+    batch = gi.make_batch(shape, lengths, seed=seed)
+    d = _np_batch(batch)
+    w = np.zeros_like(d["conv_w"]); w[:, 3] = 1.0
+    d["conv_w"] = w
+    hkdk = shape.hk * shape.dk
+    vals = np.abs(batch.qkv.float().numpy()) + 0.25
+    vals[:, :hkdk] *= q_sign
+    vals[:, hkdk:2 * hkdk] *= k_sign
+    vals[:, 2 * hkdk:] *= v_sign
+    d["qkv"] = bf16(vals)
+    d["state"] = np.abs(d["state"])
+    return d
+
+
+def test_magnitudes_through_the_whole_path():
+    """The magnitudes of full windows: never below the value's own size;
+    equal to it where no term has the other sign (no write, a non-negative
+    state read by a positive query; a first row whose negative v meets a
+    positive key on a non-negative state; a first write from the zero state);
+    a tree row's magnitudes are those of the chain over its path."""
+    shape = gi.Shape(hk=2, hv=4, dk=8, dv=6)
+    batch = gi.make_batch(shape, [5, 3], seed=20)
+    d = _np_batch(batch)
+    res = _run_window(shape, d, log=True, snap_mag=True)
+    assert np.all(res["o_mag"] >= np.abs(res["o"]) * (1 - 1e-14))
+    assert np.all(res["log_delta_mag"] >= np.abs(res["log_delta"]) * (1 - 1e-14))
+    assert np.all(res["snap_mag"] >= np.abs(res["snap64"]).astype(np.float32) * (1 - 1e-6))
+    # no write, non-negative state, positive query: every magnitude is the value
+    dq = _signed_inputs(shape, [4, 2], 21, 1.0, 1.0, 1.0)
+    dq["b"][:] = BF16_NEG_INF
+    r = _run_window(shape, dq, snap_mag=True)
+    assert np.all(r["o"] > 0) and np.allclose(r["o_mag"], r["o"], rtol=1e-14, atol=0)
+    assert np.allclose(r["snap_mag"], r["snap64"], rtol=1e-6, atol=0)
+    # first rows: negative v, positive key, non-negative state: |delta| = its magnitude
+    dk_ = _signed_inputs(shape, [1, 1, 1], 22, 1.0, 1.0, -1.0)
+    r = _run_window(shape, dk_, log=True)
+    assert np.all(r["log_delta"] < 0)
+    assert np.allclose(r["log_delta_mag"], np.abs(r["log_delta"]), rtol=1e-14, atol=0)
+    # from the zero state the write is beta v: magnitude beta |v| = |delta|
+    dz = _signed_inputs(shape, [3, 2], 23, 1.0, -1.0, 1.0)
+    dz["qkv"] = bf16(batch.qkv.float().numpy()[:5])       # mixed signs again
+    dz["state"] = np.zeros_like(dz["state"])
+    r = _run_window(shape, dz, log=True)
+    first = [0, 3]
+    assert np.allclose(r["log_delta_mag"][first], np.abs(r["log_delta"][first]), rtol=1e-15, atol=0)
+    # a tree: each row's magnitudes are those of the chain over its path
+    tb = _tree_batch([6, 4], seed=24)
+    td = _np_batch(tb)
+    tr = oracle.tree(TINY, td["conv_w"], td["a_log"], td["dt_bias"], td["row_start"], tb.parent.numpy(),
+                     td["qkv"], td["a"], td["b"], td["tail"], td["state"], snap_mag=True)
+    par = tb.parent.numpy()
+    rs = td["row_start"]
+    for st in range(2):
+        local = par[rs[st]:rs[st + 1]].tolist()
+        for leaf in range(len(local)):
+            rows = [int(rs[st]) + i for i in gi.path_to_root(local, leaf)]
+            ch = oracle.window(TINY, td["conv_w"], td["a_log"], td["dt_bias"], np.array([0, len(rows)], np.int32),
+                               td["qkv"][rows], td["a"][rows], td["b"][rows], td["tail"][st:st + 1],
+                               td["state"][st:st + 1], snap_mag=True)
+            assert np.array_equal(ch["o_mag"], tr["o_mag"][rows])
+            assert np.array_equal(ch["snap_mag"], tr["snap_mag"][rows])
+
+
+def test_conv_cancellation_counts_its_terms():
+    """v channels with weights (1, 0, 0, -1) on equal oldest and current
+    rows: the conv output cancels to exactly 0, so v = 0 and, from the zero
+    state, the write is 0; its magnitude is beta times sigmoid(0) (SiLU's gate)
+    times the conv's terms |x| + |x|, i.e. |x| / 2 with b = 0 (beta = 1/2)."""
+    shape = gi.Shape(hk=1, hv=2, dk=4, dv=3)
+    batch = gi.make_batch(shape, [1], seed=25, zero_state=True)
+    d = _np_batch(batch)
+    hkdk = shape.hk * shape.dk
+    w = np.zeros_like(d["conv_w"]); w[:, 3] = 1.0
+    w[2 * hkdk:, 0] = 1.0
+    w[2 * hkdk:, 3] = -1.0
+    d["conv_w"] = w
+    x = d["qkv"][0]
+    d["tail"][0, 0, 2 * hkdk:] = x[2 * hkdk:]
+    d["b"][:] = bf16(0.0)
+    r = _run_window(shape, d, log=True)
+    xv = (x[2 * hkdk:].astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(shape.hv, shape.dv)
+    assert np.all(r["log_delta"] == 0) and np.all(r["o"] == 0)
+    assert np.allclose(r["log_delta_mag"][0], 0.5 * np.abs(xv), rtol=1e-15, atol=0)
+    assert np.all(r["o_mag"] > 0)
+
+
 def test_prefill_matches_window_and_updates_in_place():
     batch = gi.make_batch(TINY, [7, 3, 1], seed=17)
     d = _np_batch(batch)
     w = _run_window(TINY, d)
-    o, st, tl = oracle.prefill(TINY, d["conv_w"], d["a_log"], d["dt_bias"], d["row_start"],
-                               d["qkv"], d["a"], d["b"], d["tail"], d["state"])
+    o, st, tl, om, fm = oracle.prefill(TINY, d["conv_w"], d["a_log"], d["dt_bias"], d["row_start"],
+                                       d["qkv"], d["a"], d["b"], d["tail"], d["state"], mag=True)
     assert np.array_equal(o, w["o"])
+    assert np.array_equal(om, w["o_mag"])
+    wm = _run_window(TINY, d, snap_mag=True)
+    for s_ in range(3):
+        assert np.array_equal(fm[s_].astype(np.float32), wm["snap_mag"][int(d["row_start"][s_ + 1]) - 1])
     rs = d["row_start"]
     for s in range(3):
         last = int(rs[s + 1]) - 1
