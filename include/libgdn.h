@@ -146,14 +146,20 @@ int gdn_recur_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
 /*
  * Commit of the accepted rows: only each stream's accepted path is kept (page
  * "perf(qwen27 cuda): reduce repeated-prompt TTFT", commit note on the qwen3_5
- * checkpoint with the 27B's shapes).  accept_row [n] int32, device: the packed
- * index of the stream's accepted row in tail_snap / state_snap, or -1 to keep
- * the stream as it is; an index outside [-1, total_rows) is skipped.  Copies
- * that row's recorded state and tail over the stream's state and conv_tail.
+ * checkpoint with the 27B's shapes).  Copies the accepted row's recorded state
+ * and tail over the stream's state and conv_tail.
+ *   row_start  [n+1] int32, device: the layout of the gdn_recur_window /
+ *              gdn_recur_tree call that recorded the snapshots
+ *   accept_row [n] int32, device: the packed index of the stream's accepted
+ *              row, within its own window [row_start[s], row_start[s+1]), or
+ *              -1 to keep the stream as it is.  Any other value, or a window
+ *              that ends past total_rows, skips the stream (a row of another
+ *              stream's window is never copied).
+ *   tail_snap [total_rows][3][C], state_snap [total_rows][hv][dk][dv]: read
  */
 int gdn_commit(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,
-               const int32_t *accept_row, const uint16_t *tail_snap, const float *state_snap,
-               uint16_t *conv_tail, float *state, void *stream);
+               const int32_t *row_start, const int32_t *accept_row, const uint16_t *tail_snap,
+               const float *state_snap, uint16_t *conv_tail, float *state, void *stream);
 
 /*
  * Verify windows or trees that LOG every row instead of recording its state
@@ -206,7 +212,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int32_t n_seqs, int32
  * together share one pass: page "perf(qwen27 cuda): reduce repeated-prompt
  * TTFT", commit note on the lane host admitting every queued request), in
  * the chunkwise WY form with chunks of 64 rows, updating each prompt's state
- * and tail in place.  Chunks never cross prompts.
+ * and tail in place.  Chunks never cross prompts.  Geometry: dk == dv == 128
+ * and hv / hk <= 8 (GDN_EUNSUPPORTED otherwise).
  *   seq_start [n+1] int32, device: 0 <= seq_start[s] <= seq_start[s+1] <= total_rows
  *   max_len   a bound on every prompt's length (sizes the launch)
  *   qkv [total_rows][C] bf16; a, b [total_rows][hv] bf16

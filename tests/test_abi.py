@@ -110,7 +110,7 @@ def test_empty_calls_do_nothing(L):
     sh = _shape()
     assert L.gdn_conv_step(C.byref(sh), C.byref(_params()), 0, None, None, None, None, None, None,
                            None) == gdn.GDN_OK
-    assert L.gdn_commit(C.byref(sh), 0, 0, None, None, None, None, None, None) == gdn.GDN_OK
+    assert L.gdn_commit(C.byref(sh), 0, 0, None, None, None, None, None, None, None) == gdn.GDN_OK
 
 
 def test_tree_needs_parents(L):
@@ -132,9 +132,12 @@ def test_step_refusals(L):
 
 def test_commit_refusals(L):
     sh = _shape()
-    assert L.gdn_commit(C.byref(sh), 2, 10, None, P16, P16, P16, P16, None) == gdn.GDN_EINVAL
-    assert L.gdn_commit(C.byref(sh), -1, 10, P16, P16, P16, P16, P16, None) == gdn.GDN_EINVAL
-    assert L.gdn_commit(C.byref(sh), 2, 10, P16, P16, P16, P16, P_ODD, None) == gdn.GDN_EINVAL
+    assert L.gdn_commit(C.byref(sh), 2, 10, P16, None, P16, P16, P16, P16, None) == gdn.GDN_EINVAL
+    assert "accept_row" in L.gdn_last_error().decode()
+    assert L.gdn_commit(C.byref(sh), 2, 10, None, P16, P16, P16, P16, P16, None) == gdn.GDN_EINVAL
+    assert "row_start" in L.gdn_last_error().decode()
+    assert L.gdn_commit(C.byref(sh), -1, 10, P16, P16, P16, P16, P16, P16, None) == gdn.GDN_EINVAL
+    assert L.gdn_commit(C.byref(sh), 2, 10, P16, P16, P16, P16, P16, P_ODD, None) == gdn.GDN_EINVAL
 
 
 def test_log_refusals(L):

@@ -8,7 +8,7 @@ import oracle
 from verify_causal_conv1d_amd import gdn
 from verify_causal_conv1d_amd import inputs as gi
 
-from gpu_util import TOL_PREFILL, announce, bits16, host_batch, max_rel_err, max_rel_err_segments
+from gpu_util import TOL_PREFILL, announce, bits16, bound_err, host_batch, max_rel_err, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -29,23 +29,35 @@ def run_prefill(b: gi.Batch, dev="cuda"):
 
 
 def oracle_prefill(b: gi.Batch):
+    """(o, final state, final tail, o's magnitude, the final state's
+    magnitude) of the row-by-row recurrence."""
     h = host_batch(b)
     return oracle.prefill(b.shape, h["conv_w"], h["a_log"], h["dt_bias"], h["row_start"], h["qkv"],
-                          h["a"], h["b"], h["tail"], h["state"])
+                          h["a"], h["b"], h["tail"], h["state"], mag=True)
 
 
 def check(b: gi.Batch, out, tail, state, tol=TOL_PREFILL):
-    o_ref, st_ref, tl_ref = oracle_prefill(b)
+    """Every output element within tol of its magnitude (its row's step
+    carried out on magnitudes); each final (prompt, head) state within tol of
+    its largest element; conv tails bit for bit.  The final state's element-
+    wise bound is printed only: bf16 operand errors accumulate over a
+    prompt's chunks, while an element's magnitude covers only the last row's
+    terms, so near-zero elements of a long-memory state have no meaningful
+    element-wise bound at this precision."""
+    o_ref, st_ref, tl_ref, o_mag, st_mag = oracle_prefill(b)
     o = out.cpu().numpy()
-    e_o = max_rel_err_segments(o, o_ref, b.row_start.tolist())
-    e_s = max_rel_err(state.cpu().numpy(), st_ref, 2)
-    # and no drift: the typical row is well inside the bound
+    st = state.cpu().numpy()
+    e_o = bound_err(o, o_ref, o_mag)
+    e_s = max_rel_err(st, st_ref, 2)
+    e_se = bound_err(st, st_ref, st_mag)
     if b.rows:
-        num = np.abs(o.astype(np.float64) - o_ref).reshape(b.rows, -1).max(1)
-        den = np.maximum(np.abs(o_ref).reshape(b.rows, -1).max(1), 1e-30)
-        assert np.median(num / den) <= tol / 2, f"median row error {np.median(num / den):.3e}"
+        g = np.abs(o.astype(np.float64) - o_ref) / np.maximum(o_mag, 1e-30)
+        per_row = g.reshape(b.rows, -1).max(1)
+        print(f"o: bound err {e_o:.2e} (median row {np.median(per_row):.2e}, "
+              f"per-row rel {row_rel_err(o, o_ref):.2e}); final state {e_s:.2e} "
+              f"(element bound {e_se:.2e})")
     assert np.array_equal(bits16(tail), tl_ref), "conv tails must match bitwise"
-    assert e_o <= tol, f"o: max rel err {e_o:.3e}"
+    assert e_o <= tol, f"o: element-wise bound err {e_o:.3e}"
     assert e_s <= tol, f"final state: max rel err {e_s:.3e}"
     return e_o, e_s
 
@@ -108,6 +120,20 @@ def test_prefill_27b_four_prompts():
     print(f"27B prefill: o err {e_o:.2e}, state err {e_s:.2e}")
 
 
+@pytest.mark.parametrize("zero_state", [True, False])
+def test_prefill_27b_four_prompts_long_memory(zero_state):
+    """The long-memory variant (A_log ~ U(-7, -4), alpha about 0.99) on the
+    four prompts of the 27B-like pass: the state carried across all 74 chunks
+    of the 4,722-row prompt, from zero and from a resumed state and tail."""
+    shape, lengths, kw = gi.workload("prefill27b")
+    kw = dict(kw, zero_state=zero_state)
+    b = gi.make_batch(shape, lengths, long_memory=True, **kw)
+    announce(f"prefill 27B-like long memory {lengths} zero_state={zero_state} seed={kw['seed']}")
+    out, tail, state = run_prefill(b)
+    e_o, e_s = check(b, out, tail, state)
+    print(f"27B prefill, long memory: o err {e_o:.2e}, state err {e_s:.2e}")
+
+
 def test_prefill_27b_resumed_state():
     """A non-zero initial state and tail (a resumed prompt) on the 27B-like layer."""
     shape = gi.QWEN_27B
@@ -140,8 +166,8 @@ def test_prefill_then_steps_continue_the_stream():
     whole = gi.Batch(shape=shape, params=b.params, row_start=torch.tensor([0, 93], dtype=torch.int32),
                      qkv=torch.cat([b.qkv[:90], more.qkv]), a=torch.cat([b.a[:90], more.a]),
                      b=torch.cat([b.b[:90], more.b]), tail=b.tail[0:1], state=b.state[0:1])
-    o_ref, st_ref, tl_ref = oracle_prefill(whole)
-    assert max_rel_err_segments(np.stack(outs), o_ref[90:93], [0, 3]) <= TOL_PREFILL
+    o_ref, st_ref, tl_ref, o_mag, _ = oracle_prefill(whole)
+    assert bound_err(np.stack(outs), o_ref[90:93], o_mag[90:93]) <= TOL_PREFILL
     assert max_rel_err(st.cpu().numpy(), st_ref, 2) <= TOL_PREFILL
     assert np.array_equal(bits16(tl), tl_ref)
 

@@ -334,8 +334,8 @@ int gdn_commit_replay(const gdn_shape *shape, int32_t n_streams, int32_t total_r
 }
 
 int gdn_commit(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,
-               const int32_t *accept_row, const uint16_t *tail_snap, const float *state_snap,
-               uint16_t *conv_tail, float *state, void *stream)
+               const int32_t *row_start, const int32_t *accept_row, const uint16_t *tail_snap,
+               const float *state_snap, uint16_t *conv_tail, float *state, void *stream)
 {
     int rc = check_shape(shape);
     if (rc) return rc;
@@ -346,6 +346,7 @@ int gdn_commit(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,
         g_err[0] = '\0';
         return GDN_OK;
     }
+    if (!row_start) return fail(GDN_EINVAL, "row_start is NULL");
     if (!accept_row) return fail(GDN_EINVAL, "accept_row is NULL");
     REQUIRE_PTR(tail_snap);
     REQUIRE_PTR(state_snap);
@@ -356,6 +357,7 @@ int gdn_commit(const gdn_shape *shape, int32_t n_streams, int32_t total_rows,
     A.total_rows = total_rows;
     A.state_elems = (size_t)shape->hv * shape->dk * shape->dv;
     A.tail_elems = 3 * (size_t)(2 * shape->hk * shape->dk + shape->hv * shape->dv);
+    A.row_start = row_start;
     A.accept = accept_row;
     A.tail_snap = tail_snap;
     A.state_snap = state_snap;

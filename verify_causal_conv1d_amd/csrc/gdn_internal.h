@@ -42,6 +42,7 @@ struct CommitArgs {
     int32_t n_streams, total_rows;
     size_t state_elems;   // hv * dk * dv
     size_t tail_elems;    // 3 * C
+    const int32_t *row_start;   // [n+1]: the accepted row must lie in its stream's window
     const int32_t *accept;
     const uint16_t *tail_snap;
     const float *state_snap;

@@ -504,11 +504,15 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 }
 
 // Commit: the accepted row's recorded state and tail replace the stream's.
+// A row outside the stream's own window (or a window past the recorded rows)
+// skips the stream.
 __global__ void __launch_bounds__(256) commit_kernel(const CommitArgs A)
 {
     const int s = blockIdx.y;
     const int acc = A.accept[s];
-    if (acc < 0 || acc >= A.total_rows) return;
+    if (acc < 0) return;
+    const int r0 = A.row_start[s], r1 = A.row_start[s + 1];
+    if (r0 < 0 || r1 > A.total_rows || acc < r0 || acc >= r1) return;
     const size_t nthr = (size_t)gridDim.x * blockDim.x;
     const size_t first = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const float4 *src = reinterpret_cast<const float4 *>(A.state_snap + (size_t)acc * A.state_elems);

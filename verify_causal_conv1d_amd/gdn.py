@@ -66,7 +66,7 @@ def lib():
             L.gdn_conv_step.argtypes = [P, P, i32, P, P, P, P, P, P, P]
             L.gdn_recur_window.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
             L.gdn_recur_tree.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
-            L.gdn_commit.argtypes = [P, i32, i32, P, P, P, P, P, P]
+            L.gdn_commit.argtypes = [P, i32, i32, P, P, P, P, P, P, P]
             L.gdn_recur_log.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P]
             L.gdn_commit_replay.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
             L.gdn_prefill_workspace_bytes.restype = C.c_size_t
@@ -182,15 +182,17 @@ def recur_tree(shape, params, row_start, parent, qkv, a, b, conv_tail, state, ou
                       out, tail_snap, state_snap, max_rows, parent=parent), "gdn_recur_tree")
 
 
-def commit(shape, accept_row, tail_snap, state_snap, conv_tail, state):
-    """Each stream's accepted row (packed index, -1 = keep) becomes its state."""
-    for t, dt, nm in ((accept_row, torch.int32, "accept_row"), (tail_snap, torch.bfloat16, "tail_snap"),
+def commit(shape, row_start, accept_row, tail_snap, state_snap, conv_tail, state):
+    """Each stream's accepted row (packed index within its window of
+    ``row_start``, -1 = keep) becomes its state and tail."""
+    for t, dt, nm in ((row_start, torch.int32, "row_start"), (accept_row, torch.int32, "accept_row"),
+                      (tail_snap, torch.bfloat16, "tail_snap"),
                       (state_snap, torch.float32, "state_snap"), (conv_tail, torch.bfloat16, "conv_tail"),
                       (state, torch.float32, "state")):
         _dev(t, dt, nm)
     sh = _shape(shape)
-    _check(lib().gdn_commit(C.byref(sh), accept_row.shape[0], state_snap.shape[0], _ptr(accept_row),
-                            _ptr(tail_snap), _ptr(state_snap), _ptr(conv_tail), _ptr(state),
+    _check(lib().gdn_commit(C.byref(sh), accept_row.shape[0], state_snap.shape[0], _ptr(row_start),
+                            _ptr(accept_row), _ptr(tail_snap), _ptr(state_snap), _ptr(conv_tail), _ptr(state),
                             _stream(state)), "gdn_commit")
 
 
