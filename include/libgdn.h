@@ -184,8 +184,9 @@ int gdn_recur_log(const gdn_shape *shape, const gdn_params *params, int32_t n_st
                   float *log_alpha, float *log_delta, float *log_key, void *stream);
 
 /*
- * Commit by replay after gdn_recur_log (same page and note: keeping replays
- * the kept path in one pass and moves a tree's kept rows down).
+ * Commit by replay after gdn_recur_log (same page and note: keeping a row
+ * replays its path in one pass and carries the path's own entries into
+ * place).
  * accept_row [n] int32, device: the packed index of the stream's kept row,
  * within its window [row_start[s], row_start[s+1]), or -1 to keep the stream
  * as it is; any other value, or a layout that breaks gdn_recur_log's rules,
