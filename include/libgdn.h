@@ -231,6 +231,32 @@ int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_
                         size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * gdn_prefill_chunked with its workspace in a fixed device array of
+ * GDN_PREFILL_SCRATCH_BYTES (128 MiB) that the library holds on every GPU it
+ * runs on until the process ends.  Same arguments as gdn_prefill_chunked
+ * without the workspace, and bit for bit the same results.  Allocates
+ * nothing.
+ *  - A pass whose workspace (gdn_prefill_workspace_bytes) exceeds the array
+ *    is refused with GDN_EWORKSPACE before anything is launched: at 48 value
+ *    heads of 128 that is a pass of more than about 40 chunks of 64 rows.
+ *    Longer prompts can be passed in pieces cut at multiples of 64 rows,
+ *    which give the same bits as one pass.
+ *  - `stream` must belong to the calling thread's current device; the
+ *    array's address on that device is looked up on the first call there.
+ *  - Every call on a GPU shares that GPU's array.  A pass writes every byte
+ *    of it that it reads, so nothing has to be cleared between calls, but
+ *    calls that overlap on one GPU (on different streams, or from threads
+ *    without ordering) race and give undefined results.
+ */
+#define GDN_PREFILL_SCRATCH_BYTES (128u * 1024u * 1024u)
+int gdn_prefill_chunked_noalloc(const gdn_shape *shape, const gdn_params *params, int32_t n_seqs,
+                                int32_t total_rows, int32_t max_len, const int32_t *seq_start,
+                                const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                                uint16_t *conv_tail, float *state, float *out, void *stream);
+
+/*
  * The in-projection before the mixer: its packed rows qkv and gate inputs a,
  * b from hidden rows x, y = x W^T, with W in affine 4-bit form (the
  * projections of the MLX affine 4-bit checkpoint run through affine-4

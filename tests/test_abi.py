@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from verify_causal_conv1d_amd import gdn
+from verify_causal_conv1d_amd import inputs as gi
 from verify_causal_conv1d_amd.inputs import QWEN_27B, SMALL
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -180,6 +181,25 @@ def test_prefill_refusals(L):
     assert call(wsb=1) == gdn.GDN_EWORKSPACE
     assert call(ws=None) == gdn.GDN_EWORKSPACE
     assert call(ws=P_ODD) == gdn.GDN_EINVAL
+
+
+def test_prefill_noalloc_refusals(L):
+    """The allocation-free prompt pass refuses, before any device call, what
+    gdn_prefill_chunked refuses, and any pass whose workspace is over its
+    fixed array."""
+    sh, pa = _shape(), _params()
+
+    def call(n=1, total=2688, max_len=2688, seq=P16, qkv=P16, shape=sh):
+        return L.gdn_prefill_chunked_noalloc(C.byref(shape), C.byref(pa), n, total, max_len, seq, qkv, P16,
+                                             P16, P16, P16, P16, None)
+    assert gdn.prefill_workspace_bytes(gi.QWEN_27B, 1, 2688) > gdn.PREFILL_SCRATCH_BYTES
+    assert call() == gdn.GDN_EWORKSPACE and "pieces" in L.gdn_last_error().decode()
+    assert call(n=-1) == gdn.GDN_EINVAL
+    assert call(max_len=0) == gdn.GDN_EINVAL
+    assert call(seq=None) == gdn.GDN_EINVAL
+    assert call(qkv=P_ODD) == gdn.GDN_EINVAL
+    assert call(shape=_shape(hk=2, hv=4, dk=64, dv=64)) == gdn.GDN_EUNSUPPORTED
+    assert call(n=0, total=0, seq=None) == gdn.GDN_OK
 
 
 def test_inproj_refusals(L):

@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/libgdn.h"
 #include "gdn_internal.h"
 #include "gdn_inproj.h"
@@ -372,12 +374,20 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int32_t n_seqs, int32
     return gdn::prefill_workspace_bytes(shape->hk, shape->hv, shape->dk, shape->dv, n_seqs, total_rows);
 }
 
-int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_t n_seqs,
-                        int32_t total_rows, int32_t max_len, const int32_t *seq_start,
-                        const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
-                        uint16_t *conv_tail, float *state, float *out, void *workspace,
-                        size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Checks of a prompt pass's host-visible arguments; fills P (all but the
+// workspace) and the workspace bytes the pass needs.  GDN_OK with
+// P.total_rows == 0 means there is nothing to do.
+int prefill_checked(const gdn_shape *shape, const gdn_params *params, int32_t n_seqs, int32_t total_rows,
+                    int32_t max_len, const int32_t *seq_start, const uint16_t *qkv, const uint16_t *a,
+                    const uint16_t *b, uint16_t *conv_tail, float *state, float *out, gdn::PrefillArgs &P,
+                    size_t &need)
 {
+    P = gdn::PrefillArgs{};
+    need = 0;
     int rc = check_shape(shape);
     if (rc) return rc;
     rc = check_params(params);
@@ -399,12 +409,7 @@ int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_
     REQUIRE_PTR(conv_tail);
     REQUIRE_PTR(state);
     REQUIRE_PTR(out);
-    const size_t need = gdn::prefill_workspace_bytes(shape->hk, shape->hv, shape->dk, shape->dv, n_seqs,
-                                                     total_rows);
-    if (!workspace || workspace_bytes < need)
-        return fail(GDN_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-    if (!aligned16(workspace)) return fail(GDN_EINVAL, "workspace must be 16-byte aligned");
-    gdn::PrefillArgs P = {};
+    need = gdn::prefill_workspace_bytes(shape->hk, shape->hv, shape->dk, shape->dv, n_seqs, total_rows);
     P.hk = shape->hk;
     P.hv = shape->hv;
     P.dk = shape->dk;
@@ -423,7 +428,81 @@ int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_
     P.conv_tail = conv_tail;
     P.state = state;
     P.out = out;
+    return GDN_OK;
+}
+
+// The fixed workspace of gdn_prefill_chunked_noalloc: one copy on every GPU
+// the library runs on, held until the process ends.  In host code this name
+// is only a stand-in for the device array; its device address on each GPU
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// ever passed to a kernel.
+__device__ __align__(256) unsigned char scratch[GDN_PREFILL_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device (looked up on the
+// device's first call, with that device current).
+int scratch_on_current_device(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GDN_EHIP, "scratch array address on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_t n_seqs,
+                        int32_t total_rows, int32_t max_len, const int32_t *seq_start,
+                        const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                        uint16_t *conv_tail, float *state, float *out, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    gdn::PrefillArgs P;
+    size_t need = 0;
+    int rc = prefill_checked(shape, params, n_seqs, total_rows, max_len, seq_start, qkv, a, b, conv_tail,
+                             state, out, P, need);
+    if (rc || P.total_rows == 0) return rc;
+    if (!workspace || workspace_bytes < need)
+        return fail(GDN_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(GDN_EINVAL, "workspace must be 16-byte aligned");
     P.workspace = workspace;
+    return launched(gdn::launch_prefill(P, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_prefill_chunked_noalloc(const gdn_shape *shape, const gdn_params *params, int32_t n_seqs,
+                                int32_t total_rows, int32_t max_len, const int32_t *seq_start,
+                                const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                                uint16_t *conv_tail, float *state, float *out, void *stream)
+{
+    gdn::PrefillArgs P;
+    size_t need = 0;
+    int rc = prefill_checked(shape, params, n_seqs, total_rows, max_len, seq_start, qkv, a, b, conv_tail,
+                             state, out, P, need);
+    if (rc || P.total_rows == 0) return rc;
+    if (need > (size_t)GDN_PREFILL_SCRATCH_BYTES)
+        return fail(GDN_EWORKSPACE,
+                    "prompt pass needs %zu bytes of workspace, over the fixed %zu: pass the prompts in "
+                    "pieces cut at multiples of 64 rows, or call gdn_prefill_chunked",
+                    need, (size_t)GDN_PREFILL_SCRATCH_BYTES);
+    void *ws = nullptr;
+    rc = scratch_on_current_device(&ws);
+    if (rc) return rc;
+    P.workspace = ws;
     return launched(gdn::launch_prefill(P, static_cast<hipStream_t>(stream)));
 }
 

@@ -21,11 +21,13 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 MAX_WINDOW_ROWS = 16
+PREFILL_SCRATCH_BYTES = 128 * 1024 * 1024   # the fixed workspace of prefill_chunked_noalloc
 
 EXPORTED = (
     "gdn_status_name", "gdn_last_error", "gdn_channels", "gdn_conv_step", "gdn_recur_window",
     "gdn_recur_tree", "gdn_commit", "gdn_recur_log", "gdn_commit_replay",
-    "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_check_layout",
+    "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_noalloc",
+    "gdn_check_layout",
     "gdn_inproj_affine4", "gdn_inproj_pack_affine4", "gdn_inproj_padded_features",
 )
 
@@ -73,6 +75,7 @@ def lib():
             L.gdn_prefill_workspace_bytes.argtypes = [P, i32, i32]
             L.gdn_prefill_chunked.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P,
                                               C.c_size_t, P]
+            L.gdn_prefill_chunked_noalloc.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
             L.gdn_check_layout.argtypes = [i32, i32, i32, P, P]
             L.gdn_inproj_affine4.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P, P]
             L.gdn_inproj_pack_affine4.argtypes = [P, i32, i32, P, P, P, P, P, P, P]
@@ -80,6 +83,7 @@ def lib():
             L.gdn_inproj_padded_features.argtypes = [P]
             for name in ("gdn_conv_step", "gdn_recur_window", "gdn_recur_tree", "gdn_commit",
                          "gdn_recur_log", "gdn_commit_replay", "gdn_prefill_chunked",
+                         "gdn_prefill_chunked_noalloc",
                          "gdn_check_layout", "gdn_inproj_affine4", "gdn_inproj_pack_affine4"):
                 getattr(L, name).restype = C.c_int
             _lib = L
@@ -255,6 +259,22 @@ def prefill_chunked(shape, params, seq_start, qkv, a, b, conv_tail, state, out, 
                                      _ptr(a), _ptr(b), _ptr(conv_tail), _ptr(state), _ptr(out),
                                      _ptr(workspace), workspace.numel(), _stream(qkv)),
            "gdn_prefill_chunked")
+
+
+def prefill_chunked_noalloc(shape, params, seq_start, qkv, a, b, conv_tail, state, out, max_len: int):
+    """``prefill_chunked`` with the library's fixed workspace (allocates
+    nothing; passes needing more than PREFILL_SCRATCH_BYTES are refused)."""
+    for t, dt, nm in ((seq_start, torch.int32, "seq_start"), (qkv, torch.bfloat16, "qkv"),
+                      (a, torch.bfloat16, "a"), (b, torch.bfloat16, "b"),
+                      (conv_tail, torch.bfloat16, "conv_tail"), (state, torch.float32, "state"),
+                      (out, torch.float32, "out")):
+        _dev(t, dt, nm)
+    sh = _shape(shape)
+    _check(lib().gdn_prefill_chunked_noalloc(C.byref(sh), C.byref(params._c), seq_start.shape[0] - 1,
+                                             qkv.shape[0], int(max_len), _ptr(seq_start), _ptr(qkv),
+                                             _ptr(a), _ptr(b), _ptr(conv_tail), _ptr(state), _ptr(out),
+                                             _stream(qkv)),
+           "gdn_prefill_chunked_noalloc")
 
 
 def inproj_pack(shape, wq, scales, biases, group: int):
