@@ -240,7 +240,8 @@ int gdn_prefill_chunked(const gdn_shape *shape, const gdn_params *params, int32_
  * nothing.
  *  - A pass whose workspace (gdn_prefill_workspace_bytes) exceeds the array
  *    is refused with GDN_EWORKSPACE before anything is launched: at 48 value
- *    heads of 128 that is a pass of more than about 40 chunks of 64 rows.
+ *    heads of 128 that is a pass of more than about 43 chunks of 64 rows
+ *    (one prompt of 2,752 rows).
  *    Longer prompts can be passed in pieces cut at multiples of 64 rows,
  *    which give the same bits as one pass.
  *  - `stream` must belong to the calling thread's current device; the

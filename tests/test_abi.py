@@ -189,10 +189,13 @@ def test_prefill_noalloc_refusals(L):
     fixed array."""
     sh, pa = _shape(), _params()
 
-    def call(n=1, total=2688, max_len=2688, seq=P16, qkv=P16, shape=sh):
+    rows = 64     # the fewest rows of one prompt over the fixed array
+    while gdn.prefill_workspace_bytes(gi.QWEN_27B, 1, rows) <= gdn.PREFILL_SCRATCH_BYTES:
+        rows += 64
+
+    def call(n=1, total=rows, max_len=rows, seq=P16, qkv=P16, shape=sh):
         return L.gdn_prefill_chunked_noalloc(C.byref(shape), C.byref(pa), n, total, max_len, seq, qkv, P16,
                                              P16, P16, P16, P16, None)
-    assert gdn.prefill_workspace_bytes(gi.QWEN_27B, 1, 2688) > gdn.PREFILL_SCRATCH_BYTES
     assert call() == gdn.GDN_EWORKSPACE and "pieces" in L.gdn_last_error().decode()
     assert call(n=-1) == gdn.GDN_EINVAL
     assert call(max_len=0) == gdn.GDN_EINVAL
@@ -237,12 +240,15 @@ def test_prefill_workspace_bytes(L):
     n, T, hk, hv, d = 4, 8306, 16, 48, 128
     need = L.gdn_prefill_workspace_bytes(C.byref(sh), n, T)
     # per chunk and value head (at most T/64 + n chunks): the sweep's bf16
-    # operand block ([W; Q']: 128 x dk; e^{gamma_L - gamma} k^: 64 x dk;
-    # U~: 64 x dv) and e^{gamma_L} (fp32); nothing per row
+    # operand block (W: 64 x dk; U~: 64 x dv; P: 64 x 64) and its gates
+    # (fp32: e^{gamma_L}, e^gamma and e^{gamma_L - gamma} of each row, 132
+    # floats); per chunk and key head the shared fragments (K K^T and Q K^T in
+    # fp32, k^ and q^ fragments in bf16: 4 x 64 x 64 x 4 bytes); nothing per row
     nc = T // 64 + n
-    blk = (128 * d + 64 * d + 64 * d) * 2
-    lower = nc * hv * (blk + 4)
-    assert lower <= need <= lower + 2 * 256
+    blk = (64 * d + 64 * d + 64 * 64) * 2
+    frag = 4 * 64 * 64 * 4
+    lower = nc * hv * (blk + 132 * 4) + nc * hk * frag
+    assert lower <= need <= lower + 3 * 256
     assert L.gdn_prefill_workspace_bytes(C.byref(_shape(dk=64)), 4, 100) == 0
 
 

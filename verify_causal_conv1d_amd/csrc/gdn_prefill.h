@@ -24,10 +24,12 @@ struct PrefillArgs {
 // Byte offsets of the workspace arrays.  Per chunk (dense index over the
 // prompts' chunks, at most T/64 + n_seqs) and value head, the sweep's
 // matrix-core operands, each already in the lane order the sweep's MFMAs read:
-//   blk bf16 [NC][hv][kBlockElems]  W, Q' = e^gamma q^ - P W, e^{gamma_L - gamma} k^, U~
-//   el  f32  [NC][hv]               e^{gamma_L} of the chunk
+//   blk  bf16 [NC][hv][kBlockElems]  W, U~ and P (40 KB)
+//   gv   f32  [NC][hv][132]          e^{gamma_L}, e^gamma, e^{gamma_L - gamma}
+// and per chunk and key head, what its value heads share (64 KB):
+//   frag u32x4 [NC][hk][4][16][64]   K K^T, Q K^T, k^ and q^ fragments
 struct PrefillLayout {
-    size_t blk, el, total;
+    size_t blk, gv, frag, total;
     int max_chunks_total;
 };
 

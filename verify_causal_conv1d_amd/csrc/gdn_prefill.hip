@@ -6,36 +6,42 @@
 //   A_tj = beta_t e^{gamma_t - gamma_j} k_t.k_j (j < t),  T = (I + A)^-1,
 //   W = T (beta e^gamma k),  U~ = T (beta v),  U = U~ - W M0,
 //   P_tj = e^{gamma_t - gamma_j} q_t.k_j (j <= t),
-//   O = (e^gamma q) M0 + P U = Q' M0 + P U~,   Q' = e^gamma q - P W,
+//   O = (e^gamma q) M0 + P U,
 //   M_next = e^{gamma_L} M0 + (e^{gamma_L - gamma} k)^T U.
 // (The derivation unrolls M_t = alpha_t M_{t-1} + k_t d_t^T with
 // d_t = beta_t (v_t - alpha_t M_{t-1}^T k_t) over the chunk; the gated delta
 // rule is Yang, Kautz and Hatamizadeh, "Gated Delta Networks", 2024.)
-// Folding P W into Q' moves every product that does not involve the state
-// into the parallel per-chunk kernel, and leaves the sequential sweep with
-// one fused contraction [W; Q'] M0 and the update.
+// The parallel per-chunk kernels form every operand that does not involve
+// the state; the sequential sweep forms [W; e^gamma q] M0 and the update on
+// fp32 MFMA, and P U (an in-chunk product of the chunk's own deltas U, which
+// only the sweep knows) on bf16 MFMA, and writes each output row once.
 //
-// Two launches on the caller's stream:
-//   intra     per (chunk, value head), independent: the causal conv (taps
-//             from the prompt's own earlier rows or its tail) + SiLU of the
-//             chunk's q, k and v channels straight from the packed rows, the
-//             q/k L2 norms over the 16 lanes of a head, and the gates; then
-//             K K^T and Q K^T on bf16 MFMA, T by 16 x 16 blocks (fp32 forward substitution on the
-//             diagonal, fp32 MFMA off it), then W^T, W, U~, (P W)^T and P U~
-//             on bf16 MFMA.  k^ and v are transposed by an exact MFMA with a
-//             0/1 selection operand, and every later product takes a k order
-//             in which one product's accumulator registers are the next one's
-//             operand, so nothing is transposed through LDS; products are
-//             formed transposed where that puts each lane's values where the
-//             sweep's lanes read them, and everything leaves in that order.
+// Three launches on the caller's stream:
+//   qk        per (chunk, key head), independent: the causal conv (taps from
+//             the prompt's own earlier rows or its tail) + SiLU of the chunk's
+//             q and k channels straight from the packed rows, the q/k L2 norms
+//             over the 16 lanes of a head, K K^T and Q K^T on bf16 MFMA, and
+//             the transposed k^ fragments: what the r value heads of a key
+//             head share, formed once and left in the lane order the next
+//             kernel's waves read.
+//   intra     per (chunk, value head), independent: the gates, T by 16 x 16
+//             blocks (fp32 forward substitution on the diagonal, fp32 MFMA
+//             off it), the conv + SiLU of the chunk's v channels, then W^T and
+//             U~ on bf16 MFMA, and P and e^gamma q^ as they are.  k^ and v are
+//             transposed by an exact MFMA with a 0/1 selection operand, and
+//             every product takes a k order in which one product's
+//             accumulator registers are the next one's operand, so nothing is
+//             transposed through LDS; products are formed transposed where
+//             that puts each lane's values where the sweep's lanes read them,
+//             and everything leaves in that order.
 //   sweep     per (prompt, value head, 16 state columns), 4 waves; wave w
 //             keeps state rows [32w, 32w + 32) as two fp32 16 x 16 MFMA
 //             accumulators (v_mfma_f32_16x16x4_f32) and copies them to LDS,
 //             where every wave reads all of M0.  Per chunk: rows
-//             [16w, 16w + 16) of W M0 and Q' M0 over the 128 state rows,
-//             O = Q' M0 + P U~ (P U~ left in the output rows by the
-//             per-chunk kernel), U = U~ - W M0 shared through LDS, then
-//             M = e^{gamma_L} M + K~^T U on the wave's rows.  Sequential over
+//             [16w, 16w + 16) of W M0 and (e^gamma q) M0 over the 128 state
+//             rows, U = U~ - W M0 shared through LDS, O = (e^gamma q) M0 + P U
+//             (P U on bf16 MFMA), then M = e^{gamma_L} M + K~^T U on the
+//             wave's rows.  Sequential over
 //             the prompt's chunks, operands of chunk c + 1 fetched while
 //             chunk c computes; the state never leaves the chip.  The 8
 //             column tiles of one (prompt, head) share their operands and
@@ -58,19 +64,19 @@ constexpr int NTILE = D / 16;   // 16-column state tiles of a head
 // A chunk-head block of sweep operands (bf16), every sub-array in lane order
 // [..][64 lanes][values]; lane l = (l16, g4) = (l & 15, l >> 4), and
 // accumulator register i of a 16x16 block holds row 4 g4 + i, column l16.
-//   W  [w 4][kb 8][l][4]        W[16w + l16][16kb + 4g4 + e]
-//   Q  [w 4][kb 8][l][4]        Q'[16w + l16][16kb + 4g4 + e]
-//        the A operands of k-step (kb, i) for output rows 16w..16w+15 of
-//        W M0 and Q' M0; step (kb, i) reads state rows 16kb + 4g4 + i.
-//        Apart, so that each is written in whole lines (the two are formed
-//        at different times)
-//   KT [w 4][b 2][mp 2][l][e]   = K~[16m + 4g4 + i][32w + 16b + l16],
-//        m = 2mp + e/4, i = e%4, K~ = e^{gamma_L - gamma} k^
+//   W  [w 4][kb 8][l][4]        W[16w + l16][16kb + 4g4 + e]: the A operands
+//        of k-step (kb, i) for output rows 16w..16w+15 of W M0; step (kb, i)
+//        reads state rows 16kb + 4g4 + i
 //   UA [tile 8][w 4][l][4]      = U~[16w + 4g4 + i][16tile + l16]   (accumulator layout)
-// Rows past the chunk's end are zero in every array.  The chunk's P U~ goes
-// straight to the output rows (fp32), where the sweep adds Q' M0.
-constexpr int kOffW = 0, kOffQ = 8192, kOffKT = 16384, kOffUA = 24576;
-constexpr int kBlockElems = 32768;
+//   P  [w 4][ks 2][l][8]        P[16w + l16][32ks + 4g4 + (e & 3) + 16 (e >> 2)],
+//        the A operands of P U in the permuted k order (below)
+// The A operands of q^ M0 and the k^ of the update are the key head's, in its
+// fragment block (qk_kernel).  Rows past the chunk's end are zero in every array.
+constexpr int kOffW = 0, kOffUA = 8192, kOffP = 16384;
+constexpr int kBlockElems = 20480;
+// The gates of a chunk-head (fp32): [0] e^{gamma_L}, [4 + t] e^{gamma_t},
+// [68 + t] e^{gamma_L - gamma_t}; zero past the chunk's end.
+constexpr int kGv = 132, kGvEg = 4, kGvEk = 68;
 // Word 3 of a raw buffer resource on gfx9-family chips (gfx950 included):
 // 32-bit data format, no swizzle; accesses past num_records are dropped.
 constexpr int kBufferDword3 = 0x00020000;
@@ -80,7 +86,8 @@ struct Ctx {
     int r;                      // value heads per key head
     int nc_total;               // chunk blocks in the workspace
     uint16_t *blk;
-    float *el;
+    float *gv;                  // per (chunk, value head): the gates the sweep scales by
+    uint4 *frag;                // per (chunk, key head): q^ / k^ fragments (qk_kernel)
 };
 
 // Rows of prompt p, and the dense index of its first chunk.  False if p or an
@@ -242,35 +249,41 @@ __device__ __forceinline__ uint4 select_cols(int hb, int l16, int g4)
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
+// ---------------------------------------------------------------- qk
+// Per (chunk, key head): what the r value heads of a key head share, formed
+// once.  The causal conv + SiLU of the chunk's q and k channels straight from
+// the packed rows, their L2 norms (q also times dk^-1/2), K K^T and Q K^T on
+// bf16 MFMA, and the fragments of k^ and q^ that the per-value-head kernel's
+// products take.  Each wave leaves 16 uint4 a lane in the unit's fragment
+// block, [wave 4][j 16][lane 64], in the registers and lane order that the
+// per-value-head kernel's wave of the same index reads them:
+//   j 0..3    K K^T block (w >> 1, w & 1), accumulator registers 4j .. 4j + 3
+//   j 4..7    Q K^T block, the same way
+//   j 8..11   kp[hb][ks] (j = 8 + 2 hb + ks): the transposed k^ fragments,
+//             k^[32 ks + 4 g4 + (e & 3) + 16 (e >> 2)][32 w + 16 hb + l16]
+//   j 12..15  q^[16 w + l16][16 kb + 4 g4 .. + 3] for kb = 2 (j - 12) (low
+//             half) and kb + 1 (high half): the sweep's A operands of q^ M0
+// The sweep's wave w reads the fragments k^ (j 8..11, the k^ of its state
+// update) and q^ of wave w.
+constexpr int kFragS = 0, kFragQK = 4, kFragKp = 8, kFragQ = 12, kFragVec4 = 16;
+constexpr int kQkLds = 2 * 64 * KSB * 2;   // the staged k^ and q^ rows
+
+__global__ void __launch_bounds__(256, 4) qk_kernel(const Ctx X)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int l32 = lane & 31, hh = lane >> 5;
-    // workgroup i runs on XCD i % 8.  The r value heads of one (chunk, key
-    // head), which read the same q and k rows, are consecutive workgroups of
-    // one XCD, so those rows are fetched into that XCD's L2 once.
-    const int r = X.r, hk = X.P.hk;
-    const int xcd = blockIdx.x & 7, qi = blockIdx.x >> 3;
-    const int unit = (qi / r) * 8 + xcd;              // (chunk, key head)
+    const int hk = X.P.hk;
+    // workgroup i = unit i runs on XCD i % 8, where the per-value-head
+    // workgroups of the same unit run and read its fragments
+    const int unit = blockIdx.x;
     if (unit >= X.nc_total * hk) return;
     const int cid = unit / hk, kh = unit - cid * hk;
-    const int h = kh * r + (qi - (qi / r) * r);
     int pidx, c, s0, s1;
     if (!chunk_at(X, cid, pidx, c, s0, s1)) return;
     const int r0 = s0 + c * kChunk;
     const int L = min(kChunk, s1 - r0);
-    const int hv = X.P.hv;
-    const size_t cidh = (size_t)cid * hv + h;
-    uint16_t *blk = X.blk + cidh * kBlockElems;
-
-    float *An = reinterpret_cast<float *>(lds + kIntraAn);
-    uint16_t *Pb = reinterpret_cast<uint16_t *>(lds + kIntraPb);
-    uint16_t *T1 = reinterpret_cast<uint16_t *>(lds + kIntraT1);
-    uint16_t *T2 = reinterpret_cast<uint16_t *>(lds + kIntraT2);
-    float *gam = reinterpret_cast<float *>(lds + kIntraVec);
-    float *bet = gam + 64, *eg = bet + 64, *ekt = eg + 64;
 
     const int C = X.P.C, nq = hk * D;
     const uint16_t *tail = X.P.conv_tail + (size_t)pidx * 3 * C;
@@ -281,13 +294,12 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         return ld16(u >= s0 ? X.P.qkv + (size_t)u * C + ch : tail + (size_t)(3 + u - s0) * C + ch);
     };
 
-    // ---- the chunk's k^ and q^ rows, staged once in LDS (in the space the
-    // solve's arrays use later).  Thread (which, c8) of 32 walks 8 consecutive
+    // ---- the chunk's k^ and q^ rows, staged in LDS.  Thread (which, c8) of 32 walks 8 consecutive
     // rows of 8 channels: the window's 11 raw rows requested together, then per
     // row causal conv + SiLU and the L2 norm over the 16 lanes of the head.
     // Rows past the chunk's end are zero (their raw rows are clamped to the
     // chunk's last row and never used).
-    uint16_t *Ks = reinterpret_cast<uint16_t *>(lds + kIntraAn);   // [64][KSB] k^
+    uint16_t *Ks = reinterpret_cast<uint16_t *>(lds);              // [64][KSB] k^
     uint16_t *Qs = Ks + 64 * KSB;                                  // [64][KSB] q^ (scaled)
     {
         const int which = (tid >> 4) & 1;                 // 0: k, 1: q
@@ -325,25 +337,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         }
     }
 
-    // ---- gates: gamma (inclusive in-chunk scan of log alpha), beta and the decays
-    if (wave == 0) {
-        const size_t o = (size_t)(r0 + lane) * hv + h;
-        float gl = lane < L ? log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]) : 0.0f;
-        const float bl = lane < L ? sigmoid_f(bf16f(X.P.b[o])) : 0.0f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float up = __shfl_up(gl, d);
-            if (lane >= d) gl += up;
-        }
-        const float gL = __shfl(gl, L - 1);
-        gam[lane] = gl;
-        bet[lane] = bl;
-        eg[lane] = lane < L ? __expf(gl) : 0.0f;
-        ekt[lane] = lane < L ? __expf(gL - gl) : 0.0f;
-        if (lane == 0) X.el[cidh] = __expf(gL);
-    }
-
-    lds_barrier();   // k^, q^ staged; gamma, beta visible
+    lds_barrier();   // k^, q^ staged
 
     // ---- K K^T and Q K^T, wave w: the 32 x 32 block (w >> 1, w & 1); the
     // transposed fragments of k^, packed in the permuted k order: kp[hb][ks]
@@ -369,17 +363,112 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             kp[hb][ks] = pack_perm(mfma_bf16(ld16(Ks + (32 * ks + l16) * KSB + 32 * wave + 8 * g4), sel, z),
                                    mfma_bf16(ld16(Ks + (32 * ks + 16 + l16) * KSB + 32 * wave + 8 * g4), sel, z));
     }
-    // q^[16 mt + l16][16 (2w + hb) + 4 g4 .. + 3], for Q' after the solve, is
-    // parked in the very slot of the operand block that Q' takes later: the
-    // same lane reads it back and overwrites it (held in registers through
-    // the solve it would spill)
+
+    // this wave's fragments, 1 KB contiguous a store
+    uint4 *fr = X.frag + ((size_t)unit * 4 + wave) * kFragVec4 * 64 + lane;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int j = 0; j < 4; ++j) {
+        fr[(kFragS + j) * 64] = make_uint4(__float_as_uint(S[4 * j]), __float_as_uint(S[4 * j + 1]),
+                                           __float_as_uint(S[4 * j + 2]), __float_as_uint(S[4 * j + 3]));
+        fr[(kFragQK + j) * 64] = make_uint4(__float_as_uint(QK[4 * j]), __float_as_uint(QK[4 * j + 1]),
+                                            __float_as_uint(QK[4 * j + 2]), __float_as_uint(QK[4 * j + 3]));
+    }
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-            *reinterpret_cast<uint2 *>(blk + kOffQ + ((mt * 8 + 2 * wave + hb) * 64 + lane) * 4) =
-                *reinterpret_cast<const uint2 *>(Qs + (16 * mt + l16) * KSB + 16 * (2 * wave + hb) + 4 * g4);
-    lds_barrier();   // every read of the staged rows done: -A and P may overwrite them
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) fr[(kFragKp + 2 * hb + ks) * 64] = kp[hb][ks];
+#pragma unroll
+    for (int kp2 = 0; kp2 < 4; ++kp2) {
+        const uint16_t *q0 = Qs + (16 * wave + l16) * KSB + 32 * kp2 + 4 * g4;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(q0);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(q0 + 16);
+        fr[(kFragQ + kp2) * 64] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+}
+
+__global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int l32 = lane & 31, hh = lane >> 5;
+    // workgroup i runs on XCD i % 8.  The r value heads of one (chunk, key
+    // head), which read the same fragments and q and k rows, are consecutive
+    // workgroups of one XCD (the XCD where qk_kernel formed the fragments).
+    const int r = X.r, hk = X.P.hk;
+    const int xcd = blockIdx.x & 7, qi = blockIdx.x >> 3;
+    const int unit = (qi / r) * 8 + xcd;              // (chunk, key head)
+    if (unit >= X.nc_total * hk) return;
+    const int cid = unit / hk, kh = unit - cid * hk;
+    const int h = kh * r + (qi - (qi / r) * r);
+    int pidx, c, s0, s1;
+    if (!chunk_at(X, cid, pidx, c, s0, s1)) return;
+    const int r0 = s0 + c * kChunk;
+    const int L = min(kChunk, s1 - r0);
+    const int hv = X.P.hv;
+    const size_t cidh = (size_t)cid * hv + h;
+    uint16_t *blk = X.blk + cidh * kBlockElems;
+    // this wave's fragments of the key head's k^ and q^ (qk_kernel), requested first
+    const uint4 *fr = X.frag + ((size_t)unit * 4 + wave) * kFragVec4 * 64 + lane;
+    f16v S, QK;
+    uint4 kp[2][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 sv = fr[(kFragS + j) * 64], qk = fr[(kFragQK + j) * 64];
+        S[4 * j] = __uint_as_float(sv.x);
+        S[4 * j + 1] = __uint_as_float(sv.y);
+        S[4 * j + 2] = __uint_as_float(sv.z);
+        S[4 * j + 3] = __uint_as_float(sv.w);
+        QK[4 * j] = __uint_as_float(qk.x);
+        QK[4 * j + 1] = __uint_as_float(qk.y);
+        QK[4 * j + 2] = __uint_as_float(qk.z);
+        QK[4 * j + 3] = __uint_as_float(qk.w);
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) kp[hb][ks] = fr[(kFragKp + 2 * hb + ks) * 64];
+
+    float *An = reinterpret_cast<float *>(lds + kIntraAn);
+    uint16_t *Pb = reinterpret_cast<uint16_t *>(lds + kIntraPb);
+    uint16_t *T1 = reinterpret_cast<uint16_t *>(lds + kIntraT1);
+    uint16_t *T2 = reinterpret_cast<uint16_t *>(lds + kIntraT2);
+    float *gam = reinterpret_cast<float *>(lds + kIntraVec);
+    float *bet = gam + 64, *eg = bet + 64;
+
+    const int C = X.P.C, nq = hk * D;
+    const uint16_t *tail = X.P.conv_tail + (size_t)pidx * 3 * C;
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    // packed row u (>= r0 - 3) of channel group ch: the prompt's own row, or
+    // row 3 + u - s0 of its conv tail before the prompt's first row
+    auto raw_row = [&](int ch, int u) {
+        return ld16(u >= s0 ? X.P.qkv + (size_t)u * C + ch : tail + (size_t)(3 + u - s0) * C + ch);
+    };
+
+    // ---- gates: gamma (inclusive in-chunk scan of log alpha), beta and the decays
+    if (wave == 0) {
+        const size_t o = (size_t)(r0 + lane) * hv + h;
+        float gl = lane < L ? log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]) : 0.0f;
+        const float bl = lane < L ? sigmoid_f(bf16f(X.P.b[o])) : 0.0f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float up = __shfl_up(gl, d);
+            if (lane >= d) gl += up;
+        }
+        const float gL = __shfl(gl, L - 1);
+        const float egl = lane < L ? __expf(gl) : 0.0f;
+        gam[lane] = gl;
+        bet[lane] = bl;
+        eg[lane] = egl;
+        // the sweep's scales: e^{gamma_L} of the chunk, e^gamma of each
+        // output row, e^{gamma_L - gamma} of each row's delta
+        float *gv = X.gv + cidh * kGv;
+        if (lane == 0) gv[0] = __expf(gL);
+        gv[kGvEg + lane] = egl;
+        gv[kGvEk + lane] = lane < L ? __expf(gL - gl) : 0.0f;
+    }
+
+    lds_barrier();   // gamma, beta visible
 
     // -A (strictly lower, fp32) and P (lower with diagonal, bf16)
     {
@@ -395,19 +484,6 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             Pb[t * SB + s] = f2bf(dec * QK[i]);
         }
     }
-    // K~ = e^{gamma_L - gamma} k^ in the sweep's lane order, from the fragments:
-    // KT[w][hb][mp][l][e] = K~[16 m + 4 g4 + i][32 w + 16 hb + l16], m = 2 mp + e / 4,
-    // which is element e of kp[hb][mp] scaled
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int mp = 0; mp < 2; ++mp) {
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = ekt[32 * mp + 16 * (e >> 2) + 4 * g4 + (e & 3)] * bfe(kp[hb][mp], e);
-            st16(blk + kOffKT + (((wave * 2 + hb) * 2 + mp) * 64 + lane) * 8,
-                 make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
-        }
     lds_barrier();
 
     // ---- T = (I + A)^-1 by 16 x 16 blocks, stored scaled by columns as
@@ -529,24 +605,10 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     uint4 vr[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) vr[mt] = ld16(Vs + (16 * mt + l16) * D + 8 * ((4 * wave + g4) ^ l16));
-    // the parked q^ values, read back from memory.  The empty asm clobbers
-    // memory, so the parking store's registers are not forwarded, and passes
-    // the lane's offset through, so that the parking addresses are not kept
-    // alive through the solve for reuse here.
-    int qoff = kOffQ + lane * 4;
-    asm volatile("" : "+v"(qoff) : : "memory");
-    uint2 qv[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-            qv[hb][mt] = *reinterpret_cast<const uint2 *>(blk + qoff + (mt * 8 + 2 * wave + hb) * 256);
-
     // ---- the products, wave w on key column blocks kb = 2w + hb and value
     // tiles 2w + hb (hb = 0, 1), with the permuted k order throughout:
-    //  W^T = k^T T'^T  (kb, mt) -> the W half of the sweep's WQ
-    //  W   = T' k^     (mt, kb) -> kept: its register pairs are the A operand of (P W)^T
-    //  U~  = T'' v     (mt, tile) -> the sweep's UA, and kept for P U~
+    //  W^T = k^T T'^T  (kb, mt) -> the sweep's W
+    //  U~  = T'' v     (mt, tile) -> the sweep's UA
     uint4 vp[2][2];   // v fragments, packed like kp
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -556,77 +618,32 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         for (int ks = 0; ks < 2; ++ks)
             vp[hb][ks] = pack_perm(mfma_bf16(vr[2 * ks], sel, z), mfma_bf16(vr[2 * ks + 1], sel, z));
     }
-    uint4 wp[2][2], up[2][2];   // W and U~ block pairs, packed in the permuted k order
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        const int kbk = 2 * wave + hb;
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-            f4v wpair[2], upair[2];
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int mt = 2 * kq + h2;
-                f4v wt = {0.f, 0.f, 0.f, 0.f}, w = wt, u = wt;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const uint4 t1 = lds_perm(T1 + (16 * mt + l16) * SB, ks, g4);
-                    const uint4 t2 = lds_perm(T2 + (16 * mt + l16) * SB, ks, g4);
-                    wt = mfma_bf16(kp[hb][ks], t1, wt);
-                    w = mfma_bf16(t1, kp[hb][ks], w);
-                    u = mfma_bf16(t2, vp[hb][ks], u);
-                }
-                wpair[h2] = w;
-                upair[h2] = u;
-                // wt: lane holds W[16 mt + l16][16 kbk + 4 g4 + i]; u: U~[16 mt + 4 g4 + i][16 kbk + l16]
-                *reinterpret_cast<uint2 *>(blk + kOffW + ((mt * 8 + kbk) * 64 + lane) * 4) =
-                    make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
-                *reinterpret_cast<uint2 *>(blk + kOffUA + ((kbk * 4 + mt) * 64 + lane) * 4) =
-                    make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
-                // bound how far the scheduler hoists the next block's LDS reads
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            wp[hb][kq] = pack_perm(wpair[0], wpair[1]);
-            up[hb][kq] = pack_perm(upair[0], upair[1]);
-        }
-    }
-    //  Q'^T = (e^gamma q^)^T - W^T P^T  (kb, mt) -> the Q' half of WQ
-    //  P U~                             (mt, tile) -> the chunk's output rows (fp32);
-    //  rows past the chunk's end are dropped by the buffer range check
-    const size_t orow = (size_t)hv * D;
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        X.P.out + (size_t)r0 * orow, 0, (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const int kbk = 2 * wave + hb;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            f4v pw = {0.f, 0.f, 0.f, 0.f}, pu = pw;
+            f4v wt = {0.f, 0.f, 0.f, 0.f}, u = wt;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const uint4 pr = lds_perm(Pb + (16 * mt + l16) * SB, ks, g4);
-                pw = mfma_bf16(wp[hb][ks], pr, pw);
-                pu = mfma_bf16(pr, up[hb][ks], pu);
+                const uint4 t1 = lds_perm(T1 + (16 * mt + l16) * SB, ks, g4);
+                const uint4 t2 = lds_perm(T2 + (16 * mt + l16) * SB, ks, g4);
+                wt = mfma_bf16(kp[hb][ks], t1, wt);
+                u = mfma_bf16(t2, vp[hb][ks], u);
             }
-            // pw: lane holds (P W)[t = 16 mt + l16][16 kbk + 4 g4 + i]
-            const int t = 16 * mt + l16;
-            const uint2 qq = qv[hb][mt];
-            const float q[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xffff0000u),
-                                __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xffff0000u)};
-            const float e = eg[t];
-            *reinterpret_cast<uint2 *>(blk + kOffQ + ((mt * 8 + kbk) * 64 + lane) * 4) =
-                make_uint2(pack2(fmaf(e, q[0], -pw[0]), fmaf(e, q[1], -pw[1])),
-                           pack2(fmaf(e, q[2], -pw[2]), fmaf(e, q[3], -pw[3])));
-            // pu: lane holds (P U~)[16 mt + 4 g4 + i][16 kbk + l16]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * mt + 4 * g4 + i;
-                __builtin_amdgcn_raw_buffer_store_b32(
-                    __float_as_uint(pu[i]), orsrc, (int)(((size_t)row * orow + (size_t)h * D + 16 * kbk + l16) * 4), 0,
-                    0);
-            }
+            // wt: lane holds W[16 mt + l16][16 kbk + 4 g4 + i]; u: U~[16 mt + 4 g4 + i][16 kbk + l16]
+            *reinterpret_cast<uint2 *>(blk + kOffW + ((mt * 8 + kbk) * 64 + lane) * 4) =
+                make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
+            *reinterpret_cast<uint2 *>(blk + kOffUA + ((kbk * 4 + mt) * 64 + lane) * 4) =
+                make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
+            // bound how far the scheduler hoists the next block's LDS reads
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    //  P rows 16 w .. 16 w + 15 -> the sweep's P, in the permuted k order
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+        st16(blk + kOffP + ((wave * 2 + ks) * 64 + lane) * 8, lds_perm(Pb + (16 * wave + l16) * SB, ks, g4));
 }
 
 // ---------------------------------------------------------------- sweep
@@ -641,6 +658,7 @@ constexpr int kSweepMs = 4 * kMsG, kSweepUs = 4 * kUsG;
 
 __device__ __forceinline__ f4v lds4(const float *p) { return *reinterpret_cast<const f4v *>(p); }
 __device__ __forceinline__ void lds4w(float *p, f4v v) { *reinterpret_cast<f4v *>(p) = v; }
+__device__ __forceinline__ f4v ldg4(const float *p) { return *reinterpret_cast<const f4v *>(p); }
 
 __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 {
@@ -694,13 +712,18 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     const size_t cstride = (size_t)hv * kBlockElems;
     const uint16_t *bp = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
     const uint16_t *pW = bp + kOffW + ((size_t)wave * 8 * 64 + lane) * 4;
-    const uint16_t *pQ = bp + kOffQ + ((size_t)wave * 8 * 64 + lane) * 4;
-    const uint16_t *pKT = bp + kOffKT + ((size_t)wave * 4 * 64 + lane) * 8;
     const uint16_t *pUA = bp + kOffUA + ((size_t)(tile * 4 + wave) * 64 + lane) * 4;
-    const float *pel = X.el + (size_t)cid0 * hv + h;
+    const uint16_t *pP = bp + kOffP + ((size_t)wave * 2 * 64 + lane) * 8;
+    // the key head's q^ and k^ fragments (qk_kernel), this wave's
+    const int kh = h / X.r;
+    const size_t fstride = (size_t)X.P.hk * 4 * kFragVec4 * 64;   // uint4 a chunk
+    const uint4 *pF = X.frag + (((size_t)cid0 * X.P.hk + kh) * 4 + wave) * kFragVec4 * 64 + lane;
+    // the gates: e^{gamma_L}, and this lane's rows' e^gamma and e^{gamma_L - gamma}
+    const size_t gstride = (size_t)hv * kGv;
+    const float *pG = X.gv + ((size_t)cid0 * hv + h) * kGv;
     const size_t orow = (size_t)hv * D;   // floats a packed output row
-    // this lane's output elements: rows 16 wave + 4 g4 + i of the chunk (the
-    // per-chunk kernel left P U~ there), column col of head h
+    // this lane's output elements: rows 16 wave + 4 g4 + i of the chunk,
+    // column col of head h
     auto out_rsrc = [&](int c) {
         const int r0 = s0 + c * kChunk;
         const int L = min(kChunk, s1 - r0);
@@ -711,30 +734,30 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
     for (int i = 0; i < 4; ++i) ooff[i] = (int)(((size_t)(16 * wave + 4 * g4 + i) * orow + (size_t)h * D + col) * 4);
 
-    uint2 ww[8], wq[8];
-    uint4 kt[4];
+    uint2 ww[8];
+    uint4 wq[4], kt[4], pp[2];
     uint2 ua;
     float eL;
-    f4v oin;
+    f4v eg4, ek4[4];
     // first chunk's operands, requested in the order the loop requests the
-    // next chunk's (W, Q'; ua, oin; kt, eL), so the memory-counter waits at the
-    // loop head see one request order on both of its entries
+    // next chunk's (W, q^; ua; P; k^, gates), so the memory-counter waits at
+    // the loop head see one request order on both of its entries
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        ww[kb] = ld8(pW + kb * 256);
-        wq[kb] = ld8(pQ + kb * 256);
-    }
+    for (int kb = 0; kb < 8; ++kb) ww[kb] = ld8(pW + kb * 256);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wq[j] = pF[(kFragQ + j) * 64];
     __builtin_amdgcn_sched_barrier(0);
     ua = *reinterpret_cast<const uint2 *>(pUA);
-    {
-        const __amdgpu_buffer_rsrc_t r = out_rsrc(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oin[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ooff[i], 0, 0));
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + j * 512);
-    eL = pel[0];
+    for (int ks = 0; ks < 2; ++ks) pp[ks] = ld16(pP + ks * 512);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kt[j] = pF[(kFragKp + j) * 64];
+    eL = pG[0];
+    eg4 = ldg4(pG + kGvEg + 16 * wave + 4 * g4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) ek4[m] = ldg4(pG + kGvEk + 16 * m + 4 * g4);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();   // Ms complete
 
@@ -744,10 +767,9 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     // and output rows past a chunk's end are dropped by the buffer range check.
     for (int c = 0; c < nck; ++c) {
         const int cn = min(c + 1, nck - 1);
-        const size_t nx = (size_t)cn * cstride;
-        const size_t nel = (size_t)cn * hv;
+        const size_t nx = (size_t)cn * cstride, nf = (size_t)cn * fstride, ng = (size_t)cn * gstride;
 
-        // rows [16 wave, 16 wave + 16) of W M0 and Q' M0, over all 128 state rows
+        // rows [16 wave, 16 wave + 16) of W M0 and (e^gamma q) M0, over all 128 state rows
         f4v aU = {0.f, 0.f, 0.f, 0.f}, aO = {0.f, 0.f, 0.f, 0.f};
         // the wave's B operands of all eight k-steps, read from LDS together
         // before the products (read one k-step at a time, each wait stalls the
@@ -761,25 +783,16 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
             const f4v mv = mvs[kb];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                const uint2 q2 = (kb & 1) ? make_uint2(wq[kb >> 1].z, wq[kb >> 1].w)
+                                          : make_uint2(wq[kb >> 1].x, wq[kb >> 1].y);
                 aU = mfma_f32(bfe2(ww[kb], i), mv[i], aU);
-                aO = mfma_f32(bfe2(wq[kb], i), mv[i], aO);
+                aO = mfma_f32(bfe2(q2, i), mv[i], aO);
             }
         }
-        // O = P U~ + Q' M0 for rows 16 wave + 4 g4 + i, stored before the next
-        // chunk's loads are issued (no load that a later wait needs is then
-        // queued behind a store)
-        {
-            const __amdgpu_buffer_rsrc_t r = out_rsrc(c);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(aO[i] + oin[i]), r, ooff[i], 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int kb = 0; kb < 8; ++kb) ww[kb] = ld8(pW + nx + kb * 256);
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            ww[kb] = ld8(pW + nx + kb * 256);
-            wq[kb] = ld8(pQ + nx + kb * 256);
-        }
+        for (int j = 0; j < 4; ++j) wq[j] = pF[nf + (kFragQ + j) * 64];
 
         // U = U~ - W M0 for the same rows, shared through Us
         f4v U;
@@ -790,21 +803,35 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         lds4w(Us + g4 * kUsG + l16 * kUsN + 4 * wave, U);
         __builtin_amdgcn_sched_barrier(0);
         ua = *reinterpret_cast<const uint2 *>(pUA + nx);
-        {
-            const __amdgpu_buffer_rsrc_t r = out_rsrc(cn);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) oin[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ooff[i], 0, 0));
-        }
         lds_barrier();   // Us complete; every wave is done reading Ms
 
-        // M <- e^{gamma_L} M + K~^T U on this wave's rows, then into Ms
-#pragma unroll
-        for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
         // U's four k-steps from LDS together, as for M0 above
         f4v uvs[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) uvs[m] = lds4(Us + g4 * kUsG + l16 * kUsN + 4 * m);
         __builtin_amdgcn_sched_barrier(0);
+        // O = e^gamma (q^ M0) + P U for rows 16 wave + 4 g4 + i: P U on bf16
+        // MFMA (an in-chunk product), U's rows 32 ks + 4 g4 + (e & 3) +
+        // 16 (e >> 2) packed as P's permuted k order reads them; rows past the
+        // chunk's end are dropped by the buffer range check
+        {
+            f4v pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) pu = mfma_bf16(pp[ks], pack_perm(uvs[2 * ks], uvs[2 * ks + 1]), pu);
+            const __amdgpu_buffer_rsrc_t r = out_rsrc(c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(eg4[i], aO[i], pu[i])), r, ooff[i], 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) pp[ks] = ld16(pP + nx + ks * 512);
+
+        // M <- e^{gamma_L} M + k^T (e^{gamma_L - gamma} U) on this wave's rows, then into Ms
+#pragma unroll
+        for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) uvs[m] = uvs[m] * ek4[m];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f4v uv = uvs[m];
@@ -815,8 +842,11 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kt[j] = ld16(pKT + nx + j * 512);
-        eL = pel[nel];
+        for (int j = 0; j < 4; ++j) kt[j] = pF[nf + (kFragKp + j) * 64];
+        eL = pG[ng];
+        eg4 = ldg4(pG + ng + kGvEg + 16 * wave + 4 * g4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ek4[m] = ldg4(pG + ng + kGvEk + 16 * m + 4 * g4);
 #pragma unroll
         for (int b = 0; b < 2; ++b) lds4w(Ms + g4 * kMsG + l16 * kMsN + 4 * (2 * wave + b), M[b]);
         lds_barrier();   // Ms complete; every wave is done reading Us
@@ -861,7 +891,8 @@ PrefillLayout prefill_layout(int hk, int hv, int dk, int dv, int n_seqs, int T)
     Lo.max_chunks_total = T / kChunk + n_seqs;
     const size_t nc = (size_t)Lo.max_chunks_total;
     Lo.blk = take(nc * hv * kBlockElems * 2);
-    Lo.el = take(nc * hv * 4);
+    Lo.gv = take(nc * hv * kGv * 4);
+    Lo.frag = take(nc * hk * 4 * kFragVec4 * 64 * sizeof(uint4));
     Lo.total = o;
     return Lo;
 }
@@ -886,7 +917,8 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     X.r = P.hv / P.hk;
     X.nc_total = Lo.max_chunks_total;
     X.blk = reinterpret_cast<uint16_t *>(ws + Lo.blk);
-    X.el = reinterpret_cast<float *>(ws + Lo.el);
+    X.gv = reinterpret_cast<float *>(ws + Lo.gv);
+    X.frag = reinterpret_cast<uint4 *>(ws + Lo.frag);
 
     static const hipError_t e_lds = hipFuncSetAttribute(reinterpret_cast<const void *>(intra_kernel),
                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kIntraLds);
@@ -894,6 +926,7 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
 
 
     const unsigned units = (unsigned)X.nc_total * P.hk;   // (chunk, key head) pairs
+    hipLaunchKernelGGL(qk_kernel, dim3(units), dim3(256), kQkLds, stream, X);
     hipLaunchKernelGGL(intra_kernel, dim3(8 * X.r * ((units + 7) / 8)), dim3(256), kIntraLds, stream, X);
     const unsigned groups = (unsigned)P.n_seqs * P.hv;
     hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), 0, stream, X);
