@@ -244,7 +244,8 @@ def main():
         cpu = cpu_baseline(b, tree, args.cpu_seconds, logged=args.log)
 
     # the instantiation that runs: dk = 128, logged or recording
-    row_kernel = f"rows_kernel<{shape.dk}, {'true' if args.log else 'false'}>"
+    row_kernel = (f"rows_kernel<{shape.dk}, {'true' if args.log else 'false'}, "
+                  f"{'true' if tree and not args.log else 'false'}>")
     line = {
         "metric": "GDN layer tokens/s and achieved HBM GB/s at 16 streams x 16-row verify",
         "value": round(tokens_per_s, 1),

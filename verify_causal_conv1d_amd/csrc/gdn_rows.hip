@@ -21,7 +21,7 @@
 //             lane's rows, then a butterfly over the eight 8-lane groups: a
 //             DPP row rotate, then the gfx950 lane-swap instructions.  No
 //             barrier inside the row loop, and no global load except a tree
-//             row's parent-state reload.  Narrow tiles spread the row loop's
+//             row's reload of the stream's state.  Narrow tiles spread the row loop's
 //             fp32 work (four operations per state element and row) over
 //             twice the waves of 64-column ones.
 //
@@ -29,12 +29,13 @@
 // before drafting", commit note on tree-shaped verify windows: a verify logs
 // its rows' decay, write and key instead of every row's state) record, per
 // row, alpha (per value head), khat (per key head) and the write delta with
-// M_t = alpha M_p + khat delta^T (per value head), and no snapshot.  A logged
-// tree row whose parent is not the row just done rebuilds the parent's state:
-// the stream's state reloaded, then the parent's path replayed from the log
-// kept in LDS with the very operations that first produced it.  The commit
-// replays the kept path the same way, so it reaches, bit for bit, the state a
-// recorded window holds for that row.
+// M_t = alpha M_p + khat delta^T (per value head), and no snapshot.  A tree
+// row (logged or recorded) whose parent is not the row just done rebuilds the
+// parent's state: the stream's state reloaded, then the parent's path
+// replayed from the decays, writes and keys kept in LDS with the very
+// operations that first produced it.  The commit by replay replays the kept
+// path the same way, so it reaches, bit for bit, the state a recorded window
+// holds for that row.
 //
 // Every row of every mode runs this same code in the same order, so a window's
 // rows equal one-row steps bit for bit and a tree's paths equal chains (the
@@ -57,11 +58,12 @@ __device__ __forceinline__ int global_channel(const RowsArgs &A, int dk, int kh,
     return 2 * A.hk * dk + h0 * A.dv + (ch - 2 * dk);
 }
 
-template <int DK, bool LOG>
+template <int DK, bool LOG, bool NT>
 __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 {
-    // LOG: a logged window or tree (LOG), a template argument so that the
-    // recording stores in the row loop carry no branch
+    // LOG: a logged window or tree, a template argument so that the recording
+    // stores in the row loop carry no branch.  NT: recorded trees, whose
+    // snapshots leave with non-temporal stores (chains keep ordinary ones)
     constexpr int R = DK / 8;  // state rows held by one lane
     extern __shared__ float smem[];
 
@@ -99,8 +101,9 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     float *act = smem;                                              // [mr][nch] conv+SiLU, then q^, k^
     float4 *wl = reinterpret_cast<float4 *>(act + mr * nch);        // [nch] conv weights
     uint16_t *raw = reinterpret_cast<uint16_t *>(wl + nch);         // [3 + mr][nch] raw bf16 rows
-    float *dlog = reinterpret_cast<float *>(raw + (3 + mr) * nch);  // [mr][vpw][dv] writes (logged)
-    float *galpha = dlog + (LOG ? mr * A.vpw * A.dv : 0);      // [mr][vpw]
+    float *dlog = reinterpret_cast<float *>(raw + (3 + mr) * nch);  // [mr][vpw][dv] writes (logged, trees)
+    const bool keep_writes = LOG || A.mode == MODE_TREE;
+    float *galpha = dlog + (keep_writes ? mr * A.vpw * A.dv : 0);   // [mr][vpw]
     float *gbeta = galpha + mr * A.vpw;                             // [mr][vpw]
     int *anc = reinterpret_cast<int *>(gbeta + mr * A.vpw);         // [mr][4]
     int *order = anc + mr * 4;                                      // [mr] processing order
@@ -378,13 +381,14 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         const int t_next = tree_order ? order[kn] : kn;
         const int p_next = tree_order ? anc[t_next * 4] : kn - 1;
         if (p != prev) {
-            // a tree row whose parent is not the row just done: reload the
-            // parent's state (the stream's own state for p == -1).  Recorded:
-            // the parent's snapshot, at the addresses this lane itself stored.
-            // Logged: the stream's state, then the parent's path replayed.
-            const float *src = (p < 0 || LOG)
-                                   ? st_in_head
-                                   : A.state_snap + ((size_t)(r0 + p) * A.hv + h) * head_elems + lane_off;
+            // a tree row whose parent is not the row just done: rebuild the
+            // parent's state.  The stream's state is reloaded (for p == -1 it
+            // is the state wanted), then the parent's path is replayed from
+            // the decays, writes and keys kept in LDS with the very
+            // operations that first produced it, so the rebuilt state equals
+            // the parent's bit for bit (a recorded snapshot reread instead has
+            // left the caches by then, and costs a full read from memory)
+            const float *src = st_in_head;
             // the address is formed anew here: kept from the first load of the
             // tile, its 16 row addresses would be held (and spilled) through
             // the prologue
@@ -394,8 +398,8 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
             // the loads complete inside the reload, so that rows without one
             // do not wait: a replay uses every loaded row at once, otherwise
             // an explicit wait
-            if (!LOG || p < 0) wait_vmem();
-            if (LOG && p >= 0) {
+            if (p < 0) wait_vmem();
+            if (p >= 0) {
                 const int path = pmask[p] | (1 << p);
                 for (int j = 0; j <= p; ++j) {
                     if (!((path >> j) & 1)) continue;
@@ -450,10 +454,12 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         d.z = be * (vv.z - al * u.z);
         d.w = be * (vv.w - al * u.w);
         // the recorded state (a snapshot, or the stream's state in place for a
-        // step) leaves with ordinary (cached) stores, each state row as soon
-        // as it is updated, so the stores issue among the row's arithmetic
-        // (non-temporal stores measured slower back to back, and a tree's
-        // parent reload finds the snapshot in the cache)
+        // step) leaves each state row as soon as it is updated, so the stores
+        // issue among the row's arithmetic.  Chains and steps store through
+        // the caches (non-temporal stores measured far slower back to back:
+        // 194 vs 152 us on the 16 x 16 verify); trees store non-temporally,
+        // which keeps the stream's state cached for their reloads (189 vs
+        // 203 us on 16 x 16-node trees)
         const int row = r0 + t;
         float *dst = (A.mode == MODE_STEP)
                          ? A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off
@@ -478,7 +484,10 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
                 o.w = fmaf(me.w, qq[e], o.w);
                 if (!LOG) {
                     const f4v val = {me.x, me.y, me.z, me.w};
-                    *reinterpret_cast<f4v *>(dst + (size_t)(i + e) * A.dv) = val;
+                    if (NT)
+                        __builtin_nontemporal_store(val, reinterpret_cast<f4v *>(dst + (size_t)(i + e) * A.dv));
+                    else
+                        *reinterpret_cast<f4v *>(dst + (size_t)(i + e) * A.dv) = val;
                 }
             }
         }
@@ -489,14 +498,11 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 
         if (grp == 0)
             *reinterpret_cast<float4 *>(A.out + ((size_t)row * A.hv + h) * A.dv + col) = o;
-        if (LOG) {
-            // the write: to the log, and to LDS for a later replay by this
-            // wave (every lane group holds the same delta)
-            if (grp == 0) {
-                *reinterpret_cast<float4 *>(A.log_delta + ((size_t)row * A.hv + h) * A.dv + col) = d;
-                *reinterpret_cast<float4 *>(dlog + (t * A.vpw + jl) * A.dv + col) = d;
-            }
-        }
+        // the write: to the log, and (logs and trees) to LDS for a later
+        // replay by this wave (every lane group holds the same delta)
+        if (LOG && grp == 0)
+            *reinterpret_cast<float4 *>(A.log_delta + ((size_t)row * A.hv + h) * A.dv + col) = d;
+        if (keep_writes && grp == 0) *reinterpret_cast<float4 *>(dlog + (t * A.vpw + jl) * A.dv + col) = d;
         prev = t;
         t = t_next;
         p = p_next;
@@ -647,22 +653,30 @@ size_t rows_lds_bytes(const RowsArgs &A)
     return sizeof(float) * mr * nch                  // act
            + sizeof(float) * 4 * nch                 // conv weights
            + sizeof(uint16_t) * (3 + mr) * nch       // raw rows
-           + (A.logged ? sizeof(float) * mr * A.vpw * A.dv : 0)   // logged writes
+           + (A.logged || A.mode == MODE_TREE ? sizeof(float) * mr * A.vpw * A.dv : 0)   // writes kept for replays
            + sizeof(float) * 2 * mr * A.vpw          // gates
            + sizeof(int) * (7 * mr + 1);             // ancestors, order, subtree sizes, ancestor masks, flag
 }
 
 namespace {
 // Dynamic LDS above the 64 KiB default has to be allowed per kernel once.
-template <int DK, bool LOG>
+template <int DK, bool LOG, bool NT>
 hipError_t launch_rows_as(const RowsArgs &A, dim3 grid, dim3 block, size_t lds, hipStream_t stream)
 {
-    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&rows_kernel<DK, LOG>),
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&rows_kernel<DK, LOG, NT>),
                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
                                                     (int)kRowsMaxLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((rows_kernel<DK, LOG>), grid, block, lds, stream, A);
+    hipLaunchKernelGGL((rows_kernel<DK, LOG, NT>), grid, block, lds, stream, A);
     return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_rows_dk(const RowsArgs &A, dim3 grid, dim3 block, size_t lds, hipStream_t stream)
+{
+    if (A.logged) return launch_rows_as<DK, true, false>(A, grid, block, lds, stream);
+    if (A.mode == MODE_TREE) return launch_rows_as<DK, false, true>(A, grid, block, lds, stream);
+    return launch_rows_as<DK, false, false>(A, grid, block, lds, stream);
 }
 }  // namespace
 
@@ -672,11 +686,8 @@ hipError_t launch_rows(const RowsArgs &A, hipStream_t stream)
     const dim3 block(rows_block_threads(A));
     const size_t lds = rows_lds_bytes(A);
     if (lds > kRowsMaxLds) return hipErrorInvalidValue;
-    if (A.dk == 128)
-        return A.logged ? launch_rows_as<128, true>(A, grid, block, lds, stream)
-                        : launch_rows_as<128, false>(A, grid, block, lds, stream);
-    return A.logged ? launch_rows_as<64, true>(A, grid, block, lds, stream)
-                    : launch_rows_as<64, false>(A, grid, block, lds, stream);
+    return A.dk == 128 ? launch_rows_dk<128>(A, grid, block, lds, stream)
+                       : launch_rows_dk<64>(A, grid, block, lds, stream);
 }
 
 hipError_t launch_commit(const CommitArgs &A, hipStream_t stream)
