@@ -73,8 +73,8 @@ def prefill_flops(shape, lengths, chunk=64):
     and T (beta V) (2 L^2 dk, 2 L^2 dv) and P U (2 L^2 dv), per value head.
     fp32 state contractions across chunks, per value head: W M0 and
     (e^gamma Q) M0, which read the state, and (e^{gamma_L - gamma} K)^T U, which
-    writes it (2 L dk dv each).  Products an implementation adds (P W here)
-    are not counted."""
+    writes it (2 L dk dv each).  Products an implementation adds (the 0/1-
+    selection transposes here) are not counted."""
     dk, dv = shape.dk, shape.dv
     sum_l = sum_l2 = 0
     for n in lengths:
@@ -117,6 +117,8 @@ def main():
                     help="window workloads: log every row's decay, write and key (gdn_recur_log) "
                          "instead of recording its state and tail; the commit by replay is timed too")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="verify workload: leave out the prompt-pass figures beside the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -282,6 +284,17 @@ def main():
     }
     if replay is not None:
         line["commit_by_replay"] = replay
+    if args.workload == "verify27b" and not args.log and not args.graph and not args.no_prefill:
+        # the prompt pass on the same layer (four packed prompts, T = 8,306),
+        # beside the headline: event-timed passes back to back
+        pb, p_wall, p_avg, p_med, _, p_roof = prefill_pass(torch, gdn, gi, dev, 20, 5, cold=False)
+        line["prefill"] = {
+            "workload": "4 prompts of 512, 1024, 2048 and 4722 rows packed in one pass, chunk 64",
+            "tokens_per_s": round(pb.rows * 20 / p_wall, 1),
+            "pass_ms_avg": round(p_avg, 5), "pass_ms_median": round(p_med, 5),
+            "roofline": p_roof,
+            "kernel_split": "profiles/prefill27b_kernel_trace.md",
+        }
     print(json.dumps(line), flush=True)
 
 
@@ -394,8 +407,13 @@ def timed(torch, dev, step, steps, warmup):
     return wall, sum(ms) / len(ms), ms[len(ms) // 2]
 
 
-def bench_prefill(args, torch, gdn, gi, dev):
-    """One step = one chunked prompt pass over the four packed prompts."""
+PREFILL_KERNELS = "qk_kernel, intra_kernel, sweep_kernel"
+
+
+def prefill_pass(torch, gdn, gi, dev, steps, warmup, copy_cal=False, cold=True):
+    """Timed chunked prompt passes over the four packed prompts: (batch,
+    wall seconds, event-timed average and median ms, cold median ms or None,
+    the roofline object)."""
     shape, lengths, kw = gi.workload("prefill27b")
     b = gi.make_batch(shape, lengths, **kw)
     params = gdn.LayerParams.from_host(b.params, dev)
@@ -409,14 +427,30 @@ def bench_prefill(args, torch, gdn, gi, dev):
         gdn.prefill_chunked(shape, params, seq_start, qkv, a, bb, tail, state, out, ws,
                             max_len=max(lengths))
 
-    if args.copy_calibration:
+    if copy_cal:
         copy_calibration(torch, dev)
-    wall, avg_ms, med_ms = timed(torch, dev, step, args.steps, args.warmup)
-    cold_ms = cold_timed(torch, dev, step)
+    wall, avg_ms, med_ms = timed(torch, dev, step, steps, warmup)
+    cold_ms = cold_timed(torch, dev, step) if cold else None
     f_bf16, f_fp32 = prefill_flops(shape, lengths)
     ideal_s = f_bf16 / (MFMA_BF16_PEAK_TFS * 1e12) + f_fp32 / (MFMA_FP32_PEAK_TFS * 1e12)
     fp32_equiv = f_fp32 + f_bf16 * MFMA_FP32_PEAK_TFS / MFMA_BF16_PEAK_TFS
-    achieved = fp32_equiv / (avg_ms * 1e-3) / 1e12
+    roof = {
+        "bound": "mfma", "achieved": round(fp32_equiv / (avg_ms * 1e-3) / 1e12, 2), "peak": MFMA_FP32_PEAK_TFS,
+        "unit": "TFLOP/s", "frac": round(ideal_s / (avg_ms * 1e-3), 4),
+        "traffic": measured_traffic("prefill27b", "gdn_prefill.hip"),
+        "kernel": f"whole pass ({PREFILL_KERNELS})",
+        "flops_bf16": f_bf16, "flops_fp32": f_fp32,
+        "note": "achieved counts bf16 flops at the fp32/bf16 peak ratio; frac = ideal time "
+                "(bf16 flops at 2.5 PF + fp32 flops at 157.3 TF) over the measured pass",
+    }
+    return b, wall, avg_ms, med_ms, cold_ms, roof
+
+
+def bench_prefill(args, torch, gdn, gi, dev):
+    """One step = one chunked prompt pass over the four packed prompts."""
+    shape, lengths, kw = gi.workload("prefill27b")
+    b, wall, avg_ms, med_ms, cold_ms, roof = prefill_pass(torch, gdn, gi, dev, args.steps, args.warmup,
+                                                           copy_cal=args.copy_calibration)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_prefill(b, args.cpu_seconds)
@@ -434,15 +468,7 @@ def bench_prefill(args, torch, gdn, gi, dev):
                    "prompts": lengths, "rows": b.rows, "seed": kw["seed"]},
         "pass_ms_avg": round(avg_ms, 5), "pass_ms_median": round(med_ms, 5),
         "pass_ms_cold_median": round(cold_ms, 5),
-        "roofline": {
-            "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFS,
-            "unit": "TFLOP/s", "frac": round(ideal_s / (avg_ms * 1e-3), 4),
-            "traffic": measured_traffic("prefill27b", "gdn_prefill.hip"),
-            "kernel": "whole pass (intra, sweep)",
-            "flops_bf16": f_bf16, "flops_fp32": f_fp32,
-            "note": "achieved counts bf16 flops at the fp32/bf16 peak ratio; frac = ideal time "
-                    "(bf16 flops at 2.5 PF + fp32 flops at 157.3 TF) over the measured pass",
-        },
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

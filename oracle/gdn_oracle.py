@@ -108,7 +108,7 @@ def raw_recurrence(alpha, beta, khat, qhat, v, M0, keep_all=False, mag=False):
 
 
 def _window(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, state,
-            snap64, snap32, tail_snap, log, snap_mag):
+            snap64, snap32, tail_snap, log, mag, snap_mag):
     row_start = _c(row_start, np.int32)
     n = row_start.shape[0] - 1
     R = int(row_start[-1]) if n > 0 else 0
@@ -120,8 +120,8 @@ def _window(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, s
     la = np.zeros((R, shape.hv), np.float64) if log else None
     ld = np.zeros((R, shape.hv, shape.dv), np.float64) if log else None
     lk = np.zeros((R, shape.hk, shape.dk), np.float64) if log else None
-    om = np.zeros((R, shape.hv, shape.dv), np.float64)
-    ldm = np.zeros((R, shape.hv, shape.dv), np.float64) if log else None
+    om = np.zeros((R, shape.hv, shape.dv), np.float64) if mag else None
+    ldm = np.zeros((R, shape.hv, shape.dv), np.float64) if (log and mag) else None
     sm = np.zeros((R, shape.hv, shape.dk, shape.dv), np.float32) if snap_mag else None
     sh = _shape(shape)
     rc = lib().gdn_oracle_window(
@@ -138,13 +138,14 @@ def _window(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, s
 
 
 def window(shape, conv_w, a_log, dt_bias, row_start, qkv, a, b, tail, state, *,
-           snap64=True, snap32=False, tail_snap=True, log=False, snap_mag=False):
+           snap64=True, snap32=False, tail_snap=True, log=False, mag=False, snap_mag=False):
     """Verify windows: each stream's rows form a chain.  Returns a dict with
-    ``o`` [R][hv][dv] and its magnitude ``o_mag``, ``tail_snap`` [R][3][C]
-    (uint16), the per-row states ``snap64`` (fp64) and/or ``snap32`` (rounded
-    to fp32), with ``snap_mag`` their magnitudes (fp32), and with ``log``
+    ``o`` [R][hv][dv], ``tail_snap`` [R][3][C] (uint16), the per-row states
+    ``snap64`` (fp64) and/or ``snap32`` (rounded to fp32), and with ``log``
     each row's decay ``log_alpha`` [R][hv], write ``log_delta`` [R][hv][dv]
-    with its magnitude ``log_delta_mag``, and key ``log_key`` [R][hk][dk].
+    and key ``log_key`` [R][hk][dk].  With ``mag`` also the magnitudes
+    ``o_mag`` of o (and ``log_delta_mag`` of the writes), with ``snap_mag``
+    those of the per-row states (fp32).
 
     A magnitude is the row's step carried out on magnitudes, from the state
     the row starts from: |M| and the inputs' absolute values, every sum by
@@ -153,15 +154,15 @@ def window(shape, conv_w, a_log, dt_bias, row_start, qkv, a, b, tail, state, *,
     magnitude.  It scales what rounding can do to a value whose terms
     cancel."""
     return _window(shape, conv_w, a_log, dt_bias, row_start, None, qkv, a, b, tail, state,
-                   snap64, snap32, tail_snap, log, snap_mag)
+                   snap64, snap32, tail_snap, log, mag, snap_mag)
 
 
 def tree(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, state, *,
-         snap64=True, snap32=False, tail_snap=True, log=False, snap_mag=False):
+         snap64=True, snap32=False, tail_snap=True, log=False, mag=False, snap_mag=False):
     """Tree windows: ``parent`` [R] holds each row's parent as a local index
     in its stream's window (-1 = the stream's own state and tail)."""
     return _window(shape, conv_w, a_log, dt_bias, row_start, parent, qkv, a, b, tail, state,
-                   snap64, snap32, tail_snap, log, snap_mag)
+                   snap64, snap32, tail_snap, log, mag, snap_mag)
 
 
 def replay(alpha, delta, key, M):

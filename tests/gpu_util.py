@@ -67,7 +67,7 @@ def oracle_rows(b: gi.Batch, tree=False, snap64=False, snap32=True, log=False, s
     if tree:
         args.append(b.parent.numpy())
     args += [h["qkv"], h["a"], h["b"], h["tail"], h["state"]]
-    return fn(*args, snap64=snap64, snap32=snap32, log=log, snap_mag=snap_mag)
+    return fn(*args, snap64=snap64, snap32=snap32, log=log, mag=True, snap_mag=snap_mag)
 
 
 def bound_err(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray) -> float:

@@ -162,7 +162,7 @@ def test_captured_logged_verify_round_equals_eager():
         assert torch.equal(state_g, state_e), f"replay {rep}: states differ"
         assert torch.equal(tail_g, tail_e), f"replay {rep}: tails differ"
         ref = oracle.window(shape, h["conv_w"], h["a_log"], h["dt_bias"], h["row_start"], h["qkv"], h["a"],
-                            h["b"], tail_o, state_o, snap64=False, tail_snap=False, log=True)
+                            h["b"], tail_o, state_o, snap64=False, tail_snap=False, log=True, mag=True)
         assert bound_err(out_g.cpu().numpy(), ref["o"], ref["o_mag"]) <= TOL_ROWS, rep
         assert bound_err(ld_g.cpu().numpy(), ref["log_delta"], ref["log_delta_mag"]) <= TOL_ROWS, rep
         assert max_rel_err(la_g.cpu().numpy(), ref["log_alpha"], 2) <= TOL_ROWS, rep

@@ -85,7 +85,7 @@ def check_log_against_oracle(b: gi.Batch, log, tree: bool):
     if tree:
         args.append(b.parent.numpy())
     args += [h["qkv"], h["a"], h["b"], h["tail"], h["state"]]
-    ref = fn(*args, snap64=False, snap32=False, tail_snap=False, log=True)
+    ref = fn(*args, snap64=False, snap32=False, tail_snap=False, log=True, mag=True)
     la, ld, lk = (t.cpu().numpy() for t in log)
     e_a = max_rel_err(la, ref["log_alpha"], 2)                      # each decay alone
     e_d = bound_err(ld, ref["log_delta"], ref["log_delta_mag"])     # each write element

@@ -519,33 +519,33 @@ def test_magnitudes_through_the_whole_path():
     shape = gi.Shape(hk=2, hv=4, dk=8, dv=6)
     batch = gi.make_batch(shape, [5, 3], seed=20)
     d = _np_batch(batch)
-    res = _run_window(shape, d, log=True, snap_mag=True)
+    res = _run_window(shape, d, log=True, mag=True, snap_mag=True)
     assert np.all(res["o_mag"] >= np.abs(res["o"]) * (1 - 1e-14))
     assert np.all(res["log_delta_mag"] >= np.abs(res["log_delta"]) * (1 - 1e-14))
     assert np.all(res["snap_mag"] >= np.abs(res["snap64"]).astype(np.float32) * (1 - 1e-6))
     # no write, non-negative state, positive query: every magnitude is the value
     dq = _signed_inputs(shape, [4, 2], 21, 1.0, 1.0, 1.0)
     dq["b"][:] = BF16_NEG_INF
-    r = _run_window(shape, dq, snap_mag=True)
+    r = _run_window(shape, dq, mag=True, snap_mag=True)
     assert np.all(r["o"] > 0) and np.allclose(r["o_mag"], r["o"], rtol=1e-14, atol=0)
     assert np.allclose(r["snap_mag"], r["snap64"], rtol=1e-6, atol=0)
     # first rows: negative v, positive key, non-negative state: |delta| = its magnitude
     dk_ = _signed_inputs(shape, [1, 1, 1], 22, 1.0, 1.0, -1.0)
-    r = _run_window(shape, dk_, log=True)
+    r = _run_window(shape, dk_, log=True, mag=True)
     assert np.all(r["log_delta"] < 0)
     assert np.allclose(r["log_delta_mag"], np.abs(r["log_delta"]), rtol=1e-14, atol=0)
     # from the zero state the write is beta v: magnitude beta |v| = |delta|
     dz = _signed_inputs(shape, [3, 2], 23, 1.0, -1.0, 1.0)
     dz["qkv"] = bf16(batch.qkv.float().numpy()[:5])       # mixed signs again
     dz["state"] = np.zeros_like(dz["state"])
-    r = _run_window(shape, dz, log=True)
+    r = _run_window(shape, dz, log=True, mag=True)
     first = [0, 3]
     assert np.allclose(r["log_delta_mag"][first], np.abs(r["log_delta"][first]), rtol=1e-15, atol=0)
     # a tree: each row's magnitudes are those of the chain over its path
     tb = _tree_batch([6, 4], seed=24)
     td = _np_batch(tb)
     tr = oracle.tree(TINY, td["conv_w"], td["a_log"], td["dt_bias"], td["row_start"], tb.parent.numpy(),
-                     td["qkv"], td["a"], td["b"], td["tail"], td["state"], snap_mag=True)
+                     td["qkv"], td["a"], td["b"], td["tail"], td["state"], mag=True, snap_mag=True)
     par = tb.parent.numpy()
     rs = td["row_start"]
     for st in range(2):
@@ -554,7 +554,7 @@ def test_magnitudes_through_the_whole_path():
             rows = [int(rs[st]) + i for i in gi.path_to_root(local, leaf)]
             ch = oracle.window(TINY, td["conv_w"], td["a_log"], td["dt_bias"], np.array([0, len(rows)], np.int32),
                                td["qkv"][rows], td["a"][rows], td["b"][rows], td["tail"][st:st + 1],
-                               td["state"][st:st + 1], snap_mag=True)
+                               td["state"][st:st + 1], mag=True, snap_mag=True)
             assert np.array_equal(ch["o_mag"], tr["o_mag"][rows])
             assert np.array_equal(ch["snap_mag"], tr["snap_mag"][rows])
 
@@ -575,7 +575,7 @@ def test_conv_cancellation_counts_its_terms():
     x = d["qkv"][0]
     d["tail"][0, 0, 2 * hkdk:] = x[2 * hkdk:]
     d["b"][:] = bf16(0.0)
-    r = _run_window(shape, d, log=True)
+    r = _run_window(shape, d, log=True, mag=True)
     xv = (x[2 * hkdk:].astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(shape.hv, shape.dv)
     assert np.all(r["log_delta"] == 0) and np.all(r["o"] == 0)
     assert np.allclose(r["log_delta_mag"][0], 0.5 * np.abs(xv), rtol=1e-15, atol=0)
@@ -585,7 +585,7 @@ def test_conv_cancellation_counts_its_terms():
 def test_prefill_matches_window_and_updates_in_place():
     batch = gi.make_batch(TINY, [7, 3, 1], seed=17)
     d = _np_batch(batch)
-    w = _run_window(TINY, d)
+    w = _run_window(TINY, d, mag=True)
     o, st, tl, om, fm = oracle.prefill(TINY, d["conv_w"], d["a_log"], d["dt_bias"], d["row_start"],
                                        d["qkv"], d["a"], d["b"], d["tail"], d["state"], mag=True)
     assert np.array_equal(o, w["o"])
