@@ -201,87 +201,6 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     const uint16_t *tail = A.tail_in + (size_t)s * 3 * C;
     const uint16_t *rows = A.qkv + (size_t)r0 * C;
     const int cpr = nch / 8;                     // 16-byte chunks a row
-    {
-        // every load of the batch is issued before any of them is consumed
-        const int nchunks = (len + 3) * cpr;
-        const int ngates = len * A.vpw;
-        constexpr int B = 8, BW = 2;             // row chunks / weights in flight per thread
-        for (int base = 0, wbase = 0, gbase = 0; base < nchunks || wbase < nch || gbase < ngates;
-             base += B * nthr, wbase += BW * nthr, gbase += nthr) {
-            uint4 v[B];
-            float4 w[BW];
-            // loads from clamped indices, unconditionally (the values past
-            // the end are not stored): no branch around the register arrays
-#pragma unroll
-            for (int k = 0; k < B; ++k) {
-                const int idx = min(base + k * nthr + tid, nchunks - 1);
-                const int rr = idx / cpr;
-                const int lc = (idx - rr * cpr) * 8;
-                const int gc = global_channel(A, DK, kh, h0, lc);
-                const uint16_t *src = rr < 3 ? tail + (size_t)rr * C + gc : rows + (size_t)(rr - 3) * C + gc;
-                v[k] = *reinterpret_cast<const uint4 *>(src);
-            }
-#pragma unroll
-            for (int k = 0; k < BW; ++k) {
-                const int ch = min(wbase + k * nthr + tid, nch - 1);
-                w[k] = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)global_channel(A, DK, kh, h0, ch) * 4);
-            }
-            const int gi = gbase + tid;
-            float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
-            if (gi < ngates) {
-                const int t = gi / A.vpw;
-                const int hh = h0 + (gi - t * A.vpw);
-                av = bf16f(A.a[(size_t)(r0 + t) * A.hv + hh]);
-                bv = bf16f(A.b[(size_t)(r0 + t) * A.hv + hh]);
-                al = A.a_log[hh];
-                db = A.dt_bias[hh];
-            }
-#pragma unroll
-            for (int k = 0; k < B; ++k) {
-                const int idx = base + k * nthr + tid;
-                if (idx < nchunks) {
-                    const int rr = idx / cpr;
-                    const int lc = (idx - rr * cpr) * 8;
-                    *reinterpret_cast<uint4 *>(raw + rr * nch + lc) = v[k];
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < BW; ++k) {
-                const int ch = wbase + k * nthr + tid;
-                if (ch < nch) wl[ch] = w[k];
-            }
-            if (gi < ngates) {
-                // gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
-                galpha[gi] = expf(log_decay(av, al, db));
-                gbeta[gi] = sigmoid_f(bv);
-            }
-        }
-    }
-
-    // ---- the state tile (row waves only): its loads stay in flight through
-    // the prologue
-    float4 m[R];
-    if (row_wave) {
-#pragma unroll
-        for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
-    }
-    lds_barrier();
-
-    // ---- conv + SiLU of every (row, channel), from the staged rows; a thread
-    // walks the rows of one channel, so its iterations are independent
-    for (int ch = tid; ch < nch; ch += nthr) {
-        const float4 w = wl[ch];
-        const uint16_t *rc = raw + ch;
-#pragma unroll 4
-        for (int t = 0; t < len; ++t) {
-            const int a1 = anc[t * 4 + 1], a2 = anc[t * 4 + 2], a3 = anc[t * 4 + 3];
-            float y = w.x * bf16f(rc[(3 + a3) * nch]);
-            y = fmaf(w.y, bf16f(rc[(3 + a2) * nch]), y);
-            y = fmaf(w.z, bf16f(rc[(3 + a1) * nch]), y);
-            y = fmaf(w.w, bf16f(rc[(3 + t) * nch]), y);
-            act[t * nch + ch] = silu_f(y);
-        }
-    }
     // ---- tail snapshots: the tail after row t is (x_{t-2}, x_{t-1}, x_t);
     // q/k channels are shared by the key head's workgroups, group 0 records
     // them; of the workgroups that share a head's columns, the first records.
@@ -302,45 +221,196 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
                 *reinterpret_cast<const uint4 *>(raw + src_row * nch + lc);
         }
     };
-    if (record_tails && !late_tails) {
-        tail_snaps(tid, nthr);
-    } else if (A.mode == MODE_STEP) {
-        // one-row step: the new tail replaces the old one in place.  The old
-        // tail is staged in LDS, and with one workgroup per key head in this
-        // mode no other workgroup reads these channels.
+    float4 m[R];
+    if (A.mode == MODE_STEP) {
+        // ---- one-row step: each input value goes from memory straight to the
+        // thread that uses it, with no staging through LDS.  Waves 0 and 1
+        // take the key head's q and k channels in the lanes the norm reads
+        // them (lane, and lane + 64 for dk = 128), so conv, SiLU and the norm
+        // run the window path's operations in its order without a barrier in
+        // between; thread i takes v channel i (a step's workgroup has at least
+        // as many threads as v channels).  Each thread rewrites its channels'
+        // tail in place after reading the old one: with one workgroup a key
+        // head in this mode no other workgroup reads those channels.
+        constexpr int NQ = DK / 64;               // q or k channels a lane
+        const int nv = A.vpw * A.dv;
         uint16_t *tl = A.tail_out + (size_t)s * 3 * C;
-        for (int idx = tid; idx < 3 * cpr; idx += nthr) {
-            const int j = idx / cpr;
-            const int lc = (idx - j * cpr) * 8;
-            const int gc = global_channel(A, DK, kh, h0, lc);
-            *reinterpret_cast<uint4 *>(tl + (size_t)j * C + gc) =
-                *reinterpret_cast<const uint4 *>(raw + (j + 1) * nch + lc);
-        }
-    }
-    lds_barrier();
-
-    // ---- L2 norms of q and k per row (q also scaled by dk^-1/2)
-    {
-        const int nwaves = nthr >> 6;
-        const float qscale = 1.0f / sqrtf((float)DK);
-        for (int pr = wave; pr < 2 * len; pr += nwaves) {
-            const int t = pr >> 1, which = pr & 1;
-            float *v = act + t * nch + which * DK;
-            const float x0 = v[lane];
-            float ss = x0 * x0;
-            float x1 = 0.0f;
-            if (DK == 128) {
-                x1 = v[lane + 64];
-                ss = fmaf(x1, x1, ss);
+        uint16_t xq[NQ][4], xv[4] = {0, 0, 0, 0};
+        float4 wq[NQ], wv = make_float4(0.f, 0.f, 0.f, 0.f);
+        int gq[NQ], gvc = 0;
+        const bool qk_wave = wave < 2;
+        if (qk_wave) {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                gq[j] = global_channel(A, DK, kh, h0, wave * DK + lane + 64 * j);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) xq[j][k] = tail[(size_t)k * C + gq[j]];
+                xq[j][3] = rows[gq[j]];
+                wq[j] = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)gq[j] * 4);
             }
+        }
+        if (tid < nv) {
+            gvc = global_channel(A, DK, kh, h0, 2 * DK + tid);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) xv[k] = tail[(size_t)k * C + gvc];
+            xv[3] = rows[gvc];
+            wv = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)gvc * 4);
+        }
+        float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
+        if (tid < A.vpw) {
+            av = bf16f(A.a[(size_t)r0 * A.hv + h0 + tid]);
+            bv = bf16f(A.b[(size_t)r0 * A.hv + h0 + tid]);
+            al = A.a_log[h0 + tid];
+            db = A.dt_bias[h0 + tid];
+        }
+        // the state tile (row waves only): in flight through the prologue
+        if (row_wave) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
+        }
+        if (qk_wave) {
+            float x[NQ];
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                float y = wq[j].x * bf16f(xq[j][0]);
+                y = fmaf(wq[j].y, bf16f(xq[j][1]), y);
+                y = fmaf(wq[j].z, bf16f(xq[j][2]), y);
+                y = fmaf(wq[j].w, bf16f(xq[j][3]), y);
+                x[j] = silu_f(y);
+            }
+            float ss = x[0] * x[0];
+            if (NQ == 2) ss = fmaf(x[NQ - 1], x[NQ - 1], ss);
             ss = sum_wave(ss);
             float sc = 1.0f / sqrtf(ss + 1e-6f);
-            if (which == 0) sc = sc * qscale;
-            v[lane] = x0 * sc;
-            if (DK == 128) v[lane + 64] = x1 * sc;
+            if (wave == 0) sc = sc * (1.0f / sqrtf((float)DK));
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                act[wave * DK + lane + 64 * j] = x[j] * sc;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) tl[(size_t)k * C + gq[j]] = xq[j][k + 1];
+            }
         }
+        if (tid < nv) {
+            float y = wv.x * bf16f(xv[0]);
+            y = fmaf(wv.y, bf16f(xv[1]), y);
+            y = fmaf(wv.z, bf16f(xv[2]), y);
+            y = fmaf(wv.w, bf16f(xv[3]), y);
+            act[2 * DK + tid] = silu_f(y);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tl[(size_t)k * C + gvc] = xv[k + 1];
+        }
+        if (tid < A.vpw) {
+            galpha[tid] = expf(log_decay(av, al, db));
+            gbeta[tid] = sigmoid_f(bv);
+        }
+        lds_barrier();
+    } else {
+        {
+            // every load of the batch is issued before any of them is consumed
+            const int nchunks = (len + 3) * cpr;
+            const int ngates = len * A.vpw;
+            constexpr int B = 8, BW = 2;             // row chunks / weights in flight per thread
+            for (int base = 0, wbase = 0, gbase = 0; base < nchunks || wbase < nch || gbase < ngates;
+                 base += B * nthr, wbase += BW * nthr, gbase += nthr) {
+                uint4 v[B];
+                float4 w[BW];
+                // loads from clamped indices, unconditionally (the values past
+                // the end are not stored): no branch around the register arrays
+    #pragma unroll
+                for (int k = 0; k < B; ++k) {
+                    const int idx = min(base + k * nthr + tid, nchunks - 1);
+                    const int rr = idx / cpr;
+                    const int lc = (idx - rr * cpr) * 8;
+                    const int gc = global_channel(A, DK, kh, h0, lc);
+                    const uint16_t *src = rr < 3 ? tail + (size_t)rr * C + gc : rows + (size_t)(rr - 3) * C + gc;
+                    v[k] = *reinterpret_cast<const uint4 *>(src);
+                }
+    #pragma unroll
+                for (int k = 0; k < BW; ++k) {
+                    const int ch = min(wbase + k * nthr + tid, nch - 1);
+                    w[k] = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)global_channel(A, DK, kh, h0, ch) * 4);
+                }
+                const int gi = gbase + tid;
+                float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
+                if (gi < ngates) {
+                    const int t = gi / A.vpw;
+                    const int hh = h0 + (gi - t * A.vpw);
+                    av = bf16f(A.a[(size_t)(r0 + t) * A.hv + hh]);
+                    bv = bf16f(A.b[(size_t)(r0 + t) * A.hv + hh]);
+                    al = A.a_log[hh];
+                    db = A.dt_bias[hh];
+                }
+    #pragma unroll
+                for (int k = 0; k < B; ++k) {
+                    const int idx = base + k * nthr + tid;
+                    if (idx < nchunks) {
+                        const int rr = idx / cpr;
+                        const int lc = (idx - rr * cpr) * 8;
+                        *reinterpret_cast<uint4 *>(raw + rr * nch + lc) = v[k];
+                    }
+                }
+    #pragma unroll
+                for (int k = 0; k < BW; ++k) {
+                    const int ch = wbase + k * nthr + tid;
+                    if (ch < nch) wl[ch] = w[k];
+                }
+                if (gi < ngates) {
+                    // gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+                    galpha[gi] = expf(log_decay(av, al, db));
+                    gbeta[gi] = sigmoid_f(bv);
+                }
+            }
+        }
+
+        // ---- the state tile (row waves only): its loads stay in flight through
+        // the prologue
+        if (row_wave) {
+    #pragma unroll
+            for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
+        }
+        lds_barrier();
+
+        // ---- conv + SiLU of every (row, channel), from the staged rows; a thread
+        // walks the rows of one channel, so its iterations are independent
+        for (int ch = tid; ch < nch; ch += nthr) {
+            const float4 w = wl[ch];
+            const uint16_t *rc = raw + ch;
+    #pragma unroll 4
+            for (int t = 0; t < len; ++t) {
+                const int a1 = anc[t * 4 + 1], a2 = anc[t * 4 + 2], a3 = anc[t * 4 + 3];
+                float y = w.x * bf16f(rc[(3 + a3) * nch]);
+                y = fmaf(w.y, bf16f(rc[(3 + a2) * nch]), y);
+                y = fmaf(w.z, bf16f(rc[(3 + a1) * nch]), y);
+                y = fmaf(w.w, bf16f(rc[(3 + t) * nch]), y);
+                act[t * nch + ch] = silu_f(y);
+            }
+        }
+        if (record_tails && !late_tails) tail_snaps(tid, nthr);
+        lds_barrier();
+
+        // ---- L2 norms of q and k per row (q also scaled by dk^-1/2)
+        {
+            const int nwaves = nthr >> 6;
+            const float qscale = 1.0f / sqrtf((float)DK);
+            for (int pr = wave; pr < 2 * len; pr += nwaves) {
+                const int t = pr >> 1, which = pr & 1;
+                float *v = act + t * nch + which * DK;
+                const float x0 = v[lane];
+                float ss = x0 * x0;
+                float x1 = 0.0f;
+                if (DK == 128) {
+                    x1 = v[lane + 64];
+                    ss = fmaf(x1, x1, ss);
+                }
+                ss = sum_wave(ss);
+                float sc = 1.0f / sqrtf(ss + 1e-6f);
+                if (which == 0) sc = sc * qscale;
+                v[lane] = x0 * sc;
+                if (DK == 128) v[lane + 64] = x1 * sc;
+            }
+        }
+        lds_barrier();
     }
-    lds_barrier();
 
     // ---- the log's decays (this workgroup's value heads) and keys (the key
     // head's workgroup group 0)
