@@ -27,8 +27,9 @@
 //   intra     per (chunk, value head), independent: the gates, T by 16 x 16
 //             blocks (fp32 forward substitution on the diagonal, fp32 MFMA
 //             off it), the conv + SiLU of the chunk's v channels, then W^T and
-//             U~ on bf16 MFMA, and P and e^gamma q^ as they are.  k^ and v are
-//             transposed by an exact MFMA with a 0/1 selection operand, and
+//             U~ on bf16 MFMA, and P as it is.  v is transposed by an exact
+//             MFMA with a 0/1 selection operand (k^ comes transposed from
+//             qk), and
 //             every product takes a k order in which one product's
 //             accumulator registers are the next one's operand, so nothing is
 //             transposed through LDS; products are formed transposed where
