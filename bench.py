@@ -441,7 +441,8 @@ def prefill_pass(torch, gdn, gi, dev, steps, warmup, copy_cal=False, cold=True):
         "kernel": f"whole pass ({PREFILL_KERNELS})",
         "flops_bf16": f_bf16, "flops_fp32": f_fp32,
         "note": "achieved counts bf16 flops at the fp32/bf16 peak ratio; frac = ideal time "
-                "(bf16 flops at 2.5 PF + fp32 flops at 157.3 TF) over the measured pass",
+                "(bf16 flops at 2.5 PF + fp32 flops at 157.3 TF) over the measured pass; the fp32 "
+                "state contractions run as exact three-term bf16 products on the bf16 matrix cores",
     }
     return b, wall, avg_ms, med_ms, cold_ms, roof
 

@@ -12,9 +12,11 @@
 // d_t = beta_t (v_t - alpha_t M_{t-1}^T k_t) over the chunk; the gated delta
 // rule is Yang, Kautz and Hatamizadeh, "Gated Delta Networks", 2024.)
 // The parallel per-chunk kernels form every operand that does not involve
-// the state; the sequential sweep forms [W; e^gamma q] M0 and the update on
-// fp32 MFMA, and P U (an in-chunk product of the chunk's own deltas U, which
-// only the sweep knows) on bf16 MFMA, and writes each output row once.
+// the state; the sequential sweep forms [W; e^gamma q] M0 and the update with
+// the fp32 operand (M0, U) split exactly into three bf16 terms (products as
+// exact as on fp32 MFMA, at the bf16 matrix rate), and P U (an in-chunk
+// product of the chunk's own deltas U, which only the sweep knows) on bf16
+// MFMA, and writes each output row once.
 //
 // Three launches on the caller's stream:
 //   qk        per (chunk, key head), independent: the causal conv (taps from
@@ -29,20 +31,19 @@
 //             off it), the conv + SiLU of the chunk's v channels, then W^T and
 //             U~ on bf16 MFMA, and P as it is.  v is transposed by an exact
 //             MFMA with a 0/1 selection operand (k^ comes transposed from
-//             qk), and
-//             every product takes a k order in which one product's
+//             qk), and every product takes a k order in which one product's
 //             accumulator registers are the next one's operand, so nothing is
 //             transposed through LDS; products are formed transposed where
 //             that puts each lane's values where the sweep's lanes read them,
 //             and everything leaves in that order.
 //   sweep     per (prompt, value head, 16 state columns), 4 waves; wave w
 //             keeps state rows [32w, 32w + 32) as two fp32 16 x 16 MFMA
-//             accumulators (v_mfma_f32_16x16x4_f32) and copies them to LDS,
-//             where every wave reads all of M0.  Per chunk: rows
-//             [16w, 16w + 16) of W M0 and (e^gamma q) M0 over the 128 state
-//             rows, U = U~ - W M0 shared through LDS, O = (e^gamma q) M0 + P U
-//             (P U on bf16 MFMA), then M = e^{gamma_L} M + K~^T U on the
-//             wave's rows.  Sequential over
+//             accumulators and leaves their three bf16 terms in LDS, where
+//             every wave reads all of M0.  Per chunk: rows [16w, 16w + 16)
+//             of W M0 and (e^gamma q) M0 over the 128 state rows, U = U~ - W M0
+//             shared through LDS (rounded for P U, in terms for the update),
+//             O = (e^gamma q) M0 + P U, then M = e^{gamma_L} M + K~^T U on the
+//             wave's rows, all on v_mfma_f32_16x16x32_bf16.  Sequential over
 //             the prompt's chunks, operands of chunk c + 1 fetched while
 //             chunk c computes; the state never leaves the chip.  The 8
 //             column tiles of one (prompt, head) share their operands and
@@ -81,6 +82,7 @@ constexpr int kGv = 132, kGvEg = 4, kGvEk = 68;
 // Word 3 of a raw buffer resource on gfx9-family chips (gfx950 included):
 // 32-bit data format, no swizzle; accesses past num_records are dropped.
 constexpr int kBufferDword3 = 0x00020000;
+constexpr int kNonTemporal = 2;   // cache-policy operand of a buffer store: nt
 
 struct Ctx {
     PrefillArgs P;
@@ -150,18 +152,6 @@ __device__ __forceinline__ float bfe(const uint4 &u, int e)
 {
     const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-}
-
-// bf16 value e (0..3) of an 8-byte vector, as fp32
-__device__ __forceinline__ float bfe2(const uint2 &u, int e)
-{
-    const uint32_t w = (e >> 1) == 0 ? u.x : u.y;
-    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-}
-
-__device__ __forceinline__ f4v mfma_f32(float a, float b, f4v c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f4v mfma_bf16(uint4 a, uint4 b, f4v c)
@@ -648,23 +638,63 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
 }
 
 // ---------------------------------------------------------------- sweep
-// LDS of a sweep workgroup (floats).  Ms holds the state slice M0 [128][16]
-// for every wave's B operands: element (row 16kb + 4g + i, column n) sits at
-// g*kMsG + n*kMsN + 4kb + i, so a lane's four rows of one k-block are one
-// 16-byte read and the 16 lanes of a row group fall on distinct banks.  Us
-// holds U [64][16] the same way: (row 16m + 4g + i, n) at g*kUsG + n*kUsN + 4m + i.
-constexpr int kMsN = 36, kMsG = 16 * kMsN + 4;
-constexpr int kUsN = 20, kUsG = 16 * kUsN + 4;
-constexpr int kSweepMs = 4 * kMsG, kSweepUs = 4 * kUsG;
+// The state contractions of the sweep (W M0, q^ M0 and the update k^T U')
+// pair a bf16 A operand (W, q^, k^ as the per-chunk kernels left them) with
+// an fp32 B operand (M0, or U' = e^{gamma_L - gamma} U).  An fp32 value x is
+// the exact sum of three bf16 values: t0 = x with its low 16 bits cleared,
+// t1 the same of x - t0, t2 = x - t0 - t1 (at most 8 significant bits, so a
+// bf16 exactly).  Each contraction runs as three bf16 MFMAs, one a term:
+// every product of a term with a bf16 operand is exact in fp32, and their
+// sum is a x up to the fp32 rounding of the accumulation, as in an fp32 MFMA
+// of the same operands (48 matrix-core cycles a 32-deep k-step instead of
+// 256).  The wave that holds a value splits it, once a chunk.
+//
+// LDS of a sweep workgroup, uint4 a lane (every access 16 or 8 bytes a lane,
+// lanes consecutive):
+//   Mb [3 terms][4 k-steps s][64 lanes]  the B operand of k-step s of W M0 and
+//        q^ M0: M0 rows 32 s + 4 g4 + {0..3} and 32 s + 16 + 4 g4 + {0..3},
+//        column l16 -- the two accumulator blocks of wave s, as they sit
+//   Ub [2 k-steps][64]  U rounded to bf16 (nearest), the B operand of P U:
+//        rows 32 ks + 4 g4 + {0..3} (wave 2 ks) and 32 ks + 16 + 4 g4 + {0..3}
+//        (wave 2 ks + 1)
+//   Us [3 terms][2 k-steps][64]  the terms of U', the B operand of the
+//        update, the same rows
+constexpr int kSwMb = 0, kSwUb = 12 * 64, kSwUs = kSwUb + 2 * 64, kSwLds = kSwUs + 6 * 64;
 
-__device__ __forceinline__ f4v lds4(const float *p) { return *reinterpret_cast<const f4v *>(p); }
-__device__ __forceinline__ void lds4w(float *p, f4v v) { *reinterpret_cast<f4v *>(p) = v; }
 __device__ __forceinline__ f4v ldg4(const float *p) { return *reinterpret_cast<const f4v *>(p); }
+// the high halves of two words: bf16 (truncated) of two fp32 values
+__device__ __forceinline__ uint32_t high2(uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x07060302u); }
+
+// the three bf16 terms of four fp32 values, 4 bf16 (8 bytes) each
+__device__ __forceinline__ void split4(f4v x, uint2 &t0, uint2 &t1, uint2 &t2)
+{
+    uint32_t a[4], b[4], c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        a[e] = __float_as_uint(x[e]);
+        const float r1 = x[e] - __uint_as_float(a[e] & 0xffff0000u);
+        b[e] = __float_as_uint(r1);
+        c[e] = __float_as_uint(r1 - __uint_as_float(b[e] & 0xffff0000u));
+    }
+    t0 = make_uint2(high2(a[0], a[1]), high2(a[2], a[3]));
+    t1 = make_uint2(high2(b[0], b[1]), high2(b[2], b[3]));
+    t2 = make_uint2(high2(c[0], c[1]), high2(c[2], c[3]));
+}
+
+// wave w's state blocks M[0], M[1] (rows 32 w + 16 b + 4 g4 + i) into Mb
+__device__ __forceinline__ void put_state(uint4 *sw, int wave, int lane, const f4v (&M)[2])
+{
+    uint2 a0, a1, a2, b0, b1, b2;
+    split4(M[0], a0, a1, a2);
+    split4(M[1], b0, b1, b2);
+    sw[kSwMb + (0 * 4 + wave) * 64 + lane] = make_uint4(a0.x, a0.y, b0.x, b0.y);
+    sw[kSwMb + (1 * 4 + wave) * 64 + lane] = make_uint4(a1.x, a1.y, b1.x, b1.y);
+    sw[kSwMb + (2 * 4 + wave) * 64 + lane] = make_uint4(a2.x, a2.y, b2.x, b2.y);
+}
 
 __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 {
-    __shared__ __align__(16) float Ms[kSweepMs];
-    __shared__ __align__(16) float Us[kSweepUs];
+    __shared__ uint4 sw[kSwLds];
     __shared__ int order[256];      // prompt of each length rank
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: operand bases stay scalar
@@ -699,16 +729,14 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     const int col = 16 * tile + l16;
 
     // this wave updates state rows [32 wave, 32 wave + 32): block b register i
-    // is row 32 wave + 16 b + 4 g4 + i (the 16x16 accumulator layout); every
-    // wave reads all 128 rows from Ms
+    // is row 32 wave + 16 b + 4 g4 + i (the 16x16 accumulator layout)
     float *st = X.P.state + ((size_t)pidx * hv + h) * D * D + col;
     f4v M[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) M[b][i] = st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D];
-        lds4w(Ms + g4 * kMsG + l16 * kMsN + 4 * (2 * wave + b), M[b]);
-    }
+    put_state(sw, wave, lane, M);
 
     const size_t cstride = (size_t)hv * kBlockElems;
     const uint16_t *bp = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
@@ -734,12 +762,14 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     int ooff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ooff[i] = (int)(((size_t)(16 * wave + 4 * g4 + i) * orow + (size_t)h * D + col) * 4);
+    uint2 *ub_mine = reinterpret_cast<uint2 *>(sw + kSwUb + (wave >> 1) * 64 + lane) + (wave & 1);
+    uint2 *us_mine = reinterpret_cast<uint2 *>(sw + kSwUs + (wave >> 1) * 64 + lane) + (wave & 1);
 
     uint2 ww[8];
     uint4 wq[4], kt[4], pp[2];
     uint2 ua;
     float eL;
-    f4v eg4, ek4[4];
+    f4v eg4, ek4;
     // first chunk's operands, requested in the order the loop requests the
     // next chunk's (W, q^; ua; P; k^, gates), so the memory-counter waits at
     // the loop head see one request order on both of its entries
@@ -757,10 +787,9 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     for (int j = 0; j < 4; ++j) kt[j] = pF[(kFragKp + j) * 64];
     eL = pG[0];
     eg4 = ldg4(pG + kGvEg + 16 * wave + 4 * g4);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) ek4[m] = ldg4(pG + kGvEk + 16 * m + 4 * g4);
+    ek4 = ldg4(pG + kGvEk + 16 * wave + 4 * g4);
     __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();   // Ms complete
+    lds_barrier();   // Mb complete
 
     // The loop is branch-free, so the compiler's memory-counter waits track
     // each operand exactly: each operand of chunk c + 1 is requested right
@@ -770,24 +799,24 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         const int cn = min(c + 1, nck - 1);
         const size_t nx = (size_t)cn * cstride, nf = (size_t)cn * fstride, ng = (size_t)cn * gstride;
 
-        // rows [16 wave, 16 wave + 16) of W M0 and (e^gamma q) M0, over all 128 state rows
+        // rows [16 wave, 16 wave + 16) of W M0 and (e^gamma q) M0, over all
+        // 128 state rows: four 32-deep k-steps, three terms each.  The B
+        // operands are read from LDS together before the products (read one
+        // k-step at a time, each wait stalls the matrix core).
         f4v aU = {0.f, 0.f, 0.f, 0.f}, aO = {0.f, 0.f, 0.f, 0.f};
-        // the wave's B operands of all eight k-steps, read from LDS together
-        // before the products (read one k-step at a time, each wait stalls the
-        // matrix core)
-        f4v mvs[8];
+        uint4 mb[3][4];
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) mvs[kb] = lds4(Ms + g4 * kMsG + l16 * kMsN + 4 * kb);
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) mb[t][s] = sw[kSwMb + (t * 4 + s) * 64 + lane];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            const f4v mv = mvs[kb];
+        for (int s = 0; s < 4; ++s) {
+            const uint4 wa = make_uint4(ww[2 * s].x, ww[2 * s].y, ww[2 * s + 1].x, ww[2 * s + 1].y);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint2 q2 = (kb & 1) ? make_uint2(wq[kb >> 1].z, wq[kb >> 1].w)
-                                          : make_uint2(wq[kb >> 1].x, wq[kb >> 1].y);
-                aU = mfma_f32(bfe2(ww[kb], i), mv[i], aU);
-                aO = mfma_f32(bfe2(q2, i), mv[i], aO);
+            for (int t = 0; t < 3; ++t) {
+                aU = mfma_bf16(wa, mb[t][s], aU);
+                aO = mfma_bf16(wq[s], mb[t][s], aO);
             }
         }
 #pragma unroll
@@ -795,62 +824,68 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
         for (int j = 0; j < 4; ++j) wq[j] = pF[nf + (kFragQ + j) * 64];
 
-        // U = U~ - W M0 for the same rows, shared through Us
+        // U = U~ - W M0 for the same rows: to Ub rounded, and U' = e^{gamma_L - gamma} U
+        // to Us in terms
         f4v U;
         U[0] = __uint_as_float(ua.x << 16) - aU[0];
         U[1] = __uint_as_float(ua.x & 0xffff0000u) - aU[1];
         U[2] = __uint_as_float(ua.y << 16) - aU[2];
         U[3] = __uint_as_float(ua.y & 0xffff0000u) - aU[3];
-        lds4w(Us + g4 * kUsG + l16 * kUsN + 4 * wave, U);
+        *ub_mine = make_uint2(pack2(U[0], U[1]), pack2(U[2], U[3]));
+        {
+            uint2 t0, t1, t2;
+            split4(U * ek4, t0, t1, t2);
+            us_mine[0] = t0;
+            us_mine[2 * 64 * 2] = t1;   // uint2 units: a term is 2 k-steps x 64 lanes x 2 halves
+            us_mine[2 * 2 * 64 * 2] = t2;
+        }
         __builtin_amdgcn_sched_barrier(0);
         ua = *reinterpret_cast<const uint2 *>(pUA + nx);
-        lds_barrier();   // Us complete; every wave is done reading Ms
+        lds_barrier();   // Ub, Us complete; every wave is done reading Mb
 
-        // U's four k-steps from LDS together, as for M0 above
-        f4v uvs[4];
+        uint4 ub[2], us[3][2];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) uvs[m] = lds4(Us + g4 * kUsG + l16 * kUsN + 4 * m);
+        for (int ks = 0; ks < 2; ++ks) ub[ks] = sw[kSwUb + ks * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) us[t][ks] = sw[kSwUs + (t * 2 + ks) * 64 + lane];
         __builtin_amdgcn_sched_barrier(0);
         // O = e^gamma (q^ M0) + P U for rows 16 wave + 4 g4 + i: P U on bf16
-        // MFMA (an in-chunk product), U's rows 32 ks + 4 g4 + (e & 3) +
-        // 16 (e >> 2) packed as P's permuted k order reads them; rows past the
-        // chunk's end are dropped by the buffer range check
+        // MFMA (an in-chunk product); rows past the chunk's end are dropped by
+        // the buffer range check.  The stores are non-temporal: nothing in the
+        // pass reads o, and the operand blocks the other tiles of the head
+        // still read stay in L2 (a 4,722-row prompt alone: 307 -> 278 us).
         {
             f4v pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) pu = mfma_bf16(pp[ks], pack_perm(uvs[2 * ks], uvs[2 * ks + 1]), pu);
+            for (int ks = 0; ks < 2; ++ks) pu = mfma_bf16(pp[ks], ub[ks], pu);
             const __amdgpu_buffer_rsrc_t r = out_rsrc(c);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(eg4[i], aO[i], pu[i])), r, ooff[i], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(eg4[i], aO[i], pu[i])), r, ooff[i], 0, kNonTemporal);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) pp[ks] = ld16(pP + nx + ks * 512);
 
-        // M <- e^{gamma_L} M + k^T (e^{gamma_L - gamma} U) on this wave's rows, then into Ms
+        // M <- e^{gamma_L} M + k^T U' on this wave's rows, then into Mb
 #pragma unroll
         for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) uvs[m] = uvs[m] * ek4[m];
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f4v uv = uvs[m];
+            for (int t = 0; t < 3; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) M[b] = mfma_f32(bfe(kt[2 * b + (m >> 1)], 4 * (m & 1) + i), uv[i], M[b]);
-        }
+                for (int b = 0; b < 2; ++b) M[b] = mfma_bf16(kt[2 * b + ks], us[t][ks], M[b]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) kt[j] = pF[nf + (kFragKp + j) * 64];
         eL = pG[ng];
         eg4 = ldg4(pG + ng + kGvEg + 16 * wave + 4 * g4);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) ek4[m] = ldg4(pG + ng + kGvEk + 16 * m + 4 * g4);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) lds4w(Ms + g4 * kMsG + l16 * kMsN + 4 * (2 * wave + b), M[b]);
-        lds_barrier();   // Ms complete; every wave is done reading Us
+        ek4 = ldg4(pG + ng + kGvEk + 16 * wave + 4 * g4);
+        put_state(sw, wave, lane, M);
+        lds_barrier();   // Mb complete; every wave is done reading Ub and Us
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
