@@ -190,6 +190,9 @@ int window_or_tree(const gdn_shape *shape, const gdn_params *params, int32_t n_s
         return fail(GDN_EUNSUPPORTED, "too many streams for one launch");
     if (gdn::rows_lds_bytes(A) > gdn::kRowsMaxLds)
         return fail(GDN_EUNSUPPORTED, "window needs %zu bytes of LDS", gdn::rows_lds_bytes(A));
+    // trees keep a quarter of the stream's state in LDS where it fits beside
+    // the rest, so that their reloads read less from memory
+    A.cache_rows = gdn::rows_cache_rows_that_fit(A);
     return launched(gdn::launch_rows(A, static_cast<hipStream_t>(stream)));
 }
 

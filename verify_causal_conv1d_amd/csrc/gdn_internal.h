@@ -36,6 +36,7 @@ struct RowsArgs {
     float *log_alpha;          // [total_rows][hv]      decay
     float *log_delta;          // [total_rows][hv][dv]  write
     float *log_key;            // [total_rows][hk][dk]  khat
+    int32_t cache_rows;        // MODE_TREE: dk / 32 when a quarter of each lane's state rows stays in LDS for the reloads, else 0
 };
 
 struct CommitArgs {
@@ -72,6 +73,20 @@ constexpr size_t kRowsMaxLds = 160 * 1024;
 // Threads of one row-kernel workgroup and its dynamic LDS bytes.
 int rows_block_threads(const RowsArgs &A);
 size_t rows_lds_bytes(const RowsArgs &A);
+// LDS of a row workgroup before the trees' state-row cache, which starts there
+__host__ __device__ inline size_t rows_state_cache_offset(const RowsArgs &A)
+{
+    const size_t nch = 2 * (size_t)A.dk + (size_t)A.vpw * A.dv;
+    const size_t mr = A.max_rows;
+    const size_t base = sizeof(float) * mr * nch                  // act
+           + sizeof(float) * 4 * nch                 // conv weights
+           + sizeof(uint16_t) * (3 + mr) * nch       // raw rows
+           + (A.logged || A.mode == MODE_TREE ? sizeof(float) * mr * A.vpw * A.dv : 0)   // writes kept for replays
+           + sizeof(float) * 2 * mr * A.vpw          // gates
+           + sizeof(int) * (7 * mr + 1);             // ancestors, order, subtree sizes, ancestor masks, flag
+    return (base + 15) & ~(size_t)15;
+}
+int rows_cache_rows_that_fit(const RowsArgs &A);   // dk / 32 for trees whose LDS has room, else 0
 
 hipError_t launch_rows(const RowsArgs &A, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &A, hipStream_t stream);

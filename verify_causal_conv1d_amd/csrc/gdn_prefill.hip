@@ -46,9 +46,10 @@
 //             wave's rows, all on v_mfma_f32_16x16x32_bf16.  Sequential over
 //             the prompt's chunks, operands of chunk c + 1 fetched while
 //             chunk c computes; the state never leaves the chip.  The 8
-//             column tiles of one (prompt, head) share their operands and
-//             are placed on one XCD (workgroup i runs on XCD i mod 8) so
-//             that they meet in that XCD's L2; prompts run longest first.
+//             column tiles of the r value heads of one (prompt, key head)
+//             share operands and are placed on one XCD (workgroup i runs on
+//             XCD i mod 8) so that they meet in that XCD's L2; prompts run
+//             longest first.
 // The prompt's final state replaces the stream's state, and its last three raw
 // rows (or a mix with the old tail for prompts shorter than three rows) its
 // conv tail, in place, both by the sweep, after every read of the old tail (prompt passes update the stream in place: page
@@ -700,12 +701,16 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: operand bases stay scalar
     const int l16 = lane & 15, g4 = lane >> 4;
     const int hv = X.P.hv, n = X.P.n_seqs;
-    // workgroup i runs on XCD i % 8: the 8 tiles of one (prompt, head) go to one XCD
+    // workgroup i runs on XCD i % 8: the 8 tiles of the r value heads of one
+    // (prompt, key head) go to one XCD, where they share the key head's
+    // fragments and each head's operand blocks in L2
+    const int r = X.r, hk = X.P.hk;
     const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
     const int tile = q & (NTILE - 1);
-    const int grp = ((q / NTILE) << 3) + xcd;
-    if (grp >= n * hv) return;
-    const int rank = grp / hv, h = grp - rank * hv;
+    const int gq = q / NTILE;                 // value-head slot on this XCD
+    const int u = (gq / r) * 8 + xcd;         // (prompt rank, key head)
+    if (u >= n * hk) return;
+    const int rank = u / hk, h = (u - rank * hk) * r + (gq - (gq / r) * r);
 
     // prompts by decreasing length (ties by index): the longest chains start first
     int pidx = rank;
@@ -964,8 +969,8 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     const unsigned units = (unsigned)X.nc_total * P.hk;   // (chunk, key head) pairs
     hipLaunchKernelGGL(qk_kernel, dim3(units), dim3(256), kQkLds, stream, X);
     hipLaunchKernelGGL(intra_kernel, dim3(8 * X.r * ((units + 7) / 8)), dim3(256), kIntraLds, stream, X);
-    const unsigned groups = (unsigned)P.n_seqs * P.hv;
-    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * ((groups + 7) / 8)), dim3(256), 0, stream, X);
+    const unsigned kunits = (unsigned)P.n_seqs * P.hk;   // (prompt, key head) pairs
+    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * X.r * ((kunits + 7) / 8)), dim3(256), 0, stream, X);
     return hipGetLastError();
 }
 

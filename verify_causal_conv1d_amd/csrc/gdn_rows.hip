@@ -110,6 +110,9 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     int *sub = order + mr;                                          // [mr] subtree sizes, then next free slot
     int *pmask = sub + mr;                                          // [mr] strict ancestors, a bit each
     int *bad = pmask + mr;
+    // trees: rows [0, R / 4) of each row wave's tile of the stream's state,
+    // [wave][row][lane], for the reloads
+    float4 *stc = reinterpret_cast<float4 *>(reinterpret_cast<unsigned char *>(smem) + rows_state_cache_offset(A));
 
     // ---- this wave's tile of the state
     // The workgroup holds tiles [part * tpw, (part + 1) * tpw) of each of its
@@ -443,6 +446,15 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     // tree reads each row's index and parent from LDS one row ahead; a chain
     // has them in closed form (row k, parent k - 1).
     const bool tree_order = A.mode == MODE_TREE;
+    // trees keep rows [0, R / 4) of the lane's tile in LDS (cache_rows is 0
+    // or R / 4), so a reload reads three quarters of the tile from memory
+    constexpr int RC = R / 4;
+    const bool cached = tree_order && A.cache_rows != 0;
+    float4 *my_stc = stc + (size_t)wave * RC * 64 + lane;
+    if (cached && row_wave) {
+#pragma unroll
+        for (int i = 0; i < RC; ++i) my_stc[i * 64] = m[i];
+    }
     int prev = -1;
     int t = tree_order ? order[0] : 0;
     int p = tree_order ? anc[t * 4] : -1;
@@ -453,7 +465,8 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         if (p != prev) {
             // a tree row whose parent is not the row just done: rebuild the
             // parent's state.  The stream's state is reloaded (for p == -1 it
-            // is the state wanted), then the parent's path is replayed from
+            // is the state wanted; a lane's first R / 4 rows from the copy in
+            // LDS when there is one), then the parent's path is replayed from
             // the decays, writes and keys kept in LDS with the very
             // operations that first produced it, so the rebuilt state equals
             // the parent's bit for bit (a recorded snapshot reread instead has
@@ -463,8 +476,15 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
             // tile, its 16 row addresses would be held (and spilled) through
             // the prologue
             asm volatile("" : "+v"(src));
+            if (cached) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(src + (size_t)i * A.dv);
+                for (int i = 0; i < RC; ++i) m[i] = my_stc[i * 64];
+            } else {
+#pragma unroll
+                for (int i = 0; i < RC; ++i) m[i] = *reinterpret_cast<const float4 *>(src + (size_t)i * A.dv);
+            }
+#pragma unroll
+            for (int i = RC; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(src + (size_t)i * A.dv);
             // the loads complete inside the reload, so that rows without one
             // do not wait: a replay uses every loaded row at once, otherwise
             // an explicit wait
@@ -716,16 +736,20 @@ int rows_block_threads(const RowsArgs &A)
     return wgs <= 256 ? max(need, 512) : need;
 }
 
+// row waves of a workgroup: vpw value heads of dv / 32 / cs column tiles each
+static size_t row_waves(const RowsArgs &A) { return (size_t)A.vpw * (A.dv / 32 / A.cs); }
+
 size_t rows_lds_bytes(const RowsArgs &A)
 {
-    const size_t nch = 2 * (size_t)A.dk + (size_t)A.vpw * A.dv;
-    const size_t mr = A.max_rows;
-    return sizeof(float) * mr * nch                  // act
-           + sizeof(float) * 4 * nch                 // conv weights
-           + sizeof(uint16_t) * (3 + mr) * nch       // raw rows
-           + (A.logged || A.mode == MODE_TREE ? sizeof(float) * mr * A.vpw * A.dv : 0)   // writes kept for replays
-           + sizeof(float) * 2 * mr * A.vpw          // gates
-           + sizeof(int) * (7 * mr + 1);             // ancestors, order, subtree sizes, ancestor masks, flag
+    return rows_state_cache_offset(A)
+           + (A.mode == MODE_TREE ? sizeof(float) * 4 * 64 * row_waves(A) * A.cache_rows : 0);
+}
+
+int rows_cache_rows_that_fit(const RowsArgs &A)
+{
+    const size_t rows = (size_t)A.dk / 32;   // a quarter of a lane's dk / 8 rows
+    const size_t need = rows_state_cache_offset(A) + sizeof(float) * 4 * 64 * row_waves(A) * rows;
+    return A.mode == MODE_TREE && need <= kRowsMaxLds ? (int)rows : 0;
 }
 
 namespace {
