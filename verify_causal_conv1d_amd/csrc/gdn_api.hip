@@ -256,7 +256,7 @@ int gdn_conv_step(const gdn_shape *shape, const gdn_params *params, int32_t n_st
     A.state_in = state;
     A.state_out = state;
     A.out = out;
-    return launched(gdn::launch_rows(A, static_cast<hipStream_t>(stream)));
+    return launched(gdn::launch_step(A, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_recur_window(const gdn_shape *shape, const gdn_params *params, int32_t n_streams,

@@ -88,6 +88,7 @@ __host__ __device__ inline size_t rows_state_cache_offset(const RowsArgs &A)
 }
 int rows_cache_rows_that_fit(const RowsArgs &A);   // dk / 32 for trees whose LDS has room, else 0
 
+hipError_t launch_step(const RowsArgs &A, hipStream_t stream);   // MODE_STEP, max_rows = 1, vpw = r
 hipError_t launch_rows(const RowsArgs &A, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &A, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs &A, hipStream_t stream);

@@ -58,6 +58,72 @@ __device__ __forceinline__ int global_channel(const RowsArgs &A, int dk, int kh,
     return 2 * A.hk * dk + h0 * A.dv + (ch - 2 * dk);
 }
 
+// One row of the recurrence on a lane's tile m: state rows [grp R, grp R + R)
+// of the head (stored form M = S^T), columns col .. col + 3.  krow and qrow
+// hold the lane's R entries of k^ and q^.  u = M^T k^ (the lane's rows, then
+// across the eight row groups), d = beta (v - alpha u), M <- alpha M + k^ d^T
+// with each updated state row stored to dst at once when STORE (so the stores
+// issue among the arithmetic; NT: non-temporal), o = M^T q^.  Window rows and
+// one-row steps both run this, so they agree bit for bit.
+template <int R, bool STORE, bool NT>
+__device__ __forceinline__ void row_step(float4 (&m)[R], const float *krow, const float *qrow, const float4 vv,
+                                         const float al, const float be, float *dst, const int dv,
+                                         float4 &d, float4 &o)
+{
+    float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < R; i += 4) {
+        const float4 kv = *reinterpret_cast<const float4 *>(krow + i);
+        const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u.x = fmaf(m[i + e].x, kk[e], u.x);
+            u.y = fmaf(m[i + e].y, kk[e], u.y);
+            u.z = fmaf(m[i + e].z, kk[e], u.z);
+            u.w = fmaf(m[i + e].w, kk[e], u.w);
+        }
+    }
+    u.x = sum_rows8(u.x);
+    u.y = sum_rows8(u.y);
+    u.z = sum_rows8(u.z);
+    u.w = sum_rows8(u.w);
+    d.x = be * (vv.x - al * u.x);
+    d.y = be * (vv.y - al * u.y);
+    d.z = be * (vv.z - al * u.z);
+    d.w = be * (vv.w - al * u.w);
+    o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < R; i += 4) {
+        const float4 kv = *reinterpret_cast<const float4 *>(krow + i);
+        const float4 qv = *reinterpret_cast<const float4 *>(qrow + i);
+        const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
+        const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float4 &me = m[i + e];
+            me.x = fmaf(kk[e], d.x, al * me.x);
+            me.y = fmaf(kk[e], d.y, al * me.y);
+            me.z = fmaf(kk[e], d.z, al * me.z);
+            me.w = fmaf(kk[e], d.w, al * me.w);
+            o.x = fmaf(me.x, qq[e], o.x);
+            o.y = fmaf(me.y, qq[e], o.y);
+            o.z = fmaf(me.z, qq[e], o.z);
+            o.w = fmaf(me.w, qq[e], o.w);
+            if (STORE) {
+                const f4v val = {me.x, me.y, me.z, me.w};
+                if (NT)
+                    __builtin_nontemporal_store(val, reinterpret_cast<f4v *>(dst + (size_t)(i + e) * dv));
+                else
+                    *reinterpret_cast<f4v *>(dst + (size_t)(i + e) * dv) = val;
+            }
+        }
+    }
+    o.x = sum_rows8(o.x);
+    o.y = sum_rows8(o.y);
+    o.z = sum_rows8(o.z);
+    o.w = sum_rows8(o.w);
+}
+
 template <int DK, bool LOG, bool NT>
 __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 {
@@ -83,14 +149,7 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
 
     // ---- layout of this stream's rows (device-side rules; a stream that
     // breaks them is skipped)
-    int r0, r1;
-    if (A.mode == MODE_STEP) {
-        r0 = s;
-        r1 = s + 1;
-    } else {
-        r0 = A.row_start[s];
-        r1 = A.row_start[s + 1];
-    }
+    const int r0 = A.row_start[s], r1 = A.row_start[s + 1];
     if (r0 < 0 || r1 < r0 || r1 > A.total_rows || r1 - r0 > A.max_rows) return;
     const int len = r1 - r0;
     if (len == 0) return;
@@ -208,7 +267,7 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     // q/k channels are shared by the key head's workgroups, group 0 records
     // them; of the workgroups that share a head's columns, the first records.
     // With helper waves these leave after the norms, from the helpers alone.
-    const bool record_tails = A.mode != MODE_STEP && !LOG && part == 0;
+    const bool record_tails = !LOG && part == 0;
     const int row_threads = 64 * A.vpw * tpw;
     const bool late_tails = nthr > row_threads;
     auto tail_snaps = [&](int first, int stride) {
@@ -225,89 +284,7 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         }
     };
     float4 m[R];
-    if (A.mode == MODE_STEP) {
-        // ---- one-row step: each input value goes from memory straight to the
-        // thread that uses it, with no staging through LDS.  Waves 0 and 1
-        // take the key head's q and k channels in the lanes the norm reads
-        // them (lane, and lane + 64 for dk = 128), so conv, SiLU and the norm
-        // run the window path's operations in its order without a barrier in
-        // between; thread i takes v channel i (a step's workgroup has at least
-        // as many threads as v channels).  Each thread rewrites its channels'
-        // tail in place after reading the old one: with one workgroup a key
-        // head in this mode no other workgroup reads those channels.
-        constexpr int NQ = DK / 64;               // q or k channels a lane
-        const int nv = A.vpw * A.dv;
-        uint16_t *tl = A.tail_out + (size_t)s * 3 * C;
-        uint16_t xq[NQ][4], xv[4] = {0, 0, 0, 0};
-        float4 wq[NQ], wv = make_float4(0.f, 0.f, 0.f, 0.f);
-        int gq[NQ], gvc = 0;
-        const bool qk_wave = wave < 2;
-        if (qk_wave) {
-#pragma unroll
-            for (int j = 0; j < NQ; ++j) {
-                gq[j] = global_channel(A, DK, kh, h0, wave * DK + lane + 64 * j);
-#pragma unroll
-                for (int k = 0; k < 3; ++k) xq[j][k] = tail[(size_t)k * C + gq[j]];
-                xq[j][3] = rows[gq[j]];
-                wq[j] = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)gq[j] * 4);
-            }
-        }
-        if (tid < nv) {
-            gvc = global_channel(A, DK, kh, h0, 2 * DK + tid);
-#pragma unroll
-            for (int k = 0; k < 3; ++k) xv[k] = tail[(size_t)k * C + gvc];
-            xv[3] = rows[gvc];
-            wv = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)gvc * 4);
-        }
-        float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
-        if (tid < A.vpw) {
-            av = bf16f(A.a[(size_t)r0 * A.hv + h0 + tid]);
-            bv = bf16f(A.b[(size_t)r0 * A.hv + h0 + tid]);
-            al = A.a_log[h0 + tid];
-            db = A.dt_bias[h0 + tid];
-        }
-        // the state tile (row waves only): in flight through the prologue
-        if (row_wave) {
-#pragma unroll
-            for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
-        }
-        if (qk_wave) {
-            float x[NQ];
-#pragma unroll
-            for (int j = 0; j < NQ; ++j) {
-                float y = wq[j].x * bf16f(xq[j][0]);
-                y = fmaf(wq[j].y, bf16f(xq[j][1]), y);
-                y = fmaf(wq[j].z, bf16f(xq[j][2]), y);
-                y = fmaf(wq[j].w, bf16f(xq[j][3]), y);
-                x[j] = silu_f(y);
-            }
-            float ss = x[0] * x[0];
-            if (NQ == 2) ss = fmaf(x[NQ - 1], x[NQ - 1], ss);
-            ss = sum_wave(ss);
-            float sc = 1.0f / sqrtf(ss + 1e-6f);
-            if (wave == 0) sc = sc * (1.0f / sqrtf((float)DK));
-#pragma unroll
-            for (int j = 0; j < NQ; ++j) {
-                act[wave * DK + lane + 64 * j] = x[j] * sc;
-#pragma unroll
-                for (int k = 0; k < 3; ++k) tl[(size_t)k * C + gq[j]] = xq[j][k + 1];
-            }
-        }
-        if (tid < nv) {
-            float y = wv.x * bf16f(xv[0]);
-            y = fmaf(wv.y, bf16f(xv[1]), y);
-            y = fmaf(wv.z, bf16f(xv[2]), y);
-            y = fmaf(wv.w, bf16f(xv[3]), y);
-            act[2 * DK + tid] = silu_f(y);
-#pragma unroll
-            for (int k = 0; k < 3; ++k) tl[(size_t)k * C + gvc] = xv[k + 1];
-        }
-        if (tid < A.vpw) {
-            galpha[tid] = expf(log_decay(av, al, db));
-            gbeta[tid] = sigmoid_f(bv);
-        }
-        lds_barrier();
-    } else {
+    {
         {
             // every load of the batch is issued before any of them is consumed
             const int nchunks = (len + 3) * cpr;
@@ -515,76 +492,20 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         const float *qrow = act + t * nch + grp * R;
         const float *krow = act + t * nch + DK + grp * R;
 
-        // u = M^T k (over the lane's rows, then across the four row groups)
-        float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int i = 0; i < R; i += 4) {
-            const float4 kv = *reinterpret_cast<const float4 *>(krow + i);
-            const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u.x = fmaf(m[i + e].x, kk[e], u.x);
-                u.y = fmaf(m[i + e].y, kk[e], u.y);
-                u.z = fmaf(m[i + e].z, kk[e], u.z);
-                u.w = fmaf(m[i + e].w, kk[e], u.w);
-            }
-        }
-        u.x = sum_rows8(u.x);
-        u.y = sum_rows8(u.y);
-        u.z = sum_rows8(u.z);
-        u.w = sum_rows8(u.w);
-
-        // delta = beta (v - alpha u);  M <- alpha M + k delta^T;  o = M^T q
+        // delta = beta (v - alpha u);  M <- alpha M + k delta^T;  o = M^T q.
+        // The recorded state (a snapshot) leaves each state row as soon as it
+        // is updated, so the stores issue among the row's arithmetic.  Chains
+        // store through the caches (non-temporal stores measured far slower
+        // back to back: 194 vs 152 us on the 16 x 16 verify); trees store
+        // non-temporally, which keeps the stream's state cached for their
+        // reloads (189 vs 203 us on 16 x 16-node trees)
         const float al = galpha[t * A.vpw + jl];
         const float be = gbeta[t * A.vpw + jl];
         const float4 vv = *reinterpret_cast<const float4 *>(act + t * nch + 2 * DK + jl * A.dv + col);
-        float4 d;
-        d.x = be * (vv.x - al * u.x);
-        d.y = be * (vv.y - al * u.y);
-        d.z = be * (vv.z - al * u.z);
-        d.w = be * (vv.w - al * u.w);
-        // the recorded state (a snapshot, or the stream's state in place for a
-        // step) leaves each state row as soon as it is updated, so the stores
-        // issue among the row's arithmetic.  Chains and steps store through
-        // the caches (non-temporal stores measured far slower back to back:
-        // 194 vs 152 us on the 16 x 16 verify); trees store non-temporally,
-        // which keeps the stream's state cached for their reloads (189 vs
-        // 203 us on 16 x 16-node trees)
         const int row = r0 + t;
-        float *dst = (A.mode == MODE_STEP)
-                         ? A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off
-                         : A.state_snap + ((size_t)row * A.hv + h) * head_elems + lane_off;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int i = 0; i < R; i += 4) {
-            const float4 kv = *reinterpret_cast<const float4 *>(krow + i);
-            const float4 qv = *reinterpret_cast<const float4 *>(qrow + i);
-            const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
-            const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float4 &me = m[i + e];
-                me.x = fmaf(kk[e], d.x, al * me.x);
-                me.y = fmaf(kk[e], d.y, al * me.y);
-                me.z = fmaf(kk[e], d.z, al * me.z);
-                me.w = fmaf(kk[e], d.w, al * me.w);
-                o.x = fmaf(me.x, qq[e], o.x);
-                o.y = fmaf(me.y, qq[e], o.y);
-                o.z = fmaf(me.z, qq[e], o.z);
-                o.w = fmaf(me.w, qq[e], o.w);
-                if (!LOG) {
-                    const f4v val = {me.x, me.y, me.z, me.w};
-                    if (NT)
-                        __builtin_nontemporal_store(val, reinterpret_cast<f4v *>(dst + (size_t)(i + e) * A.dv));
-                    else
-                        *reinterpret_cast<f4v *>(dst + (size_t)(i + e) * A.dv) = val;
-                }
-            }
-        }
-        o.x = sum_rows8(o.x);
-        o.y = sum_rows8(o.y);
-        o.z = sum_rows8(o.z);
-        o.w = sum_rows8(o.w);
+        float *dst = A.state_snap + ((size_t)row * A.hv + h) * head_elems + lane_off;
+        float4 d, o;
+        row_step<R, !LOG, NT>(m, krow, qrow, vv, al, be, dst, A.dv, d, o);
 
         if (grp == 0)
             *reinterpret_cast<float4 *>(A.out + ((size_t)row * A.hv + h) * A.dv + col) = o;
@@ -597,6 +518,130 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
         t = t_next;
         p = p_next;
     }
+}
+
+// One-row step in place: workgroup (stream, key head) over the key head's r
+// value heads, each value head's dv / 32 column tiles on a wave each.  Each
+// input value goes from memory straight to the thread that uses it, with no
+// staging through LDS: waves 0 and 1 take the key head's q and k channels in
+// the lanes the norm reads them (lane, and lane + 64 for dk = 128), so conv,
+// SiLU and the norm run the window path's operations in its order without a
+// barrier in between; thread i takes v channel i (the workgroup has at least
+// as many threads as v channels).  Each thread rewrites its channels' tail in
+// place after reading the old one: no other workgroup reads those channels.
+template <int DK>
+__global__ void __launch_bounds__(1024) step_kernel(const RowsArgs A)
+{
+    constexpr int R = DK / 8;  // state rows held by one lane
+    extern __shared__ float smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int s = blockIdx.x, kh = blockIdx.y;
+    const int vpw = A.r;
+    const int h0 = kh * vpw;
+    const int C = A.C;
+    const int nv = vpw * A.dv;
+    float *act = smem;                    // [2 dk + nv]: q^, k^, v of the row
+    float *galpha = act + 2 * DK + nv;    // [vpw]
+    float *gbeta = galpha + vpw;          // [vpw]
+    // wave -> (local value head, 32-column tile): dv / 32 = 2 or 4 tiles a head
+    const int tsh = A.dv == 128 ? 2 : 1;
+    const bool row_wave = wave < (vpw << tsh);
+    const int jl = min(wave >> tsh, vpw - 1);
+    const int tile = row_wave ? wave - (jl << tsh) : 0;
+    const int h = h0 + jl;
+    const int c4 = lane & 7, grp = lane >> 3;
+    const int col = tile * 32 + c4 * 4;
+    const size_t head_elems = (size_t)DK * A.dv;
+    const size_t lane_off = (size_t)(grp * R) * A.dv + col;
+    const float *st_in_head = A.state_in + ((size_t)s * A.hv + h) * head_elems + lane_off;
+    const uint16_t *tail = A.tail_in + (size_t)s * 3 * C;
+    const uint16_t *rows = A.qkv + (size_t)s * C;
+    const int r0 = s;
+    float4 m[R];
+    {
+        constexpr int NQ = DK / 64;               // q or k channels a lane
+        uint16_t *tl = A.tail_out + (size_t)s * 3 * C;
+        uint16_t xq[NQ][4], xv[4] = {0, 0, 0, 0};
+        float4 wq[NQ], wv = make_float4(0.f, 0.f, 0.f, 0.f);
+        int gq[NQ], gvc = 0;
+        const bool qk_wave = wave < 2;
+        if (qk_wave) {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                gq[j] = global_channel(A, DK, kh, h0, wave * DK + lane + 64 * j);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) xq[j][k] = tail[(size_t)k * C + gq[j]];
+                xq[j][3] = rows[gq[j]];
+                wq[j] = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)gq[j] * 4);
+            }
+        }
+        if (tid < nv) {
+            gvc = global_channel(A, DK, kh, h0, 2 * DK + tid);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) xv[k] = tail[(size_t)k * C + gvc];
+            xv[3] = rows[gvc];
+            wv = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)gvc * 4);
+        }
+        float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
+        if (tid < vpw) {
+            av = bf16f(A.a[(size_t)r0 * A.hv + h0 + tid]);
+            bv = bf16f(A.b[(size_t)r0 * A.hv + h0 + tid]);
+            al = A.a_log[h0 + tid];
+            db = A.dt_bias[h0 + tid];
+        }
+        // the state tile (row waves only): in flight through the prologue
+        if (row_wave) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
+        }
+        if (qk_wave) {
+            float x[NQ];
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                float y = wq[j].x * bf16f(xq[j][0]);
+                y = fmaf(wq[j].y, bf16f(xq[j][1]), y);
+                y = fmaf(wq[j].z, bf16f(xq[j][2]), y);
+                y = fmaf(wq[j].w, bf16f(xq[j][3]), y);
+                x[j] = silu_f(y);
+            }
+            float ss = x[0] * x[0];
+            if (NQ == 2) ss = fmaf(x[NQ - 1], x[NQ - 1], ss);
+            ss = sum_wave(ss);
+            float sc = 1.0f / sqrtf(ss + 1e-6f);
+            if (wave == 0) sc = sc * (1.0f / sqrtf((float)DK));
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                act[wave * DK + lane + 64 * j] = x[j] * sc;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) tl[(size_t)k * C + gq[j]] = xq[j][k + 1];
+            }
+        }
+        if (tid < nv) {
+            float y = wv.x * bf16f(xv[0]);
+            y = fmaf(wv.y, bf16f(xv[1]), y);
+            y = fmaf(wv.z, bf16f(xv[2]), y);
+            y = fmaf(wv.w, bf16f(xv[3]), y);
+            act[2 * DK + tid] = silu_f(y);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) tl[(size_t)k * C + gvc] = xv[k + 1];
+        }
+        if (tid < vpw) {
+            galpha[tid] = expf(log_decay(av, al, db));
+            gbeta[tid] = sigmoid_f(bv);
+        }
+        lds_barrier();
+    }
+    if (!row_wave) return;
+    wait_vmem();
+    const float *qrow = act + grp * R;
+    const float *krow = act + DK + grp * R;
+    const float4 vv = *reinterpret_cast<const float4 *>(act + 2 * DK + jl * A.dv + col);
+    float *dst = A.state_out + ((size_t)s * A.hv + h) * head_elems + lane_off;
+    float4 d, o;
+    row_step<R, true, false>(m, krow, qrow, vv, galpha[jl], gbeta[jl], dst, A.dv, d, o);
+    if (grp == 0) *reinterpret_cast<float4 *>(A.out + ((size_t)s * A.hv + h) * A.dv + col) = o;
 }
 
 // Commit: the accepted row's recorded state and tail replace the stream's.
@@ -773,6 +818,18 @@ hipError_t launch_rows_dk(const RowsArgs &A, dim3 grid, dim3 block, size_t lds, 
     return launch_rows_as<DK, false, false>(A, grid, block, lds, stream);
 }
 }  // namespace
+
+hipError_t launch_step(const RowsArgs &A, hipStream_t stream)
+{
+    const dim3 grid((unsigned)A.n_streams, (unsigned)A.hk);
+    const dim3 block(max(128, 64 * A.r * (A.dv / 32)));
+    const size_t lds = sizeof(float) * (2 * (size_t)A.dk + (size_t)A.r * A.dv + 2 * (size_t)A.r);
+    if (A.dk == 128)
+        hipLaunchKernelGGL((step_kernel<128>), grid, block, lds, stream, A);
+    else
+        hipLaunchKernelGGL((step_kernel<64>), grid, block, lds, stream, A);
+    return hipGetLastError();
+}
 
 hipError_t launch_rows(const RowsArgs &A, hipStream_t stream)
 {
