@@ -188,6 +188,25 @@ def test_step_matches_oracle_many_streams():
     assert np.array_equal(bits16(tail), ref["tail_snap"])
 
 
+@pytest.mark.parametrize("shape_name,n", [("SMALL", 300), ("dk64-dv128", 40), ("dk128-dv64", 40)])
+def test_steps_many_streams_and_mixed_heads(shape_name, n):
+    """One-row steps run one workgroup a (stream, key head): hundreds of
+    streams on the small layer, and both mixed head geometries, against the
+    oracle's one-step rows."""
+    shape = gi.SMALL if shape_name == "SMALL" else MIXED[shape_name]
+    b = gi.make_batch(shape, [1] * n, seed=91)
+    announce(f"conv_step {n} streams {shape}")
+    d = device_batch(b)
+    out = torch.full((n, shape.hv, shape.dv), float("nan"), device="cuda")
+    tail, state = d["tail"].clone(), d["state"].clone()
+    gdn.conv_step(shape, d["params"], d["qkv"], d["a"], d["b"], tail, state, out)
+    torch.cuda.synchronize()
+    ref = oracle_rows(b)
+    assert bound_err(out.cpu().numpy(), ref["o"], ref["o_mag"]) <= TOL_ROWS
+    assert max_rel_err(state.cpu().numpy(), ref["snap32"], 2) <= TOL_ROWS
+    assert np.array_equal(bits16(tail), ref["tail_snap"])
+
+
 def test_tree_paths_equal_chains_bitwise():
     shape, lengths, kw = gi.workload("tree27b")
     b = gi.make_batch(shape, lengths[:4], **kw)
