@@ -89,16 +89,18 @@ def prefill_flops(shape, lengths, chunk=64):
 
 def measured_traffic(key, source="gdn_rows.hip"):
     """HBM bytes a launch from the committed counter summary, or None when the
-    kernel source changed since the counters were taken."""
+    kernel source, or the device header every kernel includes, changed since
+    the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "verify_causal_conv1d_amd", "csrc", source)
+    csrc = os.path.join(ROOT, "verify_causal_conv1d_amd", "csrc")
     try:
         rec = json.load(open(path))[key]
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = hashlib.sha256(open(os.path.join(csrc, source), "rb").read()).hexdigest()
+        sha_h = hashlib.sha256(open(os.path.join(csrc, "gdn_device.h"), "rb").read()).hexdigest()
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sha or rec.get("device_h_sha256") != sha_h:
         return None
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 

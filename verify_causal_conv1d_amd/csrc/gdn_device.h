@@ -24,20 +24,32 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// softplus(x) = log(1 + e^x) without overflow or cancellation.
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+// The gates, SiLU and the norms use the hardware's exp2, log2, reciprocal and
+// reciprocal square root (about 1 ulp each; the IEEE sequences are 5 to 40
+// times as many instructions, 131 for log1pf(expf(x))), every kernel the same
+// functions, so window rows and one-row steps still agree bit for bit.
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+// softplus(x) = log(1 + e^x) without overflow.  For x < -17 the log term
+// rounds to 0 (the true value is below e^-17 of the result's unit, and the
+// decay it feeds differs from 1 by less than an fp32 ulp).
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))); }
+
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // log of the per-row decay: g = -exp(A_log) softplus(a + dt_bias), alpha = e^g.
 __device__ __forceinline__ float log_decay(float a, float a_log, float dt_bias)
 {
-    return -expf(a_log) * softplus_f(a + dt_bias);
+    return -__expf(a_log) * softplus_f(a + dt_bias);
 }
 
-// SiLU of a conv output: y * sigmoid(y), with the hardware exp2 and
-// reciprocal (within a few ulp, well inside the fp32 path's error budget).
-__device__ __forceinline__ float silu_f(float y) { return y * __frcp_rn(1.0f + __expf(-y)); }
+// the decay alpha = e^g
+__device__ __forceinline__ float decay_f(float g) { return __expf(g); }
+
+// SiLU of a conv output: y * sigmoid(y)
+__device__ __forceinline__ float silu_f(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
+
+// 1 / sqrt(sum of squares + eps) of an L2 norm
+__device__ __forceinline__ float inv_norm_f(float ss) { return __builtin_amdgcn_rsqf(ss + 1e-6f); }
 
 // Sum over the four 16-lane rows of the wave; every lane gets the same bits.
 // permlane16_swap pairs rows (0,1) and (2,3), permlane32_swap the two halves.

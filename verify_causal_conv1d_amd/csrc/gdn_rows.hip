@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
                 }
                 if (gi < ngates) {
                     // gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
-                    galpha[gi] = expf(log_decay(av, al, db));
+                    galpha[gi] = decay_f(log_decay(av, al, db));
                     gbeta[gi] = sigmoid_f(bv);
                 }
             }
@@ -383,7 +383,7 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
                     ss = fmaf(x1, x1, ss);
                 }
                 ss = sum_wave(ss);
-                float sc = 1.0f / sqrtf(ss + 1e-6f);
+                float sc = inv_norm_f(ss);
                 if (which == 0) sc = sc * qscale;
                 v[lane] = x0 * sc;
                 if (DK == 128) v[lane + 64] = x1 * sc;
@@ -609,7 +609,7 @@ __global__ void __launch_bounds__(1024) step_kernel(const RowsArgs A)
             float ss = x[0] * x[0];
             if (NQ == 2) ss = fmaf(x[NQ - 1], x[NQ - 1], ss);
             ss = sum_wave(ss);
-            float sc = 1.0f / sqrtf(ss + 1e-6f);
+            float sc = inv_norm_f(ss);
             if (wave == 0) sc = sc * (1.0f / sqrtf((float)DK));
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
@@ -628,7 +628,7 @@ __global__ void __launch_bounds__(1024) step_kernel(const RowsArgs A)
             for (int k = 0; k < 3; ++k) tl[(size_t)k * C + gvc] = xv[k + 1];
         }
         if (tid < vpw) {
-            galpha[tid] = expf(log_decay(av, al, db));
+            galpha[tid] = decay_f(log_decay(av, al, db));
             gbeta[tid] = sigmoid_f(bv);
         }
         lds_barrier();
