@@ -6,11 +6,13 @@
 //
 //   prologue  the raw bf16 rows of the window and the stream's tail (only the
 //             workgroup's channels) and the conv weights are staged in LDS
-//             with 16-byte loads issued together, so the prologue pays one
-//             global latency; then every (row, channel): causal conv (taps
-//             along the row's own branch) + SiLU, from LDS; gates per (row,
-//             value head); per row an L2 norm of q and of k (q also times
-//             dk^-1/2).  Tail snapshots are 16-byte copies out of the staged rows.
+//             with 16-byte loads issued together, and the state tile's loads
+//             right behind them, so the prologue pays one global latency and
+//             the state streams in while it runs; then causal conv (taps
+//             along the row's own branch) + SiLU, 8 channels of a row a
+//             thread, from LDS; gates per (row, value head); per row an L2
+//             norm of q and of k (q also times dk^-1/2).  Tail snapshots are
+//             16-byte copies out of the staged rows.
 //   rows      each wave owns 32 columns of one value head's state M = S^T
 //             ([dk][dv], dv contiguous).  Lane (c, g) = (lane & 7, lane >> 3)
 //             keeps rows [g*dk/8, (g+1)*dk/8) x columns [4c, 4c+4) of the
@@ -48,6 +50,16 @@
 
 namespace gdn {
 namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferDword3 = 0x00020000;   // buffer resource word 3 (gfx950 raw buffer)
+
+// bf16 number e (0..7) of eight packed in a 16-byte chunk, as fp32
+__device__ __forceinline__ float bf16_word(const uint4 &x, int e)
+{
+    const uint32_t w = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
 
 // Global channel of local prologue channel `ch`: [q of kh | k of kh | v of
 // the workgroup's value heads].
@@ -285,85 +297,113 @@ __global__ void __launch_bounds__(1024) rows_kernel(const RowsArgs A)
     };
     float4 m[R];
     {
-        {
-            // every load of the batch is issued before any of them is consumed
-            const int nchunks = (len + 3) * cpr;
-            const int ngates = len * A.vpw;
-            constexpr int B = 8, BW = 2;             // row chunks / weights in flight per thread
-            for (int base = 0, wbase = 0, gbase = 0; base < nchunks || wbase < nch || gbase < ngates;
-                 base += B * nthr, wbase += BW * nthr, gbase += nthr) {
-                uint4 v[B];
-                float4 w[BW];
-                // loads from clamped indices, unconditionally (the values past
-                // the end are not stored): no branch around the register arrays
-    #pragma unroll
-                for (int k = 0; k < B; ++k) {
-                    const int idx = min(base + k * nthr + tid, nchunks - 1);
-                    const int rr = idx / cpr;
-                    const int lc = (idx - rr * cpr) * 8;
-                    const int gc = global_channel(A, DK, kh, h0, lc);
-                    const uint16_t *src = rr < 3 ? tail + (size_t)rr * C + gc : rows + (size_t)(rr - 3) * C + gc;
-                    v[k] = *reinterpret_cast<const uint4 *>(src);
-                }
-    #pragma unroll
-                for (int k = 0; k < BW; ++k) {
-                    const int ch = min(wbase + k * nthr + tid, nch - 1);
-                    w[k] = *reinterpret_cast<const float4 *>(A.conv_w + (size_t)global_channel(A, DK, kh, h0, ch) * 4);
-                }
-                const int gi = gbase + tid;
-                float av = 0.f, bv = 0.f, al = 0.f, db = 0.f;
-                if (gi < ngates) {
-                    const int t = gi / A.vpw;
-                    const int hh = h0 + (gi - t * A.vpw);
-                    av = bf16f(A.a[(size_t)(r0 + t) * A.hv + hh]);
-                    bv = bf16f(A.b[(size_t)(r0 + t) * A.hv + hh]);
-                    al = A.a_log[hh];
-                    db = A.dt_bias[hh];
-                }
-    #pragma unroll
-                for (int k = 0; k < B; ++k) {
-                    const int idx = base + k * nthr + tid;
-                    if (idx < nchunks) {
-                        const int rr = idx / cpr;
-                        const int lc = (idx - rr * cpr) * 8;
-                        *reinterpret_cast<uint4 *>(raw + rr * nch + lc) = v[k];
-                    }
-                }
-    #pragma unroll
-                for (int k = 0; k < BW; ++k) {
-                    const int ch = wbase + k * nthr + tid;
-                    if (ch < nch) wl[ch] = w[k];
-                }
-                if (gi < ngates) {
-                    // gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
-                    galpha[gi] = decay_f(log_decay(av, al, db));
-                    gbeta[gi] = sigmoid_f(bv);
-                }
+        // Every load of a batch is issued before any of them is consumed; loads
+        // come from clamped indices, unconditionally (the values past the end
+        // are not stored), so no branch surrounds them.  Two row chunks and
+        // one weight a thread make one batch of a 16-row window at 768
+        // threads; longer windows take more.
+        const int nchunks = (len + 3) * cpr;
+        const int ngates = len * A.vpw;
+        auto load_chunk = [&](int idx) -> uint4 {
+            idx = min(idx, nchunks - 1);
+            const int rr = idx / cpr;
+            const int gc = global_channel(A, DK, kh, h0, (idx - rr * cpr) * 8);
+            return *reinterpret_cast<const uint4 *>(rr < 3 ? tail + (size_t)rr * C + gc : rows + (size_t)(rr - 3) * C + gc);
+        };
+        auto put_chunk = [&](int idx, const uint4 &v) {
+            if (idx < nchunks) {
+                const int rr = idx / cpr;
+                *reinterpret_cast<uint4 *>(raw + rr * nch + (idx - rr * cpr) * 8) = v;
             }
+        };
+        auto load_weight = [&](int ch) -> float4 {
+            return *reinterpret_cast<const float4 *>(A.conv_w + (size_t)global_channel(A, DK, kh, h0, min(ch, nch - 1)) * 4);
+        };
+        auto put_weight = [&](int ch, const float4 &w) {
+            if (ch < nch) wl[ch] = w;
+        };
+        // (a, b, A_log, dt_bias) of gate index gi = (row, local value head)
+        auto load_gate = [&](int gi) -> float4 {
+            gi = min(gi, ngates - 1);
+            const int t = gi / A.vpw;
+            const int hh = h0 + (gi - t * A.vpw);
+            return make_float4(bf16f(A.a[(size_t)(r0 + t) * A.hv + hh]), bf16f(A.b[(size_t)(r0 + t) * A.hv + hh]),
+                               A.a_log[hh], A.dt_bias[hh]);
+        };
+        auto put_gate = [&](int gi, const float4 &x) {
+            if (gi < ngates) {
+                // gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+                galpha[gi] = decay_f(log_decay(x.x, x.z, x.w));
+                gbeta[gi] = sigmoid_f(x.y);
+            }
+        };
+        {
+            const uint4 v0 = load_chunk(tid), v1 = load_chunk(nthr + tid);
+            const float4 w0 = load_weight(tid);
+            const float4 g0 = load_gate(tid);
+            // ---- the state tile, requested right behind the first batch and
+            // before any of it is consumed, so that the 16 B a lane and row of
+            // state stream in while the batch is written to LDS and the conv and
+            // norms run.  Helper waves read through a buffer resource of no size
+            // (no memory access, zeros): the code has no branch here, so the
+            // compiler's memory-counter waits for the batch leave these loads in
+            // flight (the counter retires loads in issue order).
+            {
+                const int wu = __builtin_amdgcn_readfirstlane(wave);
+                const int hu = h0 + min(wu / tpw, A.vpw - 1);
+                const float *head = A.state_in + ((size_t)s * A.hv + hu) * head_elems;
+                const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float *>(head), 0, wu < A.vpw * tpw ? (int)(head_elems * sizeof(float)) : 0, kBufferDword3);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)((lane_off + (size_t)i * A.dv) * sizeof(float)), 0, 0);
+                    m[i] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            put_chunk(tid, v0);
+            put_chunk(nthr + tid, v1);
+            put_weight(tid, w0);
+            put_gate(tid, g0);
         }
-
-        // ---- the state tile (row waves only): its loads stay in flight through
-        // the prologue
-        if (row_wave) {
-    #pragma unroll
-            for (int i = 0; i < R; ++i) m[i] = *reinterpret_cast<const float4 *>(st_in_head + (size_t)i * A.dv);
+        for (int base = 2 * nthr, wbase = nthr, gbase = nthr; base < nchunks || wbase < nch || gbase < ngates;
+             base += 2 * nthr, wbase += nthr, gbase += nthr) {
+            const uint4 v0 = load_chunk(base + tid), v1 = load_chunk(base + nthr + tid);
+            const float4 w0 = load_weight(wbase + tid);
+            const float4 g0 = load_gate(gbase + tid);
+            put_chunk(base + tid, v0);
+            put_chunk(base + nthr + tid, v1);
+            put_weight(wbase + tid, w0);
+            put_gate(gbase + tid, g0);
         }
         lds_barrier();
 
-        // ---- conv + SiLU of every (row, channel), from the staged rows; a thread
-        // walks the rows of one channel, so its iterations are independent
-        for (int ch = tid; ch < nch; ch += nthr) {
-            const float4 w = wl[ch];
-            const uint16_t *rc = raw + ch;
-    #pragma unroll 4
-            for (int t = 0; t < len; ++t) {
-                const int a1 = anc[t * 4 + 1], a2 = anc[t * 4 + 2], a3 = anc[t * 4 + 3];
-                float y = w.x * bf16f(rc[(3 + a3) * nch]);
-                y = fmaf(w.y, bf16f(rc[(3 + a2) * nch]), y);
-                y = fmaf(w.z, bf16f(rc[(3 + a1) * nch]), y);
-                y = fmaf(w.w, bf16f(rc[(3 + t) * nch]), y);
-                act[t * nch + ch] = silu_f(y);
+        // ---- conv + SiLU of every (row, channel), from the staged rows: a
+        // thread takes one 16-byte chunk (8 channels) of a row and reads the
+        // four raw rows of its taps at once (x_{t-3} .. x_t along the row's
+        // branch: raw rows 3 + anc[t][3], 3 + anc[t][2], 3 + anc[t][1], 3 + t;
+        // for a chain, rows t .. t + 3)
+        for (int idx = tid; idx < cpr * len; idx += nthr) {
+            const int t = idx / cpr;
+            const int lc = (idx - t * cpr) * 8;
+            const int src[4] = {3 + anc[t * 4 + 3], 3 + anc[t * 4 + 2], 3 + anc[t * 4 + 1], 3 + t};
+            uint4 xr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xr[j] = *reinterpret_cast<const uint4 *>(raw + src[j] * nch + lc);
+            float y8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float4 w = wl[lc + e];
+                float y = w.x * bf16_word(xr[0], e);
+                y = fmaf(w.y, bf16_word(xr[1], e), y);
+                y = fmaf(w.z, bf16_word(xr[2], e), y);
+                y = fmaf(w.w, bf16_word(xr[3], e), y);
+                y8[e] = silu_f(y);
             }
+            float4 *dst = reinterpret_cast<float4 *>(act + t * nch + lc);
+            dst[0] = make_float4(y8[0], y8[1], y8[2], y8[3]);
+            dst[1] = make_float4(y8[4], y8[5], y8[6], y8[7]);
         }
         if (record_tails && !late_tails) tail_snaps(tid, nthr);
         lds_barrier();
