@@ -486,7 +486,7 @@ def inproj_work(shape, rows, hidden, group):
     return nbytes, 2 * rows * n * hidden
 
 
-def inproj_kernel_name(torch, dev, shape, rows):
+def inproj_kernel_name(torch, dev, shape, rows, hidden, group):
     """The kernel instantiation gdn_inproj_affine4 launches for ``rows`` (the
     library picks it by tile count against the compute units), which names
     its measured traffic."""
@@ -494,6 +494,10 @@ def inproj_kernel_name(torch, dev, shape, rows):
     features = shape.channels + 2 * shape.hv
     if rows <= 32:
         blocks = (features + 15) // 16
+        j = (hidden // 128 + 7) // 8
+        nfd = next((c for c in (3, 2) if 4 * ((blocks + c - 1) // c) >= 3 * cus), 1)
+        if rows <= 16 and j <= 5 and 4 * nfd * (hidden // group) <= 512 * 3:
+            return f"inproj_decode_kernel<{nfd}, {j}>"
         return f"inproj_small_kernel<{1 if rows <= 16 else 2}, {2 if blocks // 2 >= cus else 1}>"
     ft = (features + 127) // 128
     if ft * ((rows + 127) // 128) <= cus:
@@ -522,7 +526,7 @@ def bench_inproj(args, torch, gdn, gi, dev):
     nbytes, flops = inproj_work(shape, rows, hidden, group)
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (MFMA_BF16_PEAK_TFS * 1e12)
-    kernel = inproj_kernel_name(torch, dev, shape, rows)
+    kernel = inproj_kernel_name(torch, dev, shape, rows, hidden, group)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(nbytes / (avg_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(t_hbm / (avg_ms * 1e-3), 4)}

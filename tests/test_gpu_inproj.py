@@ -77,6 +77,13 @@ CASES = {
     "rows40-h128-g64": (gi.SMALL, 40, 128, 64),
     "27b-rows400-h128-g32": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 400, 128, 32),
     "27b-rows600-h128-g128": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 600, 128, 128),
+    # up to 16 rows: three feature blocks a workgroup, every weight requested
+    # up front (a partial row tile, 3 chunks a wave); the small kernel where
+    # the scales and biases (groups of 32) or the chunks (48) exceed that
+    # kernel's loads
+    "27b-rows9-h3072-g64": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 9, 3072, 64),
+    "27b-rows16-h5120-g32": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 16, 5120, 32),
+    "27b-rows16-h6144-g64": (gi.Shape(hk=16, hv=48, dk=128, dv=128), 16, 6144, 64),
 }
 
 

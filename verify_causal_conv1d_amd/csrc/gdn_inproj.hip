@@ -20,6 +20,9 @@
 // the chunk.  The large kernel expands weights the same way, 16 or 32 inputs
 // of one feature (a pair or a quad of code words) a thread, into LDS.
 //
+//   decode (rows <= 16, hidden <= 5120): a workgroup is one to three blocks
+//          of 16 features x 16 rows; its 8 waves split the inputs and
+//          request all their weights at once.
 //   small  (rows <= 32): a workgroup is one or two blocks of 16 features x
 //          16 or 32 rows; its 8 waves split the inputs.
 //   large  a workgroup is 128 features x 128 or 256 rows on 32 x 32
@@ -189,6 +192,108 @@ __global__ void __launch_bounds__(512) inproj_small_kernel(const InprojArgs A)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = r0 + 16 * m + 4 * g4 + i;
+        if (r < A.rows) put(A, r, n, y[i]);
+    }
+}
+
+// ---------------------------------------------------------------- decode
+// The small kernel for 16 rows and at most 8 J chunks (J a wave): the same
+// work, chunk order and sums, but every code word of a wave's J chunks is
+// requested at the start, so that a workgroup holds all its weights in
+// flight at once (80 KB at the 27B-like layer) instead of one chunk a wave;
+// x (read from L2 by every workgroup) follows one chunk ahead, and the
+// blocks' scales and biases come through LDS.  Loads retire in issue order:
+// the first chunk waits only for its own codes, the later ones for all.
+constexpr int kDecodeSbLoads = 3;   // 16-byte scale and bias loads a thread
+
+template <int NF, int J>
+__global__ void __launch_bounds__(512) inproj_decode_kernel(const InprojArgs A)
+{
+    constexpr int W = 8;
+    __shared__ f4v red[W][NF][64];
+    // the blocks' scales and biases, [f][group][16] bf16 each (groups of at
+    // least 32 inputs: at most hidden / 32 of them, hidden <= 128 * 8 J)
+    constexpr int kMaxGroups = 8 * J * kChunk / 32;
+    __shared__ uint16_t ssb[2][NF][kMaxGroups * 16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int features = A.channels + 2 * A.hv;
+    const int blocks = (features + 15) / 16;
+    const int nck = A.hidden / kChunk, ng = A.hidden / A.group;
+    // (past the last block, a workgroup's second block repeats the last one
+    // and writes nothing)
+    const uint32_t *wblk[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+        wblk[f] = A.wq + (size_t)min((int)blockIdx.x * NF + f, blocks - 1) * nck * 256 + 4 * lane;
+    // scales and biases: at most kDecodeSbLoads 16-byte loads a thread (the
+    // launch checks), requested first and parked in LDS, so that a wave's code and
+    // x loads are not queued behind twenty 2-byte loads
+    const int sbq = ng * 16 / 8;   // 16-byte pieces of one block's scales
+    uint4 sbv[kDecodeSbLoads];
+#pragma unroll
+    for (int k2 = 0; k2 < kDecodeSbLoads; ++k2) {
+        const int q = min(tid + 512 * k2, 2 * NF * sbq - 1);
+        const int which = q / (NF * sbq), f = (q - which * NF * sbq) / sbq, e = q - (which * NF + f) * sbq;
+        const int nb = min((int)blockIdx.x * NF + f, blocks - 1);
+        sbv[k2] = ld16g((which ? A.biases : A.scales) + (size_t)nb * ng * 16 + 8 * e);
+    }
+    const uint16_t *xrow = A.x + (size_t)min(l16, A.rows - 1) * A.hidden + 32 * g4;
+    // chunk j of this wave (past the end, the last chunk again: loaded, not used)
+    auto chunk = [&](int j) { return min(wave + W * j, nck - 1); };
+    uint4 xv[2][4];
+    auto fetch_x = [&](int j, uint4 (&xd)[4]) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) xd[st] = ld16g(xrow + chunk(j) * kChunk + 8 * st);
+    };
+    fetch_x(0, xv[0]);
+    uint4 wv[J][NF];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) wv[j][f] = ld16g(wblk[f] + (size_t)chunk(j) * 256);
+#pragma unroll
+    for (int k2 = 0; k2 < kDecodeSbLoads; ++k2) {
+        const int q = tid + 512 * k2;
+        if (q < 2 * NF * sbq) {
+            const int which = q / (NF * sbq), f = (q - which * NF * sbq) / sbq, e = q - (which * NF + f) * sbq;
+            *reinterpret_cast<uint4 *>(&ssb[which][f][8 * e]) = sbv[k2];
+        }
+    }
+    lds_barrier();
+    f4v acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        if (j + 1 < J) fetch_x(j + 1, xv[(j + 1) & 1]);
+        if (wave + W * j < nck) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                    const int g = (chunk(j) * kChunk + 32 * g4) / A.group;
+                    acc[f] = mfma16x16x32(xv[j & 1][st],
+                                          dequant8(word(wv[j][f], st), bf16f(ssb[0][f][g * 16 + l16]), bf16f(ssb[1][f][g * 16 + l16])),
+                                          acc[f]);
+                }
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) red[wave][f][lane] = acc[f];
+    __syncthreads();
+    // wave f < NF adds the partial sums of block f (waves in order)
+    if (wave >= NF) return;
+    const int nb = blockIdx.x * NF + wave;
+    const int n = nb * 16 + l16;
+    if (nb >= blocks || n >= features) return;
+    f4v y = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) y += red[w][wave][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;
         if (r < A.rows) put(A, r, n, y[i]);
     }
 }
@@ -498,9 +603,33 @@ hipError_t launch_inproj(const InprojArgs &A, hipStream_t stream)
 {
     const int features = A.channels + 2 * A.hv;
     if (A.rows <= 32) {
-        // two feature blocks a workgroup while that still leaves a workgroup
-        // for every compute unit
         const int blocks = (features + 15) / 16;
+        // up to 16 rows and 40 chunks (hidden 5120): every weight requested
+        // up front.  Each workgroup reads all of x, so it takes as many
+        // feature blocks (up to 3) as leave workgroups for three quarters of
+        // the compute units (the 27B-like layer: 3, 216 workgroups), while
+        // the blocks' scales and biases fit the kernel's loads
+        const int J = (A.hidden / kChunk + 7) / 8;
+        int nfd = 1;
+        for (int c = 3; c >= 2; --c)
+            if (4 * ((blocks + c - 1) / c) >= 3 * compute_units()) {
+                nfd = c;
+                break;
+            }
+        if (A.rows <= 16 && J <= 5 && 4 * nfd * (A.hidden / A.group) <= 512 * kDecodeSbLoads) {
+            const dim3 grid((blocks + nfd - 1) / nfd, 1);
+            switch (nfd * 8 + J) {
+#define GDN_DECODE(NF, J) \
+    case NF * 8 + J: hipLaunchKernelGGL((inproj_decode_kernel<NF, J>), grid, dim3(512), 0, stream, A); break;
+                GDN_DECODE(1, 1) GDN_DECODE(1, 2) GDN_DECODE(1, 3) GDN_DECODE(1, 4) GDN_DECODE(1, 5)
+                GDN_DECODE(2, 1) GDN_DECODE(2, 2) GDN_DECODE(2, 3) GDN_DECODE(2, 4) GDN_DECODE(2, 5)
+                GDN_DECODE(3, 1) GDN_DECODE(3, 2) GDN_DECODE(3, 3) GDN_DECODE(3, 4) GDN_DECODE(3, 5)
+#undef GDN_DECODE
+            }
+            return hipGetLastError();
+        }
+        // otherwise two feature blocks a workgroup while that still leaves a
+        // workgroup for every compute unit
         const int nf = blocks / 2 >= compute_units() ? 2 : 1;
         const dim3 grid((blocks + nf - 1) / nf, A.rows <= 16 ? (A.rows + 15) / 16 : (A.rows + 31) / 32);
         if (A.rows <= 16) {
