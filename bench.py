@@ -192,27 +192,9 @@ def main():
             step()
         step = graph.replay
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Per-launch timing with events on the launch stream (torch's current
-    # stream, which is the stream libgdn launches on), then the wall clock of
-    # the whole timed region.
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    avg_ms = sum(kernel_ms) / len(kernel_ms)
-    med_ms = kernel_ms[len(kernel_ms) // 2]
+    # the timed region (events on the launch stream, torch's current stream,
+    # which is the stream libgdn launches on), then per-launch events
+    wall, avg_ms, med_ms = timed(torch, dev, step, args.steps, args.warmup)
 
     cold_ms = cold_timed(torch, dev, step) if not args.graph else None
     bytes_per_launch = window_bytes(shape, n, R, logged=args.log)
@@ -389,24 +371,35 @@ def cpu_model():
 
 
 def timed(torch, dev, step, steps, warmup):
-    """Warm-up, then per-launch events on torch's current stream (where libgdn
-    launches) and the wall clock of the whole timed region."""
+    """Warm-up, then the timed region: ``steps`` launches back to back,
+    bracketed by synchronisations, the wall clock and one event pair on
+    torch's current stream (where libgdn launches).  Returns the wall seconds,
+    the event time a launch (the average launch duration, inter-launch gaps
+    included) and the median of a second, untimed pass with an event pair
+    around each launch (per-launch event records add several microseconds of
+    gap each, so they stay out of the timed region)."""
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    first.record(stream)
+    for _ in range(steps):
+        step()
+    last.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = first.elapsed_time(last) / steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return wall, sum(ms) / len(ms), ms[len(ms) // 2]
+    return wall, avg_ms, ms[len(ms) // 2]
 
 
 PREFILL_KERNELS = "qk_kernel, intra_kernel, sweep_kernel"
