@@ -36,20 +36,21 @@
 //             transposed through LDS; products are formed transposed where
 //             that puts each lane's values where the sweep's lanes read them,
 //             and everything leaves in that order.
-//   sweep     per (prompt, value head, 16 state columns), 4 waves; wave w
-//             keeps state rows [32w, 32w + 32) as two fp32 16 x 16 MFMA
-//             accumulators and leaves their three bf16 terms in LDS, where
-//             every wave reads all of M0.  Per chunk: rows [16w, 16w + 16)
-//             of W M0 and (e^gamma q) M0 over the 128 state rows, U = U~ - W M0
-//             shared through LDS (rounded for P U, in terms for the update),
+//   sweep     per (prompt, value head, 32 state columns: two 16-column
+//             tiles), 4 waves; wave w keeps state rows [32w, 32w + 32) of
+//             both tiles as four fp32 16 x 16 MFMA accumulators and leaves
+//             their three bf16 terms in LDS, where every wave reads all of
+//             M0.  Per chunk and tile: rows [16w, 16w + 16) of W M0 and
+//             (e^gamma q) M0 over the 128 state rows, U = U~ - W M0 shared
+//             through LDS (rounded for P U, in terms for the update),
 //             O = (e^gamma q) M0 + P U, then M = e^{gamma_L} M + K~^T U on the
-//             wave's rows, all on v_mfma_f32_16x16x32_bf16.  Sequential over
-//             the prompt's chunks, operands of chunk c + 1 fetched while
-//             chunk c computes; the state never leaves the chip.  The 8
-//             column tiles of the r value heads of one (prompt, key head)
-//             share operands and are placed on one XCD (workgroup i runs on
-//             XCD i mod 8) so that they meet in that XCD's L2; prompts run
-//             longest first.
+//             wave's rows, all on v_mfma_f32_16x16x32_bf16; the chunk's
+//             operands serve both tiles.  Sequential over the prompt's
+//             chunks, operands of chunk c + 1 fetched while chunk c
+//             computes; the state never leaves the chip.  The 4 tile pairs
+//             of the r value heads of one (prompt, key head) share operands
+//             and are placed on one XCD (workgroup i runs on XCD i mod 8) so
+//             that they meet in that XCD's L2; prompts run longest first.
 // The prompt's final state replaces the stream's state, and its last three raw
 // rows (or a mix with the old tail for prompts shorter than three rows) its
 // conv tail, in place, both by the sweep, after every read of the old tail (prompt passes update the stream in place: page
@@ -650,17 +651,25 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
 // of the same operands (48 matrix-core cycles a 32-deep k-step instead of
 // 256).  The wave that holds a value splits it, once a chunk.
 //
+// A workgroup takes two adjacent 16-column tiles of a head (32 state
+// columns), so that the chunk's W, q^, k^ and P operands, which every tile of
+// the head reads whole, are requested once for both (the 4-prompt pass: 464
+// -> 398 us against one tile a workgroup).  Wave w keeps state rows
+// [32 w, 32 w + 32) x 32 columns (four 16 x 16 accumulators) and takes
+// output rows [16 w, 16 w + 16) of both tiles.
+//
 // LDS of a sweep workgroup, uint4 a lane (every access 16 or 8 bytes a lane,
-// lanes consecutive):
-//   Mb [3 terms][4 k-steps s][64 lanes]  the B operand of k-step s of W M0 and
-//        q^ M0: M0 rows 32 s + 4 g4 + {0..3} and 32 s + 16 + 4 g4 + {0..3},
-//        column l16 -- the two accumulator blocks of wave s, as they sit
-//   Ub [2 k-steps][64]  U rounded to bf16 (nearest), the B operand of P U:
-//        rows 32 ks + 4 g4 + {0..3} (wave 2 ks) and 32 ks + 16 + 4 g4 + {0..3}
-//        (wave 2 ks + 1)
-//   Us [3 terms][2 k-steps][64]  the terms of U', the B operand of the
-//        update, the same rows
-constexpr int kSwMb = 0, kSwUb = 12 * 64, kSwUs = kSwUb + 2 * 64, kSwLds = kSwUs + 6 * 64;
+// lanes consecutive), tile t of the pair:
+//   Mb [3 terms][4 k-steps s][2 tiles][64 lanes]  the B operand of k-step s
+//        of W M0 and q^ M0: M0 rows 32 s + 4 g4 + {0..3} and
+//        32 s + 16 + 4 g4 + {0..3}, column 16 t + l16 of the pair -- the two
+//        accumulator blocks of wave s, as they sit
+//   Ub [2 k-steps][2 tiles][64]  U rounded to bf16 (nearest), the B operand
+//        of P U: rows 32 ks + 4 g4 + {0..3} (wave 2 ks) and
+//        32 ks + 16 + 4 g4 + {0..3} (wave 2 ks + 1)
+//   Us [3 terms][2 k-steps][2 tiles][64]  the terms of U', the B operand of
+//        the update, the same rows
+constexpr int kSwMb = 0, kSwUb = 24 * 64, kSwUs = kSwUb + 4 * 64, kSwLds = kSwUs + 12 * 64;
 
 __device__ __forceinline__ f4v ldg4(const float *p) { return *reinterpret_cast<const f4v *>(p); }
 // the high halves of two words: bf16 (truncated) of two fp32 values
@@ -682,15 +691,18 @@ __device__ __forceinline__ void split4(f4v x, uint2 &t0, uint2 &t1, uint2 &t2)
     t2 = make_uint2(high2(c[0], c[1]), high2(c[2], c[3]));
 }
 
-// wave w's state blocks M[0], M[1] (rows 32 w + 16 b + 4 g4 + i) into Mb
-__device__ __forceinline__ void put_state(uint4 *sw, int wave, int lane, const f4v (&M)[2])
+// wave w's state blocks of both tiles into Mb, in their three terms
+__device__ __forceinline__ void put_state(uint4 *sw, int wave, int lane, const f4v (&M)[2][2])
 {
-    uint2 a0, a1, a2, b0, b1, b2;
-    split4(M[0], a0, a1, a2);
-    split4(M[1], b0, b1, b2);
-    sw[kSwMb + (0 * 4 + wave) * 64 + lane] = make_uint4(a0.x, a0.y, b0.x, b0.y);
-    sw[kSwMb + (1 * 4 + wave) * 64 + lane] = make_uint4(a1.x, a1.y, b1.x, b1.y);
-    sw[kSwMb + (2 * 4 + wave) * 64 + lane] = make_uint4(a2.x, a2.y, b2.x, b2.y);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        uint2 a0, a1, a2, b0, b1, b2;
+        split4(M[t][0], a0, a1, a2);
+        split4(M[t][1], b0, b1, b2);
+        sw[kSwMb + ((0 * 4 + wave) * 2 + t) * 64 + lane] = make_uint4(a0.x, a0.y, b0.x, b0.y);
+        sw[kSwMb + ((1 * 4 + wave) * 2 + t) * 64 + lane] = make_uint4(a1.x, a1.y, b1.x, b1.y);
+        sw[kSwMb + ((2 * 4 + wave) * 2 + t) * 64 + lane] = make_uint4(a2.x, a2.y, b2.x, b2.y);
+    }
 }
 
 __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
@@ -700,19 +712,21 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: operand bases stay scalar
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int hv = X.P.hv, n = X.P.n_seqs;
-    // workgroup i runs on XCD i % 8: the 8 tiles of the r value heads of one
-    // (prompt, key head) go to one XCD, where they share the key head's
+    const int hv = X.P.hv;
+    // workgroup i runs on XCD i % 8: the 4 tile pairs of the r value heads of
+    // one (prompt, key head) go to one XCD, where they share the key head's
     // fragments and each head's operand blocks in L2
     const int r = X.r, hk = X.P.hk;
+    constexpr int NP = NTILE / 2;             // tile pairs of a head
     const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-    const int tile = q & (NTILE - 1);
-    const int gq = q / NTILE;                 // value-head slot on this XCD
+    const int tp = q & (NP - 1);
+    const int gq = q / NP;                    // value-head slot on this XCD
     const int u = (gq / r) * 8 + xcd;         // (prompt rank, key head)
-    if (u >= n * hk) return;
+    if (u >= X.P.n_seqs * hk) return;
     const int rank = u / hk, h = (u - rank * hk) * r + (gq - (gq / r) * r);
 
     // prompts by decreasing length (ties by index): the longest chains start first
+    const int n = X.P.n_seqs;
     int pidx = rank;
     if (n <= 256) {
         if (tid < n) {
@@ -731,48 +745,48 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
     if (!prompt_chunks(X, pidx, s0, s1, cid0)) return;
     const int nck = (s1 - s0 + kChunk - 1) / kChunk;
     if (nck == 0) return;
-    const int col = 16 * tile + l16;
+    const int col = 32 * tp + l16;            // tile t: column col + 16 t
 
     // this wave updates state rows [32 wave, 32 wave + 32): block b register i
     // is row 32 wave + 16 b + 4 g4 + i (the 16x16 accumulator layout)
     float *st = X.P.state + ((size_t)pidx * hv + h) * D * D + col;
-    f4v M[2];
+    f4v M[2][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) M[b][i] = st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D];
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) M[t][b][i] = st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D + 16 * t];
     put_state(sw, wave, lane, M);
 
     const size_t cstride = (size_t)hv * kBlockElems;
     const uint16_t *bp = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
     const uint16_t *pW = bp + kOffW + ((size_t)wave * 8 * 64 + lane) * 4;
-    const uint16_t *pUA = bp + kOffUA + ((size_t)(tile * 4 + wave) * 64 + lane) * 4;
+    const uint16_t *pUA = bp + kOffUA + ((size_t)(2 * tp * 4 + wave) * 64 + lane) * 4;   // tile t: + 4 * 64 * 4 t
     const uint16_t *pP = bp + kOffP + ((size_t)wave * 2 * 64 + lane) * 8;
     // the key head's q^ and k^ fragments (qk_kernel), this wave's
     const int kh = h / X.r;
-    const size_t fstride = (size_t)X.P.hk * 4 * kFragVec4 * 64;   // uint4 a chunk
+    const size_t fstride = (size_t)X.P.hk * 4 * kFragVec4 * 64;
     const uint4 *pF = X.frag + (((size_t)cid0 * X.P.hk + kh) * 4 + wave) * kFragVec4 * 64 + lane;
     // the gates: e^{gamma_L}, and this lane's rows' e^gamma and e^{gamma_L - gamma}
     const size_t gstride = (size_t)hv * kGv;
     const float *pG = X.gv + ((size_t)cid0 * hv + h) * kGv;
-    const size_t orow = (size_t)hv * D;   // floats a packed output row
-    // this lane's output elements: rows 16 wave + 4 g4 + i of the chunk,
-    // column col of head h
+    const size_t orow = (size_t)hv * D;
     auto out_rsrc = [&](int c) {
         const int r0 = s0 + c * kChunk;
         const int L = min(kChunk, s1 - r0);
         return __builtin_amdgcn_make_buffer_rsrc(X.P.out + (size_t)r0 * orow, 0,
                                                  (int)((size_t)L * orow * sizeof(float)), kBufferDword3);
     };
+    // this lane's output elements: rows 16 wave + 4 g4 + i of the chunk,
+    // column col (+ 16 t) of head h
     int ooff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ooff[i] = (int)(((size_t)(16 * wave + 4 * g4 + i) * orow + (size_t)h * D + col) * 4);
-    uint2 *ub_mine = reinterpret_cast<uint2 *>(sw + kSwUb + (wave >> 1) * 64 + lane) + (wave & 1);
-    uint2 *us_mine = reinterpret_cast<uint2 *>(sw + kSwUs + (wave >> 1) * 64 + lane) + (wave & 1);
 
     uint2 ww[8];
     uint4 wq[4], kt[4], pp[2];
-    uint2 ua;
+    uint2 ua[2];
     float eL;
     f4v eg4, ek4;
     // first chunk's operands, requested in the order the loop requests the
@@ -783,7 +797,8 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
     for (int j = 0; j < 4; ++j) wq[j] = pF[(kFragQ + j) * 64];
     __builtin_amdgcn_sched_barrier(0);
-    ua = *reinterpret_cast<const uint2 *>(pUA);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ua[t] = *reinterpret_cast<const uint2 *>(pUA + t * 1024);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) pp[ks] = ld16(pP + ks * 512);
@@ -804,24 +819,29 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         const int cn = min(c + 1, nck - 1);
         const size_t nx = (size_t)cn * cstride, nf = (size_t)cn * fstride, ng = (size_t)cn * gstride;
 
-        // rows [16 wave, 16 wave + 16) of W M0 and (e^gamma q) M0, over all
-        // 128 state rows: four 32-deep k-steps, three terms each.  The B
-        // operands are read from LDS together before the products (read one
-        // k-step at a time, each wait stalls the matrix core).
-        f4v aU = {0.f, 0.f, 0.f, 0.f}, aO = {0.f, 0.f, 0.f, 0.f};
-        uint4 mb[3][4];
+        // W M0 and (e^gamma q) M0 for rows [16 wave, 16 wave + 16) over all 128
+        // state rows, tile after tile: four 32-deep k-steps, three terms each.
+        // A tile's B operands are read from LDS together before its products
+        // (read one k-step at a time, each wait stalls the matrix core).
+        f4v aU[2], aO[2];
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
+        for (int t = 0; t < 2; ++t) {
+            aU[t] = f4v{0.f, 0.f, 0.f, 0.f};
+            aO[t] = aU[t];
+            uint4 mb[3][4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) mb[t][s] = sw[kSwMb + (t * 4 + s) * 64 + lane];
-        __builtin_amdgcn_sched_barrier(0);
+            for (int tm = 0; tm < 3; ++tm)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 wa = make_uint4(ww[2 * s].x, ww[2 * s].y, ww[2 * s + 1].x, ww[2 * s + 1].y);
+                for (int s = 0; s < 4; ++s) mb[tm][s] = sw[kSwMb + ((tm * 4 + s) * 2 + t) * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                aU = mfma_bf16(wa, mb[t][s], aU);
-                aO = mfma_bf16(wq[s], mb[t][s], aO);
+            for (int s = 0; s < 4; ++s) {
+                const uint4 wa = make_uint4(ww[2 * s].x, ww[2 * s].y, ww[2 * s + 1].x, ww[2 * s + 1].y);
+#pragma unroll
+                for (int tm = 0; tm < 3; ++tm) {
+                    aU[t] = mfma_bf16(wa, mb[tm][s], aU[t]);
+                    aO[t] = mfma_bf16(wq[s], mb[tm][s], aO[t]);
+                }
             }
         }
 #pragma unroll
@@ -829,61 +849,63 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
         for (int j = 0; j < 4; ++j) wq[j] = pF[nf + (kFragQ + j) * 64];
 
-        // U = U~ - W M0 for the same rows: to Ub rounded, and U' = e^{gamma_L - gamma} U
-        // to Us in terms
-        f4v U;
-        U[0] = __uint_as_float(ua.x << 16) - aU[0];
-        U[1] = __uint_as_float(ua.x & 0xffff0000u) - aU[1];
-        U[2] = __uint_as_float(ua.y << 16) - aU[2];
-        U[3] = __uint_as_float(ua.y & 0xffff0000u) - aU[3];
-        *ub_mine = make_uint2(pack2(U[0], U[1]), pack2(U[2], U[3]));
-        {
+        // U = U~ - W M0: to Ub rounded, U' = e^{gamma_L - gamma} U to Us in terms
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f4v U;
+            U[0] = __uint_as_float(ua[t].x << 16) - aU[t][0];
+            U[1] = __uint_as_float(ua[t].x & 0xffff0000u) - aU[t][1];
+            U[2] = __uint_as_float(ua[t].y << 16) - aU[t][2];
+            U[3] = __uint_as_float(ua[t].y & 0xffff0000u) - aU[t][3];
+            uint2 *ub_mine = reinterpret_cast<uint2 *>(sw + kSwUb + ((wave >> 1) * 2 + t) * 64 + lane) + (wave & 1);
+            uint2 *us_mine = reinterpret_cast<uint2 *>(sw + kSwUs + ((wave >> 1) * 2 + t) * 64 + lane) + (wave & 1);
+            *ub_mine = make_uint2(pack2(U[0], U[1]), pack2(U[2], U[3]));
             uint2 t0, t1, t2;
             split4(U * ek4, t0, t1, t2);
             us_mine[0] = t0;
-            us_mine[2 * 64 * 2] = t1;   // uint2 units: a term is 2 k-steps x 64 lanes x 2 halves
-            us_mine[2 * 2 * 64 * 2] = t2;
+            us_mine[2 * 2 * 64 * 2] = t1;       // uint2 units: a term is 2 k-steps x 2 tiles x 64 lanes x 2 halves
+            us_mine[2 * 2 * 2 * 64 * 2] = t2;
         }
         __builtin_amdgcn_sched_barrier(0);
-        ua = *reinterpret_cast<const uint2 *>(pUA + nx);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ua[t] = *reinterpret_cast<const uint2 *>(pUA + nx + t * 1024);
         lds_barrier();   // Ub, Us complete; every wave is done reading Mb
 
-        uint4 ub[2], us[3][2];
+        const __amdgpu_buffer_rsrc_t orsrc = out_rsrc(c);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) ub[ks] = sw[kSwUb + ks * 64 + lane];
+        for (int t = 0; t < 2; ++t) {
+            uint4 ub[2], us[3][2];
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
+            for (int ks = 0; ks < 2; ++ks) ub[ks] = sw[kSwUb + (ks * 2 + t) * 64 + lane];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) us[t][ks] = sw[kSwUs + (t * 2 + ks) * 64 + lane];
-        __builtin_amdgcn_sched_barrier(0);
-        // O = e^gamma (q^ M0) + P U for rows 16 wave + 4 g4 + i: P U on bf16
-        // MFMA (an in-chunk product); rows past the chunk's end are dropped by
-        // the buffer range check.  The stores are non-temporal: nothing in the
-        // pass reads o, and the operand blocks the other tiles of the head
-        // still read stay in L2 (a 4,722-row prompt alone: 307 -> 278 us).
-        {
+            for (int tm = 0; tm < 3; ++tm)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) us[tm][ks] = sw[kSwUs + ((tm * 2 + ks) * 2 + t) * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
+            // O = e^gamma (q^ M0) + P U: P U on bf16 MFMA (an in-chunk product);
+            // rows past the chunk's end are dropped by the buffer range check.
+            // The stores are non-temporal: nothing in the pass reads o, and the
+            // operand blocks the other tiles of the head still read stay in L2.
             f4v pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) pu = mfma_bf16(pp[ks], ub[ks], pu);
-            const __amdgpu_buffer_rsrc_t r = out_rsrc(c);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(eg4[i], aO[i], pu[i])), r, ooff[i], 0, kNonTemporal);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(eg4[i], aO[t][i], pu[i])), orsrc, ooff[i] + 64 * t, 0,
+                                                      kNonTemporal);
+            // M <- e^{gamma_L} M + k^T U' on this wave's rows of tile t
+#pragma unroll
+            for (int b = 0; b < 2; ++b) M[t][b] = M[t][b] * eL;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int tm = 0; tm < 3; ++tm)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) M[t][b] = mfma_bf16(kt[2 * b + ks], us[tm][ks], M[t][b]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) pp[ks] = ld16(pP + nx + ks * 512);
-
-        // M <- e^{gamma_L} M + k^T U' on this wave's rows, then into Mb
-#pragma unroll
-        for (int b = 0; b < 2; ++b) M[b] = M[b] * eL;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int t = 0; t < 3; ++t)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) M[b] = mfma_bf16(kt[2 * b + ks], us[t][ks], M[b]);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) kt[j] = pF[nf + (kFragKp + j) * 64];
         eL = pG[ng];
@@ -893,28 +915,30 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         lds_barrier();   // Mb complete; every wave is done reading Ub and Us
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D] = M[b][i];
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[(size_t)(32 * wave + 16 * b + 4 * g4 + i) * D + 16 * t] = M[t][b][i];
 
     // the prompt's conv tail: its last three raw rows, continuing into the old
     // tail when the prompt is shorter.  Every read of the old tail (the
     // per-chunk kernel's) has finished: this launch follows it on the stream.
-    // The (head, tile) workgroups of the prompt split the channel groups; one
-    // thread reads all three old rows of a group before it writes any.
+    // The (head, tile pair) workgroups of the prompt split the channel groups;
+    // one thread reads all three old rows of a group before it writes any.
     {
         const int C = X.P.C, len = s1 - s0;
         uint16_t *tl = X.P.conv_tail + (size_t)pidx * 3 * C;
-        const int units = C / 8, part = hv * NTILE;
-        for (int u = h * NTILE + tile + part * tid; u < units; u += part * 256) {
+        const int units = C / 8, part = hv * NP;
+        for (int v = h * NP + tp + part * tid; v < units; v += part * 256) {
             uint4 nt[3];
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
                 const int m = len - 3 + j;   // local row of new tail row j
-                nt[j] = ld16(m >= 0 ? X.P.qkv + (size_t)(s0 + m) * C + 8 * u : tl + (size_t)(m + 3) * C + 8 * u);
+                nt[j] = ld16(m >= 0 ? X.P.qkv + (size_t)(s0 + m) * C + 8 * v : tl + (size_t)(m + 3) * C + 8 * v);
             }
 #pragma unroll
-            for (int j = 0; j < 3; ++j) st16(tl + (size_t)j * C + 8 * u, nt[j]);
+            for (int j = 0; j < 3; ++j) st16(tl + (size_t)j * C + 8 * v, nt[j]);
         }
     }
 }
@@ -970,7 +994,7 @@ hipError_t launch_prefill(const PrefillArgs &P, hipStream_t stream)
     hipLaunchKernelGGL(qk_kernel, dim3(units), dim3(256), kQkLds, stream, X);
     hipLaunchKernelGGL(intra_kernel, dim3(8 * X.r * ((units + 7) / 8)), dim3(256), kIntraLds, stream, X);
     const unsigned kunits = (unsigned)P.n_seqs * P.hk;   // (prompt, key head) pairs
-    hipLaunchKernelGGL(sweep_kernel, dim3(8 * NTILE * X.r * ((kunits + 7) / 8)), dim3(256), 0, stream, X);
+    hipLaunchKernelGGL(sweep_kernel, dim3(8 * (NTILE / 2) * X.r * ((kunits + 7) / 8)), dim3(256), 0, stream, X);
     return hipGetLastError();
 }
 
