@@ -85,6 +85,8 @@ constexpr int kGv = 132, kGvEg = 4, kGvEk = 68;
 // 32-bit data format, no swizzle; accesses past num_records are dropped.
 constexpr int kBufferDword3 = 0x00020000;
 constexpr int kNonTemporal = 2;   // cache-policy operand of a buffer store: nt
+constexpr int kDppSwapPairs = 0xB1;   // DPP quad_perm(1, 0, 3, 2): lanes 2m and 2m + 1 trade
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct Ctx {
     PrefillArgs P;
@@ -871,7 +873,7 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
         for (int t = 0; t < 2; ++t) ua[t] = *reinterpret_cast<const uint2 *>(pUA + nx + t * 1024);
         lds_barrier();   // Ub, Us complete; every wave is done reading Mb
 
-        const __amdgpu_buffer_rsrc_t orsrc = out_rsrc(c);
+        float ov[2][4];   // o of this lane's rows and columns, both tiles
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             uint4 ub[2], us[3][2];
@@ -882,17 +884,12 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) us[tm][ks] = sw[kSwUs + ((tm * 2 + ks) * 2 + t) * 64 + lane];
             __builtin_amdgcn_sched_barrier(0);
-            // O = e^gamma (q^ M0) + P U: P U on bf16 MFMA (an in-chunk product);
-            // rows past the chunk's end are dropped by the buffer range check.
-            // The stores are non-temporal: nothing in the pass reads o, and the
-            // operand blocks the other tiles of the head still read stay in L2.
+            // O = e^gamma (q^ M0) + P U: P U on bf16 MFMA (an in-chunk product)
             f4v pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) pu = mfma_bf16(pp[ks], ub[ks], pu);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(eg4[i], aO[t][i], pu[i])), orsrc, ooff[i] + 64 * t, 0,
-                                                      kNonTemporal);
+            for (int i = 0; i < 4; ++i) ov[t][i] = fmaf(eg4[i], aO[t][i], pu[i]);
             // M <- e^{gamma_L} M + k^T U' on this wave's rows of tile t
 #pragma unroll
             for (int b = 0; b < 2; ++b) M[t][b] = M[t][b] * eL;
@@ -902,6 +899,24 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
                 for (int tm = 0; tm < 3; ++tm)
 #pragma unroll
                     for (int b = 0; b < 2; ++b) M[t][b] = mfma_bf16(kt[2 * b + ks], us[tm][ks], M[t][b]);
+        }
+        {
+            // o leaves in 8-byte stores: lanes 2m and 2m + 1 trade one value a
+            // row (a DPP swap), so that the even lane holds tile 0's columns
+            // 2m, 2m + 1 and the odd one tile 1's (8 stores a wave and chunk
+            // became 4: 398 -> 384 us).  Rows past the chunk's end are dropped
+            // by the buffer range check.  The stores are non-temporal: nothing
+            // in the pass reads o, and the operand blocks the other tiles of
+            // the head still read stay in L2.
+            const __amdgpu_buffer_rsrc_t orsrc = out_rsrc(c);
+            const bool odd = lane & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float give = odd ? ov[0][i] : ov[1][i];
+                const float got = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(give), kDppSwapPairs, 0xF, 0xF, false));
+                const u32x2 v = {__float_as_uint(odd ? got : ov[0][i]), __float_as_uint(odd ? ov[1][i] : got)};
+                __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, ooff[i] + (odd ? 15 * 4 : 0), 0, kNonTemporal);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
