@@ -68,10 +68,13 @@ constexpr int NTILE = D / 16;   // 16-column state tiles of a head
 // A chunk-head block of sweep operands (bf16), every sub-array in lane order
 // [..][64 lanes][values]; lane l = (l16, g4) = (l & 15, l >> 4), and
 // accumulator register i of a 16x16 block holds row 4 g4 + i, column l16.
-//   W  [w 4][kb 8][l][4]        W[16w + l16][16kb + 4g4 + e]: the A operands
-//        of k-step (kb, i) for output rows 16w..16w+15 of W M0; step (kb, i)
-//        reads state rows 16kb + 4g4 + i
-//   UA [tile 8][w 4][l][4]      = U~[16w + 4g4 + i][16tile + l16]   (accumulator layout)
+//   W  [w 4][s 4][l][8]         W[16w + l16][16kb + 4g4 + (e & 3)] with
+//        kb = 2s + (e >> 2): the A operand of 32-deep k-step s for output rows
+//        16w..16w+15 of W M0, one 16-byte load a lane (value e reads state
+//        row 16kb + 4g4 + (e & 3))
+//   UA [pair 4][w 4][l][8]      = U~[16w + 4g4 + (e & 3)][16 (2 pair + (e >> 2)) + l16]
+//        (accumulator layout; the two tiles of a sweep workgroup's pair side by
+//        side, one 16-byte load a lane)
 //   P  [w 4][ks 2][l][8]        P[16w + l16][32ks + 4g4 + (e & 3) + 16 (e >> 2)],
 //        the A operands of P U in the permuted k order (below)
 // The A operands of q^ M0 and the k^ of the update are the key head's, in its
@@ -148,7 +151,6 @@ __device__ bool chunk_at(const Ctx &X, int cid, int &p, int &c, int &s0, int &s1
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(uint16_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
-__device__ __forceinline__ uint2 ld8(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
 __device__ __forceinline__ bf8v as_bf8(uint4 v) { return __builtin_bit_cast(bf8v, v); }
 
 // bf16 value e (0..7) of a 16-byte vector, as fp32
@@ -627,9 +629,9 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
                 u = mfma_bf16(t2, vp[hb][ks], u);
             }
             // wt: lane holds W[16 mt + l16][16 kbk + 4 g4 + i]; u: U~[16 mt + 4 g4 + i][16 kbk + l16]
-            *reinterpret_cast<uint2 *>(blk + kOffW + ((mt * 8 + kbk) * 64 + lane) * 4) =
+            *reinterpret_cast<uint2 *>(blk + kOffW + ((mt * 4 + (kbk >> 1)) * 64 + lane) * 8 + (kbk & 1) * 4) =
                 make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
-            *reinterpret_cast<uint2 *>(blk + kOffUA + ((kbk * 4 + mt) * 64 + lane) * 4) =
+            *reinterpret_cast<uint2 *>(blk + kOffUA + (((kbk >> 1) * 4 + mt) * 64 + lane) * 8 + (kbk & 1) * 4) =
                 make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
             // bound how far the scheduler hoists the next block's LDS reads
             __builtin_amdgcn_sched_barrier(0);
@@ -763,8 +765,8 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 
     const size_t cstride = (size_t)hv * kBlockElems;
     const uint16_t *bp = X.blk + ((size_t)cid0 * hv + h) * kBlockElems;
-    const uint16_t *pW = bp + kOffW + ((size_t)wave * 8 * 64 + lane) * 4;
-    const uint16_t *pUA = bp + kOffUA + ((size_t)(2 * tp * 4 + wave) * 64 + lane) * 4;   // tile t: + 4 * 64 * 4 t
+    const uint16_t *pW = bp + kOffW + ((size_t)wave * 4 * 64 + lane) * 8;
+    const uint16_t *pUA = bp + kOffUA + ((size_t)(tp * 4 + wave) * 64 + lane) * 8;
     const uint16_t *pP = bp + kOffP + ((size_t)wave * 2 * 64 + lane) * 8;
     // the key head's q^ and k^ fragments (qk_kernel), this wave's
     const int kh = h / X.r;
@@ -786,21 +788,20 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
     for (int i = 0; i < 4; ++i) ooff[i] = (int)(((size_t)(16 * wave + 4 * g4 + i) * orow + (size_t)h * D + col) * 4);
 
-    uint2 ww[8];
+    uint4 ww[4];
     uint4 wq[4], kt[4], pp[2];
-    uint2 ua[2];
+    uint4 ua;          // U~ of this lane's rows: tile 0 in x, y; tile 1 in z, w
     float eL;
     f4v eg4, ek4;
     // first chunk's operands, requested in the order the loop requests the
     // next chunk's (W, q^; ua; P; k^, gates), so the memory-counter waits at
     // the loop head see one request order on both of its entries
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) ww[kb] = ld8(pW + kb * 256);
+    for (int s = 0; s < 4; ++s) ww[s] = ld16(pW + s * 512);
 #pragma unroll
     for (int j = 0; j < 4; ++j) wq[j] = pF[(kFragQ + j) * 64];
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) ua[t] = *reinterpret_cast<const uint2 *>(pUA + t * 1024);
+    ua = ld16(pUA);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) pp[ks] = ld16(pP + ks * 512);
@@ -838,16 +839,15 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const uint4 wa = make_uint4(ww[2 * s].x, ww[2 * s].y, ww[2 * s + 1].x, ww[2 * s + 1].y);
 #pragma unroll
                 for (int tm = 0; tm < 3; ++tm) {
-                    aU[t] = mfma_bf16(wa, mb[tm][s], aU[t]);
+                    aU[t] = mfma_bf16(ww[s], mb[tm][s], aU[t]);
                     aO[t] = mfma_bf16(wq[s], mb[tm][s], aO[t]);
                 }
             }
         }
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) ww[kb] = ld8(pW + nx + kb * 256);
+        for (int s = 0; s < 4; ++s) ww[s] = ld16(pW + nx + s * 512);
 #pragma unroll
         for (int j = 0; j < 4; ++j) wq[j] = pF[nf + (kFragQ + j) * 64];
 
@@ -855,10 +855,11 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             f4v U;
-            U[0] = __uint_as_float(ua[t].x << 16) - aU[t][0];
-            U[1] = __uint_as_float(ua[t].x & 0xffff0000u) - aU[t][1];
-            U[2] = __uint_as_float(ua[t].y << 16) - aU[t][2];
-            U[3] = __uint_as_float(ua[t].y & 0xffff0000u) - aU[t][3];
+            const uint32_t u01 = t ? ua.z : ua.x, u23 = t ? ua.w : ua.y;
+            U[0] = __uint_as_float(u01 << 16) - aU[t][0];
+            U[1] = __uint_as_float(u01 & 0xffff0000u) - aU[t][1];
+            U[2] = __uint_as_float(u23 << 16) - aU[t][2];
+            U[3] = __uint_as_float(u23 & 0xffff0000u) - aU[t][3];
             uint2 *ub_mine = reinterpret_cast<uint2 *>(sw + kSwUb + ((wave >> 1) * 2 + t) * 64 + lane) + (wave & 1);
             uint2 *us_mine = reinterpret_cast<uint2 *>(sw + kSwUs + ((wave >> 1) * 2 + t) * 64 + lane) + (wave & 1);
             *ub_mine = make_uint2(pack2(U[0], U[1]), pack2(U[2], U[3]));
@@ -869,8 +870,7 @@ __global__ void __launch_bounds__(256) sweep_kernel(const Ctx X)
             us_mine[2 * 2 * 2 * 64 * 2] = t2;
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) ua[t] = *reinterpret_cast<const uint2 *>(pUA + nx + t * 1024);
+        ua = ld16(pUA + nx);
         lds_barrier();   // Ub, Us complete; every wave is done reading Mb
 
         float ov[2][4];   // o of this lane's rows and columns, both tiles
