@@ -616,26 +616,32 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             vp[hb][ks] = pack_perm(mfma_bf16(vr[2 * ks], sel, z), mfma_bf16(vr[2 * ks + 1], sel, z));
     }
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        const int kbk = 2 * wave + hb;
+    for (int mt = 0; mt < 4; ++mt) {
+        uint4 t1[2], t2[2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f4v wt = {0.f, 0.f, 0.f, 0.f}, u = wt;
+        for (int ks = 0; ks < 2; ++ks) {
+            t1[ks] = lds_perm(T1 + (16 * mt + l16) * SB, ks, g4);
+            t2[ks] = lds_perm(T2 + (16 * mt + l16) * SB, ks, g4);
+        }
+        f4v wt[2], u[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            wt[hb] = f4v{0.f, 0.f, 0.f, 0.f};
+            u[hb] = wt[hb];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const uint4 t1 = lds_perm(T1 + (16 * mt + l16) * SB, ks, g4);
-                const uint4 t2 = lds_perm(T2 + (16 * mt + l16) * SB, ks, g4);
-                wt = mfma_bf16(kp[hb][ks], t1, wt);
-                u = mfma_bf16(t2, vp[hb][ks], u);
+                wt[hb] = mfma_bf16(kp[hb][ks], t1[ks], wt[hb]);
+                u[hb] = mfma_bf16(t2[ks], vp[hb][ks], u[hb]);
             }
-            // wt: lane holds W[16 mt + l16][16 kbk + 4 g4 + i]; u: U~[16 mt + 4 g4 + i][16 kbk + l16]
-            *reinterpret_cast<uint2 *>(blk + kOffW + ((mt * 4 + (kbk >> 1)) * 64 + lane) * 8 + (kbk & 1) * 4) =
-                make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
-            *reinterpret_cast<uint2 *>(blk + kOffUA + (((kbk >> 1) * 4 + mt) * 64 + lane) * 8 + (kbk & 1) * 4) =
-                make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
-            // bound how far the scheduler hoists the next block's LDS reads
-            __builtin_amdgcn_sched_barrier(0);
         }
+        // wt[hb]: lane holds W[16 mt + l16][16 kb + 4 g4 + i], u[hb]: U~[16 mt + 4 g4 + i][16 kb + l16]
+        // for kb = 2 wave + hb: the two halves of one 16-byte piece each
+        *reinterpret_cast<uint4 *>(blk + kOffW + ((mt * 4 + wave) * 64 + lane) * 8) =
+            make_uint4(pack2(wt[0][0], wt[0][1]), pack2(wt[0][2], wt[0][3]), pack2(wt[1][0], wt[1][1]), pack2(wt[1][2], wt[1][3]));
+        *reinterpret_cast<uint4 *>(blk + kOffUA + ((wave * 4 + mt) * 64 + lane) * 8) =
+            make_uint4(pack2(u[0][0], u[0][1]), pack2(u[0][2], u[0][3]), pack2(u[1][0], u[1][1]), pack2(u[1][2], u[1][3]));
+        // bound how far the scheduler hoists the next block's LDS reads
+        __builtin_amdgcn_sched_barrier(0);
     }
     //  P rows 16 w .. 16 w + 15 -> the sweep's P, in the permuted k order
 #pragma unroll
