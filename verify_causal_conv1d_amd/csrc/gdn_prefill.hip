@@ -205,13 +205,14 @@ __device__ __forceinline__ f4v neg_diag_times(const float *An, int i, f4v s, int
 
 constexpr int SB = 72;   // bf16 row stride of the [.][64] LDS arrays (144 B: rows 4 banks apart)
 
-// LDS of an intra workgroup (bytes): 44 KiB, three workgroups a CU
+// LDS of an intra workgroup (bytes): 46 KiB, three workgroups a CU
 constexpr int kIntraAn = 0;                        // fp32 [64][64]: -A, and T blocks later stages read
 constexpr int kIntraPb = 64 * 64 * 4;              // bf16 [64][SB]  P
 constexpr int kIntraT1 = kIntraPb + 64 * SB * 2;   // bf16 [64][SB]  T' = T diag(beta e^gamma)
 constexpr int kIntraT2 = kIntraT1 + 64 * SB * 2;   // bf16 [64][SB]  T'' = T diag(beta)
 constexpr int kIntraVec = kIntraT2 + 64 * SB * 2;  // fp32 [4][64]   gamma, beta, e^gamma, e^{gamma_L - gamma}
-constexpr int kIntraLds = kIntraVec + 4 * 64 * 4;
+constexpr int kIntraW = kIntraVec + 4 * 64 * 4;      // fp32 [128][4]  the value head's conv weights
+constexpr int kIntraLds = kIntraW + D * 4 * 4;
 constexpr int KSB = 136;   // bf16 row stride of the staged k^ / q^ rows (272 B: rows 4 banks apart)
 static_assert(2 * 64 * KSB * 2 <= kIntraVec, "staged k^ and q^ fit below the gate vectors");
 
@@ -442,6 +443,11 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         return ld16(u >= s0 ? X.P.qkv + (size_t)u * C + ch : tail + (size_t)(3 + u - s0) * C + ch);
     };
 
+    // the value head's conv weights, one 16-byte piece a thread of waves 1 and
+    // 2, for the v conv after the solve (one load a thread instead of eight)
+    float4 *wl = reinterpret_cast<float4 *>(lds + kIntraW);
+    if (tid >= 64 && tid < 64 + D)
+        wl[tid - 64] = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)(2 * nq + h * D + tid - 64) * 4);
     // ---- gates: gamma (inclusive in-chunk scan of log alpha), beta and the decays
     if (wave == 0) {
         const size_t o = (size_t)(r0 + lane) * hv + h;
@@ -578,7 +584,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         float w[8][4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float4 wv = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)(ch + e) * 4);
+            const float4 wv = wl[8 * cg + e];
             w[e][0] = wv.x; w[e][1] = wv.y; w[e][2] = wv.z; w[e][3] = wv.w;
         }
 #pragma unroll
