@@ -406,7 +406,12 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     const int hv = X.P.hv;
     const size_t cidh = (size_t)cid * hv + h;
     uint16_t *blk = X.blk + cidh * kBlockElems;
-    // this wave's fragments of the key head's k^ and q^ (qk_kernel), requested first
+    // the chunk's gate inputs (wave 0 scans them first), requested before the
+    // fragments so that their wait does not include the fragments'; rows past
+    // the chunk's end read its last row (not used)
+    const size_t go = (size_t)min(r0 + lane, r0 + L - 1) * X.P.hv + h;
+    const float a_in = bf16f(X.P.a[go]), b_in = bf16f(X.P.b[go]);
+    // this wave's fragments of the key head's k^ and q^ (qk_kernel)
     const uint4 *fr = X.frag + ((size_t)unit * 4 + wave) * kFragVec4 * 64 + lane;
     f16v S, QK;
     uint4 kp[2][2];
@@ -450,9 +455,8 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         wl[tid - 64] = *reinterpret_cast<const float4 *>(X.P.conv_w + (size_t)(2 * nq + h * D + tid - 64) * 4);
     // ---- gates: gamma (inclusive in-chunk scan of log alpha), beta and the decays
     if (wave == 0) {
-        const size_t o = (size_t)(r0 + lane) * hv + h;
-        float gl = lane < L ? log_decay(bf16f(X.P.a[o]), X.P.a_log[h], X.P.dt_bias[h]) : 0.0f;
-        const float bl = lane < L ? sigmoid_f(bf16f(X.P.b[o])) : 0.0f;
+        float gl = lane < L ? log_decay(a_in, X.P.a_log[h], X.P.dt_bias[h]) : 0.0f;
+        const float bl = lane < L ? sigmoid_f(b_in) : 0.0f;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const float up = __shfl_up(gl, d);
