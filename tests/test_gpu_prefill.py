@@ -102,6 +102,29 @@ def test_prefill_value_heads_per_key_head(hk, hv):
     check(b, out, tail, state)
 
 
+def test_prefill_many_prompts_with_equal_lengths():
+    """40 prompts, several of equal length (the sweep orders prompts by length,
+    ties by index) and some empty, so that the (prompt, key head) units fill
+    the XCD slots unevenly."""
+    rng = np.random.default_rng(41)
+    lengths = [int(x) for x in rng.choice([0, 1, 7, 64, 65, 100, 150], size=40)]
+    b = gi.make_batch(SMALL_27B_HEADS, lengths, seed=41)
+    announce(f"prefill {len(lengths)} prompts {lengths}")
+    out, tail, state = run_prefill(b)
+    check(b, out, tail, state)
+
+
+def test_prefill_more_than_256_prompts():
+    """Past 256 prompts the sweep takes prompts in index order (no length
+    ranking in LDS); short prompts, one key head, two value heads."""
+    rng = np.random.default_rng(42)
+    lengths = [int(x) for x in rng.integers(0, 9, size=260)]
+    b = gi.make_batch(gi.Shape(hk=1, hv=2, dk=128, dv=128), lengths, seed=42)
+    announce(f"prefill {len(lengths)} short prompts, {sum(lengths)} rows")
+    out, tail, state = run_prefill(b)
+    check(b, out, tail, state)
+
+
 def test_prefill_with_empty_prompt():
     lengths = [70, 0, 33]
     b = gi.make_batch(SMALL_27B_HEADS, lengths, seed=34)
