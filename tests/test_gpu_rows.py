@@ -84,6 +84,20 @@ MIXED = {"dk64-dv128": gi.Shape(hk=2, hv=6, dk=64, dv=128),
          "dk128-dv64": gi.Shape(hk=2, hv=4, dk=128, dv=64)}
 
 
+def test_narrow_workgroups_stage_in_several_batches():
+    """A launch of more than 256 workgroups gets no helper waves: with one
+    value head of dv = 64 a key head a workgroup has 128 threads, and its 19
+    staged rows of 320 channels (and 320 conv weights) take three batches of
+    loads.  Windows and trees against the oracle."""
+    shape = gi.Shape(hk=16, hv=16, dk=128, dv=64)
+    lengths = [16] * 14 + [9, 1, 16, 5, 12, 16]
+    for tree, seed in ((False, 95), (True, 96)):
+        b = gi.make_batch(shape, lengths, seed=seed, tree=tree)
+        announce(f"{'recur_tree' if tree else 'recur_window'} 20 streams hk=hv=16 dv=64 seed={seed}")
+        out, tsnap, ssnap = run_window(b, tree=tree)
+        check_against_oracle(b, out, tsnap, ssnap, tree=tree)
+
+
 @pytest.mark.parametrize("geom", list(MIXED))
 def test_mixed_head_sizes(geom):
     """dk != dv (both sizes the geometry allows): ragged windows and draft
