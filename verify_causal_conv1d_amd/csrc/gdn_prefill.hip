@@ -535,6 +535,15 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             T2[t * SB + 16 * jb + l16] = f2bf(z[r] * b2);
         }
     };
+    // v's raw rows for the conv below, thread (channel group vcg, rows
+    // vt0 - 3 .. vt0 + 3 of the chunk), requested here so that the rest of
+    // the solve covers their wait (362 -> 348 us a 4-prompt pass, bit for bit
+    // the same); during the diagonal blocks' substitution they would not fit
+    // in the registers beside it
+    const int vcg = tid & 15, vt0 = 4 * (tid >> 4);
+    uint4 vx[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) vx[k] = raw_row(2 * nq + h * D + 8 * vcg, min(r0 + vt0 + k - 3, r0 + L - 1));
     // Stage 2: T_{i,i-1} = -B_i A_{i,i-1} B_{i-1}, wave i (An holds -A)
     if (wave >= 1) {
         const int i = wave;
@@ -572,19 +581,16 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
     }
     lds_barrier();
 
-    // ---- v of value head h: causal conv + SiLU from the raw rows, requested
-    // only now (other workgroups on the CU cover the wait), staged as bf16 in
-    // the space of -A, which the solve no longer reads.  Vs row t holds 16
-    // groups of 8 channels, group c at position c ^ (t & 15), so that both the
-    // row-wise writes and the column-wise reads below meet 16 distinct banks.
-    // Thread (c, rows 4 j .. 4 j + 3) holds the 7 raw rows it needs.
+    // ---- v of value head h: causal conv + SiLU from the raw rows (in vx since
+    // the solve's second stage), staged as bf16 in the space of -A, which the
+    // solve no longer reads.  Vs row t holds 16 groups of 8 channels, group c
+    // at position c ^ (t & 15), so that both the row-wise writes and the
+    // column-wise reads below meet 16 distinct banks.  Thread (c, rows
+    // 4 j .. 4 j + 3) holds the 7 raw rows it needs.
     uint16_t *Vs = reinterpret_cast<uint16_t *>(lds + kIntraAn);   // [64][128]
     {
-        const int cg = tid & 15, t0 = 4 * (tid >> 4);
-        const int ch = 2 * nq + h * D + 8 * cg;
-        uint4 x[7];   // raw rows t0 - 3 .. t0 + 3 of the chunk
-#pragma unroll
-        for (int k = 0; k < 7; ++k) x[k] = raw_row(ch, min(r0 + t0 + k - 3, r0 + L - 1));
+        const int cg = vcg, t0 = vt0;
+        const uint4 *x = vx;   // raw rows t0 - 3 .. t0 + 3 of the chunk
         float w[8][4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
