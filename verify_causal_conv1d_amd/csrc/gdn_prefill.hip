@@ -181,14 +181,18 @@ __device__ __forceinline__ float silu_fast(float y)
 // strictly upper blocks are free and keep the fp32 T blocks later stages read
 // (B_i over A_ii once that is used, T_10 in block (0,1), T_21 in (1,2), T_20
 // in (0,2)).
+// An's rows are AS = 68 floats apart (272 B, 4 banks on): a block operand
+// read takes 16 rows at one column, which 256-byte rows put on the same
+// banks (341 vs 346 us a 4-prompt pass, bit for bit the same).
+constexpr int AS = 68;
 
 // z += X Y for fp32 16 x 16 blocks X = An block (xi, xj), Y = An block (yi, yj)
 __device__ __forceinline__ f4v mm_blocks(const float *An, int xi, int xj, int yi, int yj, f4v z, int l16, int g4)
 {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        z = __builtin_amdgcn_mfma_f32_16x16x4f32(An[(16 * xi + l16) * 64 + 16 * xj + 4 * kk + g4],
-                                                 An[(16 * yi + 4 * kk + g4) * 64 + 16 * yj + l16], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(An[(16 * xi + l16) * AS + 16 * xj + 4 * kk + g4],
+                                                 An[(16 * yi + 4 * kk + g4) * AS + 16 * yj + l16], z, 0, 0, 0);
     return z;
 }
 
@@ -199,15 +203,15 @@ __device__ __forceinline__ f4v neg_diag_times(const float *An, int i, f4v s, int
     f4v z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        z = __builtin_amdgcn_mfma_f32_16x16x4f32(-An[(16 * i + l16) * 64 + 16 * i + 4 * g4 + kk], s[kk], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(-An[(16 * i + l16) * AS + 16 * i + 4 * g4 + kk], s[kk], z, 0, 0, 0);
     return z;
 }
 
 constexpr int SB = 72;   // bf16 row stride of the [.][64] LDS arrays (144 B: rows 4 banks apart)
 
-// LDS of an intra workgroup (bytes): 46 KiB, three workgroups a CU
-constexpr int kIntraAn = 0;                        // fp32 [64][64]: -A, and T blocks later stages read
-constexpr int kIntraPb = 64 * 64 * 4;              // bf16 [64][SB]  P
+// LDS of an intra workgroup (bytes): 47 KiB, three workgroups a CU
+constexpr int kIntraAn = 0;                        // fp32 [64][AS]: -A, and T blocks later stages read
+constexpr int kIntraPb = 64 * AS * 4;              // bf16 [64][SB]  P
 constexpr int kIntraT1 = kIntraPb + 64 * SB * 2;   // bf16 [64][SB]  T' = T diag(beta e^gamma)
 constexpr int kIntraT2 = kIntraT1 + 64 * SB * 2;   // bf16 [64][SB]  T'' = T diag(beta)
 constexpr int kIntraVec = kIntraT2 + 64 * SB * 2;  // fp32 [4][64]   gamma, beta, e^gamma, e^{gamma_L - gamma}
@@ -487,7 +491,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
             const int t = 32 * bi + 8 * (i >> 2) + 4 * hh + (i & 3);
             const bool live = s <= t && t < L;
             const float dec = live ? __expf(gam[t] - gs) : 0.0f;
-            An[t * 64 + s] = (live && s < t) ? -bet[t] * dec * S[i] : 0.0f;
+            An[t * AS + s] = (live && s < t) ? -bet[t] * dec * S[i] : 0.0f;
             Pb[t * SB + s] = f2bf(dec * QK[i]);
         }
     }
@@ -503,7 +507,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             float acc = (t == j) ? 1.0f : 0.0f;
-            const float *row = An + (16 * w + t) * 64 + 16 * w;
+            const float *row = An + (16 * w + t) * AS + 16 * w;
 #pragma unroll
             for (int s = 0; s < t; ++s) acc = fmaf(row[s], Tc[s], acc);
             Tc[t] = acc;
@@ -515,7 +519,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         for (int i = 0; i < 4; ++i) {
             const float v = g4 == 0 ? Tc[i] : g4 == 1 ? Tc[4 + i] : g4 == 2 ? Tc[8 + i] : Tc[12 + i];
             const int t = 16 * w + 4 * g4 + i;
-            An[t * 64 + 16 * w + j] = v;
+            An[t * AS + 16 * w + j] = v;
             T1[t * SB + 16 * w + j] = f2bf(v * b1);
             T2[t * SB + 16 * w + j] = f2bf(v * b2);
             for (int cb = w + 1; cb < 4; ++cb) {
@@ -553,7 +557,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         put_t(i, i - 1, z);
         if (i < 3) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) An[(16 * (i - 1) + 4 * g4 + r) * 64 + 16 * i + l16] = z[r];   // T_10 -> (0,1), T_21 -> (1,2)
+            for (int r = 0; r < 4; ++r) An[(16 * (i - 1) + 4 * g4 + r) * AS + 16 * i + l16] = z[r];   // T_10 -> (0,1), T_21 -> (1,2)
         }
     }
     lds_barrier();
@@ -567,7 +571,7 @@ __global__ void __launch_bounds__(256, 3) intra_kernel(const Ctx X)
         put_t(i, i - 2, z);
         if (i == 2) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) An[(4 * g4 + r) * 64 + 32 + l16] = z[r];   // T_20 -> (0,2)
+            for (int r = 0; r < 4; ++r) An[(4 * g4 + r) * AS + 32 + l16] = z[r];   // T_20 -> (0,2)
         }
     }
     lds_barrier();
