@@ -177,7 +177,7 @@ __device__ __forceinline__ float silu_fast(float y)
 // T = (I + A)^-1 for the strictly lower-triangular 64 x 64 A, by 16 x 16
 // blocks: the diagonal blocks B_i = (I + A_ii)^-1 by forward substitution,
 // then T_ij = -B_i sum_{k=j}^{i-1} A_ik T_kj (i > j) on fp32 MFMA, one
-// diagonal distance after the other.  An holds -A in fp32, [64][64]; its
+// diagonal distance after the other.  An holds -A in fp32, 64 x 64; its
 // strictly upper blocks are free and keep the fp32 T blocks later stages read
 // (B_i over A_ii once that is used, T_10 in block (0,1), T_21 in (1,2), T_20
 // in (0,2)).
