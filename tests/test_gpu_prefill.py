@@ -89,11 +89,12 @@ def test_prefill_2b_layer():
     check(b, out, tail, state)
 
 
-@pytest.mark.parametrize("hk,hv", [(2, 4), (1, 4), (2, 12)])
+@pytest.mark.parametrize("hk,hv", [(2, 4), (1, 4), (2, 12), (1, 5), (1, 8), (3, 24)])
 def test_prefill_value_heads_per_key_head(hk, hv):
-    """Two and four value heads a key head (the per-chunk kernel then takes
-    two value heads a workgroup) and six (three a workgroup, two workgroups a
-    key head)."""
+    """Two, four, five, six and eight value heads a key head (eight is the
+    most the pass takes).  The per-chunk kernel places the r value heads of a
+    (chunk, key head) as consecutive workgroups of one XCD, and the sweep the
+    tile pairs of a (prompt, key head): odd r and r = 8 exercise both maps."""
     shape = gi.Shape(hk=hk, hv=hv, dk=128, dv=128)
     lengths = [70, 5, 130]
     b = gi.make_batch(shape, lengths, seed=35 + hv)

@@ -98,6 +98,22 @@ def test_narrow_workgroups_stage_in_several_batches():
         check_against_oracle(b, out, tsnap, ssnap, tree=tree)
 
 
+@pytest.mark.parametrize("hk,hv,d,n", [(1, 8, 64, 17), (1, 5, 128, 26), (2, 16, 128, 9)])
+def test_many_value_heads_per_key_head(hk, hv, d, n):
+    """Eight value heads a key head at d = 64 (a workgroup of 16 waves, the
+    most one holds, on all eight heads), five at d = 128 (no divisor but one
+    fits a workgroup) and eight at d = 128 (four heads a workgroup, two
+    workgroups a key head), with enough streams that the launch keeps whole
+    heads in a workgroup: windows and trees against the oracle."""
+    shape = gi.Shape(hk=hk, hv=hv, dk=d, dv=d)
+    lengths = ([16, 3, 11, 16, 1] * 6)[:n]
+    for tree, seed in ((False, 120 + hv), (True, 130 + hv)):
+        b = gi.make_batch(shape, lengths, seed=seed, tree=tree)
+        announce(f"{'recur_tree' if tree else 'recur_window'} hk={hk} hv={hv} d={d} seed={seed}")
+        out, tsnap, ssnap = run_window(b, tree=tree)
+        check_against_oracle(b, out, tsnap, ssnap, tree=tree)
+
+
 @pytest.mark.parametrize("geom", list(MIXED))
 def test_mixed_head_sizes(geom):
     """dk != dv (both sizes the geometry allows): ragged windows and draft
