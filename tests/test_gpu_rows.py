@@ -218,12 +218,17 @@ def test_step_matches_oracle_many_streams():
     assert np.array_equal(bits16(tail), ref["tail_snap"])
 
 
-@pytest.mark.parametrize("shape_name,n", [("SMALL", 300), ("dk64-dv128", 40), ("dk128-dv64", 40)])
+WIDE_STEPS = {"r8-d64": gi.Shape(hk=1, hv=8, dk=64, dv=64), "r4-d128": gi.Shape(hk=2, hv=8, dk=128, dv=128)}
+
+
+@pytest.mark.parametrize("shape_name,n", [("SMALL", 300), ("dk64-dv128", 40), ("dk128-dv64", 40),
+                                          ("r8-d64", 20), ("r4-d128", 12)])
 def test_steps_many_streams_and_mixed_heads(shape_name, n):
     """One-row steps run one workgroup a (stream, key head): hundreds of
-    streams on the small layer, and both mixed head geometries, against the
-    oracle's one-step rows."""
-    shape = gi.SMALL if shape_name == "SMALL" else MIXED[shape_name]
+    streams on the small layer, both mixed head geometries, and the widest
+    workgroups a step takes (16 waves: eight value heads of 64 columns, four
+    of 128), against the oracle's one-step rows."""
+    shape = gi.SMALL if shape_name == "SMALL" else MIXED.get(shape_name) or WIDE_STEPS[shape_name]
     b = gi.make_batch(shape, [1] * n, seed=91)
     announce(f"conv_step {n} streams {shape}")
     d = device_batch(b)
