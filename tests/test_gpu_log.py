@@ -104,6 +104,9 @@ CASES = {
     "trees-dk64-dv128": (gi.Shape(hk=2, hv=6, dk=64, dv=128), [16, 11, 2], True, 68),
     "chains-dk128-dv64": (gi.Shape(hk=2, hv=4, dk=128, dv=64), [3, 16, 8], False, 69),
     "trees-dk128-dv64": (gi.Shape(hk=2, hv=4, dk=128, dv=64), [16, 16, 6], True, 70),
+    # enough streams that whole key heads stay in a workgroup: 16 waves
+    "chains-r8-d64-wide": (gi.Shape(hk=1, hv=8, dk=64, dv=64), ([16, 3, 11, 16, 1] * 4)[:17], False, 71),
+    "trees-r4-d128-wide": (gi.Shape(hk=2, hv=8, dk=128, dv=128), ([16, 9, 1, 16, 5] * 2)[:9], True, 72),
 }
 
 
